@@ -1,0 +1,153 @@
+/*
+ * lsa.h -- C ABI of the MI355X (gfx950) LongCat Sparse Attention hot path.
+ *
+ * Four operations, in the order one attention layer calls them:
+ *   lsa_index_scores       lightning-indexer scores of every cached key        (stage 1)
+ *   lsa_topk_select        top-k positions with sink/window columns forced      (stage 2)
+ *   lsa_sparse_mla_decode  absorbed-MLA attention over the selected latent rows (stage 3)
+ *   lsa_sparse_mla_prefill the same for a chunk of Lq query tokens, causal      (stage 3)
+ *
+ * Sources: the page "MLX-VLM 的 LongCat-Flash-Lite-Sparse 支持LSA 稀疏注意力、n-gram
+ * 融合与预填充优化解析", sections "LSA" (indexer, top-k with forced columns, dense fallback,
+ * decode gather, prefill mask, one index pass shared by both attention sub-blocks of a layer)
+ * and "架构总览" (absorbed MLA, kv_lora_rank 512, rope 64); and the page "LongCat Sparse
+ * Attention技术深度解析", section "模型架构配置" (index_n_heads 32, index_head_dim 128,
+ * index_topk 2048, index_init_tokens 16, index_local_tokens 1024).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers unless stated otherwise; all are owned by the caller.  The
+ *   library allocates nothing on these paths and keeps no pointer after returning.  Buffers
+ *   must stay alive until the enqueued work has finished.
+ * - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call only enqueues
+ *   work on it and returns without synchronising; order between calls is stream order, so
+ *   the caller appends the current token's index key and latent row before calling.
+ * - Sequences: B sequences, the cache of sequence b holds seqlens[b] tokens (device int32),
+ *   the last Lq of which are the current queries.  Query i of sequence b sits at position
+ *   p = seqlens[b] - Lq + i and may see keys [0, p] (n = p + 1 keys).
+ *   Caller preconditions (device-side, not checked): Lq <= seqlens[b] <= S_max.
+ * - bf16 tensors are passed as raw 16-bit storage (`const void*`).  All layouts are dense,
+ *   row-major, with the last dimension contiguous.
+ * - Errors: host-checkable problems return a non-zero status BEFORE anything is enqueued, and
+ *   lsa_last_error() then describes them (thread-local).  A zero-sized batch (B == 0 or
+ *   Lq == 0) is a valid no-op.  A kernel-launch failure returns LSA_ERR_LAUNCH.  Faults in
+ *   device memory surface at the caller's next synchronisation, as usual for HIP.
+ * - Results are deterministic: identical inputs give bit-identical outputs.
+ * - No global mutable state except the thread-local error text.
+ */
+#ifndef LSA_H_
+#define LSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int lsa_status;
+#define LSA_OK 0
+#define LSA_ERR_NULL_ARG 1    /* a required pointer is NULL */
+#define LSA_ERR_BAD_SHAPE 2   /* a size is negative/zero where it must be positive, or inconsistent */
+#define LSA_ERR_UNSUPPORTED 3 /* a size outside the compiled set (see each entry point) */
+#define LSA_ERR_WORKSPACE 4   /* workspace missing or smaller than the query function says */
+#define LSA_ERR_LAUNCH 5      /* the HIP runtime rejected a kernel launch */
+
+/* Short constant name of a status ("LSA_OK", ...); never NULL. */
+const char* lsa_status_str(lsa_status s);
+
+/* Detail of the last failure on the calling thread ("" if none).  Valid until the next call
+ * on this thread. */
+const char* lsa_last_error(void);
+
+/*
+ * Lightning-indexer scores ("LSA" section; the fused epilogue of "预填充优化" accumulates
+ * max(g, 0) * w over the index heads):
+ *
+ *   scores[b,i,s] = sum_{h<Hi} w[b,i,h] * max(0, sum_{d<Di} q_idx[b,i,h,d] * k_idx[b,s,d])
+ *
+ * for every s in [0, p].  One index key per cached token, shared by all index heads.
+ *   q_idx   bf16 [B, Lq, Hi, Di]   index queries (already projected, rotated)
+ *   w       fp32 [B, Lq, Hi]       per-head weights (any sign)
+ *   k_idx   bf16 [B, S_max, Di]    index-key cache (already normalised, rotated)
+ *   seqlens int32 [B]
+ *   scores  fp32 [B, Lq, S_max]    output; entries s > p are left untouched
+ * Products are exact in fp32 and accumulated in fp32 (bf16 matrix cores), the head sum in
+ * fp32.  Supported: 1 <= Hi <= 32, Di in {32, 64, 128}; S_max >= 1.
+ */
+lsa_status lsa_index_scores(const void* q_idx, const float* w, const void* k_idx,
+                            const int32_t* seqlens, int B, int Lq, int Hi, int Di, int S_max,
+                            float* scores, void* stream);
+
+/* Workspace (bytes) lsa_topk_select needs for these sizes (0 is possible). */
+size_t lsa_topk_workspace_bytes(int B, int Lq, int S_max, int topk, int init_tokens,
+                                int local_tokens);
+
+/*
+ * Top-k selection ("LSA" section: argpartition of the top index_topk scores; the
+ * index_init_tokens sink columns and index_local_tokens sliding-window columns forced so they
+ * are always selected; dense fallback when the cached length does not exceed index_topk).
+ * For each query row with n = p + 1 valid keys:
+ *   - n <= topk: indices = 0, 1, ..., n-1 (dense fallback), n_sel = n;
+ *   - otherwise positions s < init_tokens and s > p - local_tokens are forced in, and the
+ *     remaining topk - init_tokens - local_tokens slots go to the largest fp32 scores among
+ *     positions [init_tokens, p - local_tokens]; equal scores go to the LOWEST position
+ *     (-0.0 and +0.0 are equal); n_sel = topk.
+ * Indices are written in ascending order; unused slots are -1.
+ *   scores    fp32 [B, Lq, S_max] (only s <= p is read; values must be finite)
+ *   indices   int32 [B, Lq, topk]  output
+ *   n_sel     int32 [B, Lq]        output
+ *   workspace device buffer of at least lsa_topk_workspace_bytes(...) bytes (may be NULL when
+ *             that is 0); its contents on entry do not matter.
+ * Supported: 1 <= topk <= 8192, init_tokens >= 0, local_tokens >= 0,
+ * init_tokens + local_tokens <= topk (else LSA_ERR_BAD_SHAPE).
+ */
+lsa_status lsa_topk_select(const float* scores, const int32_t* seqlens, int B, int Lq, int S_max,
+                           int topk, int init_tokens, int local_tokens, int32_t* indices,
+                           int32_t* n_sel, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace (bytes) lsa_sparse_mla_decode / _prefill need for these sizes (0 is possible).
+ * `dense` is 1 when the call will pass indices == NULL. */
+size_t lsa_mla_workspace_bytes(int B, int Lq, int H, int Dv, int S_max, int topk, int dense);
+
+/*
+ * Absorbed-MLA attention over selected latent rows ("LSA" section: decode gathers KV rows by
+ * the top-k indices; "架构总览": latent rank 512 plus rope 64, absorbed projections).
+ * For each query row (b, i) at position p and each head h:
+ *   sel   = indices[b,i,0:n_sel[b,i]]   or, when indices == NULL, every position 0..p
+ *   l_s   = softmax_scale * sum_{d<Dqk} q[b,i,h,d] * kv[b,s,d]        for s in sel
+ *   out[b,i,h,c] = sum_s softmax(l)_s * kv[b,s,c]                       for c < Dv
+ *   lse[b,i,h]   = log(sum_s exp(l_s))                                  (natural log)
+ * A latent row is [latent (Dv) | rope (Dqk - Dv)]; the value vector is its first Dv entries.
+ * Products are bf16 x bf16 on matrix cores with fp32 accumulation; the softmax is fp32; the
+ * probabilities enter the value product as bf16; out is rounded to bf16.
+ *   q       bf16 [B, H, Dqk] (decode) / [B, Lq, H, Dqk] (prefill)
+ *   kv      bf16 [B, S_max, Dqk]   latent cache
+ *   indices int32 [B, Lq, topk] from lsa_topk_select (ascending or not; entries >= n_sel are
+ *           ignored), or NULL for dense attention over [0, p]
+ *   n_sel   int32 [B, Lq] (ignored when indices == NULL)
+ *   out     bf16 [B, H, Dv] / [B, Lq, H, Dv]
+ *   lse     fp32 [B, H] / [B, Lq, H], or NULL
+ * The same indices may serve several calls (the two attention sub-blocks of a layer share
+ * one index pass); the inputs are never written.
+ * Rows that select nothing get out = 0 and lse = -inf.
+ * Supported: (Dqk, Dv) in {(576, 512), (80, 64)}; H >= 1 (heads are processed in groups of
+ * 32); topk >= 1 when indices != NULL.
+ */
+lsa_status lsa_sparse_mla_decode(const void* q, const void* kv, const int32_t* indices,
+                                 const int32_t* n_sel, const int32_t* seqlens, int B, int H,
+                                 int Dqk, int Dv, int S_max, int topk, float softmax_scale,
+                                 void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+lsa_status lsa_sparse_mla_prefill(const void* q, const void* kv, const int32_t* indices,
+                                  const int32_t* n_sel, const int32_t* seqlens, int B, int Lq,
+                                  int H, int Dqk, int Dv, int S_max, int topk,
+                                  float softmax_scale, void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSA_H_ */

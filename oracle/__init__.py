@@ -1,0 +1,123 @@
+"""CPU oracle for the LSA hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
+import this package.  The GPU library never loads it, and it shares no code with the GPU path:
+the arithmetic lives in ``lsa_oracle.c`` (plain C, fp64, naive loops), and this module only
+marshals numpy arrays to it.  See the header of ``lsa_oracle.c`` for the passages each
+function follows and the readings taken where the pages are silent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lsa_oracle.c")
+_LIB = os.path.join(_HERE, "liblsa_oracle.so")
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, IEEE semantics: no fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+           "-o", _LIB + ".tmp", _SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        L.lsa_oracle_index_scores.argtypes = [P, P, P, P, I, I, I, I, I, P]
+        L.lsa_oracle_index_scores.restype = I
+        L.lsa_oracle_topk.argtypes = [P, P, I, I, I, I, I, I, P, P]
+        L.lsa_oracle_topk.restype = I
+        L.lsa_oracle_sparse_mla.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, ctypes.c_double,
+                                            P, P]
+        L.lsa_oracle_sparse_mla.restype = I
+        L.lsa_oracle_set_threads.argtypes = [I]
+        L.lsa_oracle_max_threads.restype = I
+        _lib = L
+    return _lib
+
+
+def set_threads(n: int) -> None:
+    lib().lsa_oracle_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().lsa_oracle_max_threads())
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def index_scores(q_idx, w, k_idx, seqlens, Lq: int) -> np.ndarray:
+    """q_idx bf16 bits [B,Lq,Hi,Di], w f32 [B,Lq,Hi], k_idx bf16 bits [B,S_max,Di] ->
+    f32 scores [B,Lq,S_max] (NaN where s > p)."""
+    q_idx = _c(q_idx, np.uint16)
+    w = _c(w, np.float32)
+    k_idx = _c(k_idx, np.uint16)
+    seqlens = _c(seqlens, np.int32)
+    B, Lq_, Hi, Di = q_idx.shape
+    assert Lq_ == Lq and w.shape == (B, Lq, Hi) and k_idx.shape[0] == B and k_idx.shape[2] == Di
+    S_max = k_idx.shape[1]
+    out = np.full((B, Lq, S_max), np.nan, dtype=np.float32)
+    rc = lib().lsa_oracle_index_scores(q_idx.ctypes.data, w.ctypes.data, k_idx.ctypes.data,
+                                       seqlens.ctypes.data, B, Lq, Hi, Di, S_max, out.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"lsa_oracle_index_scores: bad input ({rc})")
+    return out
+
+
+def topk_select(scores, seqlens, topk: int, init_tokens: int, local_tokens: int):
+    """scores f32 [B,Lq,S_max] -> (indices int32 [B,Lq,topk] ascending, -1 padded; n_sel [B,Lq])."""
+    scores = _c(scores, np.float32)
+    seqlens = _c(seqlens, np.int32)
+    B, Lq, S_max = scores.shape
+    idx = np.empty((B, Lq, topk), dtype=np.int32)
+    nsel = np.empty((B, Lq), dtype=np.int32)
+    rc = lib().lsa_oracle_topk(scores.ctypes.data, seqlens.ctypes.data, B, Lq, S_max, topk,
+                               init_tokens, local_tokens, idx.ctypes.data, nsel.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"lsa_oracle_topk: bad input ({rc})")
+    return idx, nsel
+
+
+def sparse_mla(q, kv, indices, n_sel, seqlens, Dv: int, scale: float):
+    """q bf16 bits [B,Lq,H,Dqk]; kv bf16 bits [B,S_max,Dqk]; indices int32 [B,Lq,topk] or None
+    (dense over [0,p]); n_sel int32 [B,Lq] -> (out f64 [B,Lq,H,Dv], lse f64 [B,Lq,H])."""
+    q = _c(q, np.uint16)
+    kv = _c(kv, np.uint16)
+    seqlens = _c(seqlens, np.int32)
+    B, Lq, H, Dqk = q.shape
+    assert kv.shape[0] == B and kv.shape[2] == Dqk and 0 < Dv <= Dqk
+    S_max = kv.shape[1]
+    if indices is not None:
+        indices = _c(indices, np.int32)
+        n_sel = _c(n_sel, np.int32)
+        topk = indices.shape[2]
+        assert indices.shape[:2] == (B, Lq) and n_sel.shape == (B, Lq)
+        ip, np_ = indices.ctypes.data, n_sel.ctypes.data
+    else:
+        topk, ip, np_ = 0, None, None
+    out = np.empty((B, Lq, H, Dv), dtype=np.float64)
+    lse = np.empty((B, Lq, H), dtype=np.float64)
+    rc = lib().lsa_oracle_sparse_mla(q.ctypes.data, kv.ctypes.data, ip, np_, seqlens.ctypes.data,
+                                     B, Lq, H, Dqk, Dv, S_max, topk, float(scale),
+                                     out.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"lsa_oracle_sparse_mla: bad input ({rc})")
+    return out, lse
