@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of the LSA hot path on one MI355X: lightning indexer -> top-2048 (sink/window
+forced) -> sparse absorbed-MLA over the selected latent rows, through the C ABI.
+
+Default workload: 128K-context decode, batch 32, one index + top-k pass shared by the layer's
+two attention sub-blocks (two MLA calls).  A step is one pass of the whole path over the
+batch; inputs are generated in HBM before timing.  Prints ONE JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "LSA decode queries/s @128K ctx (indexer+top-2048+MLA); % HBM peak GB/s"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, public spec
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="query rows the oracle times (0: auto)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run one device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(wl):
+    """Bytes the method must move per step (per query row, summed): index keys of the visible
+    positions, index query and weights, index write; per MLA call the selected latent rows, the
+    query, the output and the index read.  The fp32 score round trip between the first two
+    stages is excluded (reported separately)."""
+    tot = 0
+    score_rt = 0
+    for b in range(wl.B):
+        for i in range(wl.Lq):
+            n = wl.seqlens[b] - wl.Lq + i + 1
+            k = min(n, wl.topk)
+            tot += n * wl.Di * 2 + wl.Hi * wl.Di * 2 + wl.Hi * 4 + wl.topk * 4
+            tot += wl.mla_calls * (k * wl.Dqk * 2 + wl.H * wl.Dqk * 2 + wl.H * wl.Dv * 2 + wl.topk * 4)
+            score_rt += 2 * n * 4
+    return tot, score_rt
+
+
+def indexer_bytes(wl):
+    """Algorithmic bytes of one indexer launch: keys of the visible positions, the index query
+    and weights, and the fp32 score written per visible position."""
+    tot = 0
+    for b in range(wl.B):
+        for i in range(wl.Lq):
+            n = wl.seqlens[b] - wl.Lq + i + 1
+            tot += n * wl.Di * 2 + wl.Hi * wl.Di * 2 + wl.Hi * 4 + n * 4
+    return tot
+
+
+def cpu_baseline(wl, sample_rows):
+    """Time the CPU oracle (as it stands) on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    from long_context_sparse_lightning_amd.workloads import host_kv_rows, host_slice
+
+    rows = [(b, i) for b in range(wl.B) for i in range(wl.Lq)]
+    step = max(1, len(rows) // sample_rows)
+    rows = rows[::step][:sample_rows]
+    # inputs first (not timed)
+    prepared = []
+    for b, i in rows:
+        p = wl.seqlens[b] - wl.Lq + i
+        prepared.append((b, i, p, host_slice(wl, "qidx", b)[i:i + 1][None],
+                         host_slice(wl, "w", b)[i:i + 1][None],
+                         host_slice(wl, "kidx", b)[None, : p + 1],
+                         [host_slice(wl, f"q{c}", b)[i][None, None] for c in range(wl.mla_calls)]))
+    cores = oracle.max_threads()
+    t_total = 0.0
+    for b, i, p, qi, w, k, qs in prepared:
+        n = p + 1
+        sl = np.array([n], np.int32)
+        t0 = time.perf_counter()
+        sc = oracle.index_scores(qi, w, k, sl, 1)
+        idx, nsel = oracle.topk_select(sc, sl, wl.topk, wl.init, wl.local)
+        t_total += time.perf_counter() - t0
+        sel = idx[0, 0, : nsel[0, 0]]
+        m = sel.size
+        kvs = [host_kv_rows(wl, f"kv{c}", b, sel)[None] for c in range(wl.mla_calls)]
+        t0 = time.perf_counter()
+        for c in range(wl.mla_calls):
+            oracle.sparse_mla(qs[c], kvs[c], np.arange(m, dtype=np.int32)[None, None],
+                              np.array([[m]], np.int32), np.array([m], np.int32), wl.Dv, wl.scale)
+        t_total += time.perf_counter() - t0
+    return {"value": len(rows) / t_total, "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(rows)} of {wl.B * wl.Lq} query rows of {wl.name} (full indexer scan, "
+                      f"top-k and {wl.mla_calls} MLA call(s) each); {t_total:.2f} s wall on "
+                      f"{cores} threads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from long_context_sparse_lightning_amd import lsa
+    from long_context_sparse_lightning_amd.workloads import WORKLOADS, device_inputs
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    X = device_inputs(wl, device=dev)
+    B, Lq = wl.B, wl.Lq
+    scores = torch.empty(B, Lq, wl.S_max, dtype=torch.float32, device=dev)
+    idx = torch.empty(B, Lq, wl.topk, dtype=torch.int32, device=dev)
+    nsel = torch.empty(B, Lq, dtype=torch.int32, device=dev)
+    tws = torch.empty(max(1, lsa.lsa_topk_workspace_bytes(B, Lq, wl.S_max, wl.topk, wl.init,
+                                                          wl.local)), dtype=torch.uint8, device=dev)
+    mws = torch.empty(max(1, lsa.lsa_mla_workspace_bytes(B, Lq, wl.H, wl.Dv, wl.S_max, wl.topk,
+                                                         False)), dtype=torch.uint8, device=dev)
+    outs = [torch.empty(B, Lq, wl.H, wl.Dv, dtype=torch.bfloat16, device=dev)
+            for _ in range(wl.mla_calls)]
+    lses = [torch.empty(B, Lq, wl.H, dtype=torch.float32, device=dev) for _ in range(wl.mla_calls)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(k1_events=None):
+        if k1_events is not None:
+            k1_events[0].record(stream)
+        lsa.lsa_index_scores(X["qidx"], X["w"], X["kidx"], X["seqlens"], scores=scores)
+        if k1_events is not None:
+            k1_events[1].record(stream)
+        lsa.lsa_topk_select(scores, X["seqlens"], wl.topk, wl.init, wl.local, indices=idx,
+                            n_sel=nsel, workspace=tws)
+        for c in range(wl.mla_calls):
+            if wl.decode:
+                lsa.lsa_sparse_mla_decode(X[f"q{c}"][:, 0], X[f"kv{c}"], idx[:, 0], nsel[:, 0],
+                                          X["seqlens"], wl.Dv, wl.scale, out=outs[c][:, 0],
+                                          lse=lses[c][:, 0], workspace=mws)
+            else:
+                lsa.lsa_sparse_mla_prefill(X[f"q{c}"], X[f"kv{c}"], idx, nsel, X["seqlens"], wl.Dv,
+                                           wl.scale, out=outs[c], lse=lses[c], workspace=mws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] {wl.name}: warmup done", file=sys.stderr, flush=True)
+
+    k1_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(args.steps):
+        step(k1_ev[s])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    elapsed_ms = t_start.elapsed_time(t_end)
+    k1_ms = sum(a.elapsed_time(b) for a, b in k1_ev) / args.steps
+    print(f"[bench] timed {args.steps} steps: {elapsed_ms:.3f} ms (host wall {wall * 1e3:.3f} ms)",
+          file=sys.stderr, flush=True)
+
+    ms_per_step = elapsed_ms / args.steps
+    queries = B * Lq
+    value = queries * args.steps / (elapsed_ms / 1e3)
+    alg, score_rt = algorithmic_bytes(wl)
+    k1_bytes = indexer_bytes(wl)
+    k1_gbs = k1_bytes / (k1_ms / 1e3) / 1e9
+    step_gbs = alg / (ms_per_step / 1e3) / 1e9
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        bcopy = torch.empty_like(a)
+        torch.cuda.synchronize()
+        bcopy.copy_(a)
+        torch.cuda.synchronize()
+        del a, bcopy
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded SplitMix64; dyadic index q/k, unit-variance bf16 latent cache)",
+        "config": {"workload": wl.name, "batch": B, "context": wl.S_max, "query_tokens": Lq,
+                   "index_heads": wl.Hi, "index_dim": wl.Di, "topk": wl.topk,
+                   "init_tokens": wl.init, "local_tokens": wl.local, "mla_heads": wl.H,
+                   "qk_dim": wl.Dqk, "v_dim": wl.Dv, "mla_calls_per_step": wl.mla_calls},
+        "hbm_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
+        "step_alg_bytes": alg,
+        "step_score_roundtrip_bytes": score_rt,
+        "roofline": {"kernel": "lsa_index_scores", "bound": "hbm", "achieved": round(k1_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_ms": round(k1_ms, 5),
+                     "alg_bytes_per_launch": k1_bytes},
+    }
+    if not args.no_cpu_baseline:
+        sample = args.cpu_sample or (16 if wl.decode else 64)
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl, sample)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    sys.exit(main())

@@ -1,0 +1,166 @@
+// C ABI of the LSA hot path (declared in include/lsa.h): argument checks, workspace sizing and
+// kernel launches.  Every check happens before anything is enqueued; on failure the status is
+// returned and a thread-local message describes it.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "lsa.h"
+#include "lsa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+lsa_status fail(lsa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+lsa_status ok() {
+  g_last_error[0] = '\0';
+  return LSA_OK;
+}
+
+lsa_status launched(hipError_t err, const char* what) {
+  if (err != hipSuccess)
+    return fail(LSA_ERR_LAUNCH, "%s: kernel launch failed: %s", what, hipGetErrorString(err));
+  return ok();
+}
+
+constexpr int kMaxTopk = 8192;
+
+}  // namespace
+
+extern "C" {
+
+const char* lsa_status_str(lsa_status s) {
+  switch (s) {
+    case LSA_OK: return "LSA_OK";
+    case LSA_ERR_NULL_ARG: return "LSA_ERR_NULL_ARG";
+    case LSA_ERR_BAD_SHAPE: return "LSA_ERR_BAD_SHAPE";
+    case LSA_ERR_UNSUPPORTED: return "LSA_ERR_UNSUPPORTED";
+    case LSA_ERR_WORKSPACE: return "LSA_ERR_WORKSPACE";
+    case LSA_ERR_LAUNCH: return "LSA_ERR_LAUNCH";
+    default: return "LSA_ERR_UNKNOWN";
+  }
+}
+
+const char* lsa_last_error(void) { return g_last_error; }
+
+lsa_status lsa_index_scores(const void* q_idx, const float* w, const void* k_idx,
+                            const int32_t* seqlens, int B, int Lq, int Hi, int Di, int S_max,
+                            float* scores, void* stream) {
+  if (B < 0 || Lq < 0) return fail(LSA_ERR_BAD_SHAPE, "lsa_index_scores: B=%d Lq=%d must be >= 0", B, Lq);
+  if (Hi <= 0 || Di <= 0 || S_max <= 0)
+    return fail(LSA_ERR_BAD_SHAPE, "lsa_index_scores: Hi=%d Di=%d S_max=%d must be > 0", Hi, Di, S_max);
+  if (Hi > 32) return fail(LSA_ERR_UNSUPPORTED, "lsa_index_scores: Hi=%d > 32", Hi);
+  if (Di != 32 && Di != 64 && Di != 128)
+    return fail(LSA_ERR_UNSUPPORTED, "lsa_index_scores: Di=%d not in {32, 64, 128}", Di);
+  if (B == 0 || Lq == 0) return ok();
+  if (!q_idx || !w || !k_idx || !seqlens || !scores)
+    return fail(LSA_ERR_NULL_ARG, "lsa_index_scores: NULL q_idx/w/k_idx/seqlens/scores");
+  return launched(lsa::launch_index_scores(static_cast<const uint16_t*>(q_idx), w,
+                                           static_cast<const uint16_t*>(k_idx), seqlens, B, Lq, Hi,
+                                           Di, S_max, scores, static_cast<hipStream_t>(stream)),
+                  "lsa_index_scores");
+}
+
+static lsa_status check_topk(int B, int Lq, int S_max, int topk, int init_tokens, int local_tokens) {
+  if (B < 0 || Lq < 0) return fail(LSA_ERR_BAD_SHAPE, "lsa_topk_select: B=%d Lq=%d must be >= 0", B, Lq);
+  if (S_max <= 0 || topk <= 0)
+    return fail(LSA_ERR_BAD_SHAPE, "lsa_topk_select: S_max=%d topk=%d must be > 0", S_max, topk);
+  if (init_tokens < 0 || local_tokens < 0 ||
+      static_cast<long>(init_tokens) + local_tokens > topk)
+    return fail(LSA_ERR_BAD_SHAPE,
+                "lsa_topk_select: need 0 <= init_tokens (%d), 0 <= local_tokens (%d), sum <= topk (%d)",
+                init_tokens, local_tokens, topk);
+  if (topk > kMaxTopk) return fail(LSA_ERR_UNSUPPORTED, "lsa_topk_select: topk=%d > %d", topk, kMaxTopk);
+  return LSA_OK;
+}
+
+size_t lsa_topk_workspace_bytes(int B, int Lq, int S_max, int topk, int init_tokens,
+                                int local_tokens) {
+  if (check_topk(B, Lq, S_max, topk, init_tokens, local_tokens) != LSA_OK) return 0;
+  return lsa::topk_workspace_bytes(B, Lq, S_max, topk, init_tokens, local_tokens);
+}
+
+lsa_status lsa_topk_select(const float* scores, const int32_t* seqlens, int B, int Lq, int S_max,
+                           int topk, int init_tokens, int local_tokens, int32_t* indices,
+                           int32_t* n_sel, void* workspace, size_t workspace_bytes, void* stream) {
+  lsa_status st = check_topk(B, Lq, S_max, topk, init_tokens, local_tokens);
+  if (st != LSA_OK) return st;
+  if (B == 0 || Lq == 0) return ok();
+  if (!scores || !seqlens || !indices || !n_sel)
+    return fail(LSA_ERR_NULL_ARG, "lsa_topk_select: NULL scores/seqlens/indices/n_sel");
+  const size_t need = lsa::topk_workspace_bytes(B, Lq, S_max, topk, init_tokens, local_tokens);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(LSA_ERR_WORKSPACE, "lsa_topk_select: workspace %zu bytes at %p, need %zu",
+                workspace_bytes, workspace, need);
+  return launched(lsa::launch_topk(scores, seqlens, B, Lq, S_max, topk, init_tokens, local_tokens,
+                                   indices, n_sel, workspace, static_cast<hipStream_t>(stream)),
+                  "lsa_topk_select");
+}
+
+static lsa_status check_mla(const char* fn, int B, int Lq, int H, int Dqk, int Dv, int S_max, int topk,
+                            bool dense, float softmax_scale) {
+  if (B < 0 || Lq < 0) return fail(LSA_ERR_BAD_SHAPE, "%s: B=%d Lq=%d must be >= 0", fn, B, Lq);
+  if (H <= 0 || Dqk <= 0 || Dv <= 0 || S_max <= 0)
+    return fail(LSA_ERR_BAD_SHAPE, "%s: H=%d Dqk=%d Dv=%d S_max=%d must be > 0", fn, H, Dqk, Dv, S_max);
+  if (Dv > Dqk) return fail(LSA_ERR_BAD_SHAPE, "%s: Dv=%d > Dqk=%d", fn, Dv, Dqk);
+  if (!dense && topk <= 0) return fail(LSA_ERR_BAD_SHAPE, "%s: topk=%d must be > 0", fn, topk);
+  if (!(softmax_scale == softmax_scale) || softmax_scale == INFINITY || softmax_scale == -INFINITY)
+    return fail(LSA_ERR_BAD_SHAPE, "%s: softmax_scale must be finite", fn);
+  if (!((Dqk == 576 && Dv == 512) || (Dqk == 80 && Dv == 64)))
+    return fail(LSA_ERR_UNSUPPORTED, "%s: (Dqk, Dv) = (%d, %d) not in {(576, 512), (80, 64)}", fn,
+                Dqk, Dv);
+  return LSA_OK;
+}
+
+size_t lsa_mla_workspace_bytes(int B, int Lq, int H, int Dv, int S_max, int topk, int dense) {
+  if (B <= 0 || Lq <= 0 || H <= 0 || Dv <= 0 || S_max <= 0 || (!dense && topk <= 0)) return 0;
+  return lsa::mla_workspace_bytes(B, Lq, H, Dv, S_max, topk, dense);
+}
+
+static lsa_status run_mla(const char* fn, const void* q, const void* kv, const int32_t* indices,
+                          const int32_t* n_sel, const int32_t* seqlens, int B, int Lq, int H,
+                          int Dqk, int Dv, int S_max, int topk, float softmax_scale, void* out,
+                          float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  const bool dense = indices == nullptr;
+  lsa_status st = check_mla(fn, B, Lq, H, Dqk, Dv, S_max, topk, dense, softmax_scale);
+  if (st != LSA_OK) return st;
+  if (B == 0 || Lq == 0) return ok();
+  if (!q || !kv || !seqlens || !out) return fail(LSA_ERR_NULL_ARG, "%s: NULL q/kv/seqlens/out", fn);
+  if (!dense && !n_sel) return fail(LSA_ERR_NULL_ARG, "%s: indices given without n_sel", fn);
+  const size_t need = lsa::mla_workspace_bytes(B, Lq, H, Dv, S_max, topk, dense);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(LSA_ERR_WORKSPACE, "%s: workspace %zu bytes at %p, need %zu", fn, workspace_bytes,
+                workspace, need);
+  return launched(lsa::launch_mla(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv),
+                                  indices, n_sel, seqlens, B, Lq, H, Dqk, Dv, S_max, dense ? 0 : topk,
+                                  softmax_scale, static_cast<uint16_t*>(out), lse, workspace,
+                                  static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+lsa_status lsa_sparse_mla_decode(const void* q, const void* kv, const int32_t* indices,
+                                 const int32_t* n_sel, const int32_t* seqlens, int B, int H,
+                                 int Dqk, int Dv, int S_max, int topk, float softmax_scale,
+                                 void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return run_mla("lsa_sparse_mla_decode", q, kv, indices, n_sel, seqlens, B, 1, H, Dqk, Dv, S_max,
+                 topk, softmax_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+lsa_status lsa_sparse_mla_prefill(const void* q, const void* kv, const int32_t* indices,
+                                  const int32_t* n_sel, const int32_t* seqlens, int B, int Lq,
+                                  int H, int Dqk, int Dv, int S_max, int topk,
+                                  float softmax_scale, void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return run_mla("lsa_sparse_mla_prefill", q, kv, indices, n_sel, seqlens, B, Lq, H, Dqk, Dv,
+                 S_max, topk, softmax_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Internal declarations shared by the LSA kernels and the C-ABI layer (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lsa {
+
+// ------------------------------------------------------------------ vector types (gfx950)
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// 16-byte global load of 8 bf16 values.
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
+  u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() { return __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0}); }
+
+// D = A * B + C on the 32x32x16 bf16 matrix core.  Per lane l (c = l % 32, g = l / 32):
+//   A: row c, k = 8g .. 8g+7;  B: column c, k = 8g .. 8g+7;
+//   C/D register r: column c, row 8*(r/4) + 4*g + (r%4).
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row of the 32x32 accumulator held in register r by lanes of half g.
+__device__ __forceinline__ constexpr int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
+
+__device__ __forceinline__ uint16_t bf16_bits_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Lane prefix count of a 64-bit wave mask: number of set bits in lanes below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+}
+
+__device__ __forceinline__ uint64_t wave_ballot(bool pred) { return __ballot(pred); }
+
+// ------------------------------------------------------------------ launchers
+// Each returns hipSuccess or the launch error; arguments were validated by the C-ABI layer.
+hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+                               const int32_t* seqlens, int B, int Lq, int Hi, int Di, int S_max,
+                               float* scores, hipStream_t stream);
+
+size_t topk_workspace_bytes(int B, int Lq, int S_max, int topk, int init_tokens, int local_tokens);
+hipError_t launch_topk(const float* scores, const int32_t* seqlens, int B, int Lq, int S_max,
+                       int topk, int init_tokens, int local_tokens, int32_t* indices,
+                       int32_t* n_sel, void* workspace, hipStream_t stream);
+
+size_t mla_workspace_bytes(int B, int Lq, int H, int Dv, int S_max, int topk, int dense);
+hipError_t launch_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indices,
+                      const int32_t* n_sel, const int32_t* seqlens, int B, int Lq, int H, int Dqk,
+                      int Dv, int S_max, int topk, float softmax_scale, uint16_t* out, float* lse,
+                      void* workspace, hipStream_t stream);
+
+}  // namespace lsa

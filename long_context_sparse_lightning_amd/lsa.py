@@ -1,0 +1,186 @@
+"""Thin ctypes binding of ``liblsa.so`` (C ABI in ``include/lsa.h``).
+
+Argument marshalling only: shapes come from the tensors, pointers from ``data_ptr()`` and the
+stream from ``torch.cuda.current_stream()``; every step of the hot path runs in the library's
+HIP kernels.  PyTorch provides device memory (including workspaces) and streams, nothing else.
+The binding refuses to run without the built library -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblsa.so")
+
+LSA_OK = 0
+STATUS = {0: "LSA_OK", 1: "LSA_ERR_NULL_ARG", 2: "LSA_ERR_BAD_SHAPE", 3: "LSA_ERR_UNSUPPORTED",
+          4: "LSA_ERR_WORKSPACE", 5: "LSA_ERR_LAUNCH"}
+
+EXPORTED = ["lsa_status_str", "lsa_last_error", "lsa_index_scores", "lsa_topk_workspace_bytes",
+            "lsa_topk_select", "lsa_mla_workspace_bytes", "lsa_sparse_mla_decode",
+            "lsa_sparse_mla_prefill"]
+
+
+class LsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load liblsa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} not found: build it with "
+                               "`python -m long_context_sparse_lightning_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.lsa_status_str.argtypes = [I]
+        L.lsa_status_str.restype = ctypes.c_char_p
+        L.lsa_last_error.argtypes = []
+        L.lsa_last_error.restype = ctypes.c_char_p
+        L.lsa_index_scores.argtypes = [P, P, P, P, I, I, I, I, I, P, P]
+        L.lsa_index_scores.restype = I
+        L.lsa_topk_workspace_bytes.argtypes = [I, I, I, I, I, I]
+        L.lsa_topk_workspace_bytes.restype = Z
+        L.lsa_topk_select.argtypes = [P, P, I, I, I, I, I, I, P, P, P, Z, P]
+        L.lsa_topk_select.restype = I
+        L.lsa_mla_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+        L.lsa_mla_workspace_bytes.restype = Z
+        L.lsa_sparse_mla_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, P, P, P, Z, P]
+        L.lsa_sparse_mla_decode.restype = I
+        L.lsa_sparse_mla_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, P, Z, P]
+        L.lsa_sparse_mla_prefill.restype = I
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != LSA_OK:
+        raise LsaError(status, lib().lsa_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _want(t, name, dtype, ndim):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device tensor")
+
+
+def lsa_index_scores(q_idx, w, k_idx, seqlens, scores=None):
+    """q_idx bf16 [B,Lq,Hi,Di], w f32 [B,Lq,Hi], k_idx bf16 [B,S_max,Di], seqlens i32 [B]
+    -> scores f32 [B,Lq,S_max] (entries after each query's position are left untouched)."""
+    _want(q_idx, "q_idx", torch.bfloat16, 4)
+    _want(w, "w", torch.float32, 3)
+    _want(k_idx, "k_idx", torch.bfloat16, 3)
+    _want(seqlens, "seqlens", torch.int32, 1)
+    B, Lq, Hi, Di = q_idx.shape
+    S_max = k_idx.shape[1]
+    if scores is None:
+        scores = torch.empty(B, Lq, S_max, dtype=torch.float32, device=q_idx.device)
+    _want(scores, "scores", torch.float32, 3)
+    _check(lib().lsa_index_scores(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(seqlens), B, Lq, Hi, Di,
+                                  S_max, _ptr(scores), _stream(q_idx)))
+    return scores
+
+
+def lsa_topk_workspace_bytes(B, Lq, S_max, topk, init_tokens, local_tokens) -> int:
+    return int(lib().lsa_topk_workspace_bytes(B, Lq, S_max, topk, init_tokens, local_tokens))
+
+
+def lsa_topk_select(scores, seqlens, topk, init_tokens, local_tokens, indices=None, n_sel=None,
+                    workspace=None):
+    """scores f32 [B,Lq,S_max] -> (indices i32 [B,Lq,topk] ascending, -1 padded; n_sel i32 [B,Lq])."""
+    _want(scores, "scores", torch.float32, 3)
+    _want(seqlens, "seqlens", torch.int32, 1)
+    B, Lq, S_max = scores.shape
+    dev = scores.device
+    if indices is None:
+        indices = torch.empty(B, Lq, topk, dtype=torch.int32, device=dev)
+    if n_sel is None:
+        n_sel = torch.empty(B, Lq, dtype=torch.int32, device=dev)
+    need = lsa_topk_workspace_bytes(B, Lq, S_max, topk, init_tokens, local_tokens)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().lsa_topk_select(_ptr(scores), _ptr(seqlens), B, Lq, S_max, topk, init_tokens,
+                                 local_tokens, _ptr(indices), _ptr(n_sel), _ptr(workspace), wbytes,
+                                 _stream(scores)))
+    return indices, n_sel
+
+
+def lsa_mla_workspace_bytes(B, Lq, H, Dv, S_max, topk, dense) -> int:
+    return int(lib().lsa_mla_workspace_bytes(B, Lq, H, Dv, S_max, topk, 1 if dense else 0))
+
+
+def _mla(decode, q, kv, indices, n_sel, seqlens, Dv, softmax_scale, out, lse, workspace):
+    _want(kv, "kv", torch.bfloat16, 3)
+    _want(seqlens, "seqlens", torch.int32, 1)
+    if decode:
+        _want(q, "q", torch.bfloat16, 3)
+        B, H, Dqk = q.shape
+        Lq = 1
+        out_shape = (B, H, Dv)
+    else:
+        _want(q, "q", torch.bfloat16, 4)
+        B, Lq, H, Dqk = q.shape
+        out_shape = (B, Lq, H, Dv)
+    S_max = kv.shape[1]
+    dense = indices is None
+    topk = 0
+    if not dense:
+        _want(indices, "indices", torch.int32, 2 if decode else 3)
+        _want(n_sel, "n_sel", torch.int32, 1 if decode else 2)
+        topk = indices.shape[-1]
+    dev = q.device
+    if out is None:
+        out = torch.empty(out_shape, dtype=torch.bfloat16, device=dev)
+    need = lsa_mla_workspace_bytes(B, Lq, H, Dv, S_max, topk, dense)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if decode:
+        st = lib().lsa_sparse_mla_decode(_ptr(q), _ptr(kv), _ptr(indices), _ptr(n_sel),
+                                         _ptr(seqlens), B, H, Dqk, Dv, S_max, topk,
+                                         float(softmax_scale), _ptr(out), _ptr(lse),
+                                         _ptr(workspace), wbytes, _stream(q))
+    else:
+        st = lib().lsa_sparse_mla_prefill(_ptr(q), _ptr(kv), _ptr(indices), _ptr(n_sel),
+                                          _ptr(seqlens), B, Lq, H, Dqk, Dv, S_max, topk,
+                                          float(softmax_scale), _ptr(out), _ptr(lse),
+                                          _ptr(workspace), wbytes, _stream(q))
+    _check(st)
+    return out
+
+
+def lsa_sparse_mla_decode(q, kv, indices, n_sel, seqlens, Dv, softmax_scale, out=None, lse=None,
+                          workspace=None):
+    """q bf16 [B,H,Dqk], kv bf16 [B,S_max,Dqk], indices i32 [B,topk] (or None: dense over
+    [0, p]), n_sel i32 [B] -> out bf16 [B,H,Dv] (lse f32 [B,H] written if given)."""
+    return _mla(True, q, kv, indices, n_sel, seqlens, Dv, softmax_scale, out, lse, workspace)
+
+
+def lsa_sparse_mla_prefill(q, kv, indices, n_sel, seqlens, Dv, softmax_scale, out=None, lse=None,
+                           workspace=None):
+    """q bf16 [B,Lq,H,Dqk], kv bf16 [B,S_max,Dqk], indices i32 [B,Lq,topk] (or None: dense
+    causal), n_sel i32 [B,Lq] -> out bf16 [B,Lq,H,Dv] (lse f32 [B,Lq,H] written if given)."""
+    return _mla(False, q, kv, indices, n_sel, seqlens, Dv, softmax_scale, out, lse, workspace)

@@ -4,7 +4,8 @@
  * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's CPU-baseline leg
  * may load this library.  It shares no code, header or constant with the GPU library and
  * includes no HIP header.  It is deliberately plain: fp64 arithmetic, naive loops, a library
- * sort; OpenMP is used only to run independent (sequence, query) rows side by side.
+ * sort; OpenMP only runs independent outputs (query rows, and (row, key) pairs for the
+ * scores) side by side, never changing what is summed or in which order.
  *
  * Sources (the web pages this project follows):
  *  - "MLX-VLM 的 LongCat-Flash-Lite-Sparse 支持LSA 稀疏注意力、n-gram 融合与预填充优化解析"
@@ -76,19 +77,20 @@ int lsa_oracle_max_threads(void) {
 int lsa_oracle_index_scores(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
                             const int32_t* seqlens, int B, int Lq, int Hi, int Di, int S_max,
                             float* scores) {
-  int bad = 0;
   long rows = (long)B * Lq;
-#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
   for (long r = 0; r < rows; ++r) {
-    int b = (int)(r / Lq), i = (int)(r % Lq);
-    long p = query_position(seqlens[b], Lq, i);
-    if (p < 0 || p >= S_max) {
-      bad |= 1;
-      continue;
-    }
-    const uint16_t* qr = q_idx + r * (long)Hi * Di;
-    const float* wr = w + r * (long)Hi;
-    for (long s = 0; s <= p; ++s) {
+    long p = query_position(seqlens[r / Lq], Lq, (int)(r % Lq));
+    if (p < 0 || p >= S_max) return -1;
+  }
+  /* one (row, key) pair per iteration; positions after the query are skipped */
+#pragma omp parallel for collapse(2) schedule(static)
+  for (long r = 0; r < rows; ++r) {
+    for (long s = 0; s < S_max; ++s) {
+      int b = (int)(r / Lq), i = (int)(r % Lq);
+      long p = query_position(seqlens[b], Lq, i);
+      if (s > p) continue;
+      const uint16_t* qr = q_idx + r * (long)Hi * Di;
+      const float* wr = w + r * (long)Hi;
       const uint16_t* ks = k_idx + ((long)b * S_max + s) * Di;
       double total = 0.0;
       for (int h = 0; h < Hi; ++h) {
@@ -100,7 +102,7 @@ int lsa_oracle_index_scores(const uint16_t* q_idx, const float* w, const uint16_
       scores[r * (long)S_max + s] = (float)total;
     }
   }
-  return bad ? -1 : 0;
+  return 0;
 }
 
 typedef struct {

@@ -1,0 +1,115 @@
+"""Host-only checks of the C ABI: the library loads, exports every function include/lsa.h
+declares, and rejects bad arguments before enqueueing anything (no GPU needed: every call
+below returns during argument checking)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_sparse_lightning_amd import lsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "lsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lsa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_operations():
+    names = declared_functions()
+    for f in ("lsa_index_scores", "lsa_topk_select", "lsa_sparse_mla_decode",
+              "lsa_sparse_mla_prefill"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = lsa.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} not exported by liblsa.so"
+    assert sorted(lsa.EXPORTED) == declared_functions()
+
+
+def test_status_strings():
+    L = lsa.lib()
+    for code, name in lsa.STATUS.items():
+        assert L.lsa_status_str(code).decode() == name
+    assert L.lsa_status_str(99).decode() == "LSA_ERR_UNKNOWN"
+
+
+def _err():
+    return lsa.lib().lsa_last_error().decode()
+
+
+def test_index_scores_argument_errors():
+    L = lsa.lib()
+    p = ctypes.c_void_p(16)
+    assert L.lsa_index_scores(None, None, None, None, 2, 1, 32, 128, 100, None, None) == 1
+    assert "NULL" in _err()
+    assert L.lsa_index_scores(p, p, p, p, -1, 1, 32, 128, 100, p, None) == 2
+    assert L.lsa_index_scores(p, p, p, p, 1, 1, 0, 128, 100, p, None) == 2
+    assert L.lsa_index_scores(p, p, p, p, 1, 1, 33, 128, 100, p, None) == 3
+    assert L.lsa_index_scores(p, p, p, p, 1, 1, 32, 96, 100, p, None) == 3
+    assert "Di=96" in _err()
+    # empty batch: valid no-op even with NULL pointers
+    assert L.lsa_index_scores(None, None, None, None, 0, 1, 32, 128, 100, None, None) == 0
+    assert _err() == ""
+
+
+def test_topk_argument_errors_and_workspace():
+    L = lsa.lib()
+    p = ctypes.c_void_p(16)
+    assert L.lsa_topk_select(p, p, 1, 1, 4096, 8, 5, 4, p, p, None, 0, None) == 2  # init+local>topk
+    assert L.lsa_topk_select(p, p, 1, 1, 4096, 10000, 16, 1024, p, p, None, 0, None) == 3
+    assert L.lsa_topk_select(None, p, 1, 1, 4096, 256, 4, 64, p, p, None, 0, None) == 1
+    # a row longer than one chunk needs workspace
+    need = L.lsa_topk_workspace_bytes(32, 1, 131072, 2048, 16, 1024)
+    assert need > 0
+    assert L.lsa_topk_select(p, p, 32, 1, 131072, 2048, 16, 1024, p, p, None, 0, None) == 4
+    assert L.lsa_topk_select(p, p, 32, 1, 131072, 2048, 16, 1024, p, p, p, need - 1, None) == 4
+    assert "need" in _err()
+    # one chunk per row: no workspace at all
+    assert L.lsa_topk_workspace_bytes(8, 1, 16384, 2048, 16, 1024) == 0
+    assert L.lsa_topk_workspace_bytes(1, 1, 4096, 8, 5, 4) == 0  # invalid -> 0
+
+
+def test_mla_argument_errors_and_workspace():
+    L = lsa.lib()
+    p = ctypes.c_void_p(16)
+    dec = L.lsa_sparse_mla_decode
+    assert dec(p, p, p, p, p, 4, 32, 576, 640, 1000, 64, 0.1, p, None, p, 1 << 30, None) == 2
+    assert dec(p, p, p, p, p, 4, 32, 512, 448, 1000, 64, 0.1, p, None, p, 1 << 30, None) == 3
+    assert dec(p, p, p, None, p, 4, 32, 576, 512, 1000, 64, 0.1, p, None, p, 1 << 30, None) == 1
+    assert dec(p, p, p, p, p, 4, 32, 576, 512, 1000, 0, 0.1, p, None, p, 1 << 30, None) == 2
+    assert dec(p, p, p, p, p, 4, 32, 576, 512, 1000, 64, float("nan"), p, None, p, 1 << 30,
+               None) == 2
+    need = L.lsa_mla_workspace_bytes(32, 1, 32, 512, 131072, 2048, 0)
+    assert need > 0
+    assert dec(p, p, p, p, p, 32, 32, 576, 512, 131072, 2048, 0.07, p, None, None, 0, None) == 4
+    pre = L.lsa_sparse_mla_prefill
+    assert pre(p, p, None, None, p, 0, 10, 32, 576, 512, 100, 0, 0.1, None, None, None, 0,
+               None) == 0
+    # many query rows: one workgroup per row, no partials -> no workspace
+    assert L.lsa_mla_workspace_bytes(1, 4096, 32, 512, 131072, 2048, 0) == 0
+
+
+@pytest.mark.parametrize("name", ["tiny_decode", "decode_32k", "decode_128k", "prefill_128k",
+                                  "decode_1m"])
+def test_workspace_sizes_are_modest(name):
+    from long_context_sparse_lightning_amd.workloads import WORKLOADS
+
+    wl = WORKLOADS[name]
+    t = lsa.lsa_topk_workspace_bytes(wl.B, wl.Lq, wl.S_max, wl.topk, wl.init, wl.local)
+    m = lsa.lsa_mla_workspace_bytes(wl.B, wl.Lq, wl.H, wl.Dv, wl.S_max, wl.topk, False)
+    assert 0 <= t <= 512 << 20 and 0 <= m <= 256 << 20
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+
+    with pytest.raises(ValueError):
+        lsa.lsa_index_scores(torch.zeros(1, 1, 4, 32, dtype=torch.bfloat16),
+                             torch.zeros(1, 1, 4), torch.zeros(1, 64, 32, dtype=torch.bfloat16),
+                             torch.tensor([64], dtype=torch.int32))
