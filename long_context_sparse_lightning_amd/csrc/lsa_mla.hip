@@ -7,24 +7,31 @@
 // row is 576 values and the value vector is its first 512).  Decode and prefill share this
 // kernel: a prefill chunk is B*Lq independent query rows, each with its own selection.
 //
-// Design for gfx950.  A workgroup (4 wavefronts) owns one (query row, group of 32 heads,
-// slice of the selected rows).  Rows arrive 32 at a time: each thread gathers 16-byte pieces
-// of whole 1152-byte latent rows (consecutive threads read consecutive pieces of a row, so
-// every row is read as full cache lines) into registers, and they are stored to LDS at a
-// padded pitch (an odd number of 16-byte units, so the per-row fragment reads below hit
-// distinct banks).  The next tile's gather is in flight while the current tile is computed.
-//  * logits: S^T = KV_tile (32 rows x Dqk) . Q^T on the 32x32x16 bf16 matrix core; the Dqk/16
-//    steps are split over the 4 wavefronts and their partial sums added in LDS in a fixed
-//    order.  With rows as the M dimension each lane holds 16 rows of one head, so the
-//    softmax max/sum needs one cross-lane exchange.
-//  * online softmax in fp32 (base-2 exponentials with log2(e) folded into the scale); the
-//    probabilities are rounded to bf16 and the running sum adds the rounded values, so the
-//    normalisation matches what the value product sees.
-//  * values: O (32 heads x Dv) += P (32 x 32 rows) . V; each wavefront owns Dv/4 output
-//    columns.  P is already in the A-operand layout (the row order inside a k-step only has
-//    to agree between A and B), and the B operand is read from the LDS tile per lane.
-//  * several workgroups per query row when rows are few (decode): each writes fp32 partial
-//    O with its max and sum, and a small combine kernel merges them with log-sum-exp weights.
+// Design for gfx950.  A workgroup owns one (query row, group of 32 heads, slice of the selected
+// rows) and runs four wavefronts.  The slice is cut into 32-row tiles that stream through a
+// 3-stage LDS ring filled by LDS-DMA loads (global_load_lds_dwordx4: a lane names one 16-byte
+// piece of a latent row and the hardware writes it straight into LDS), so two tiles are in
+// flight while one is computed, without holding any of it in registers.  Every 1152-byte row
+// is read whole by consecutive lanes.  Within LDS, tile row r is rotated by r 16-byte units,
+// which spreads both access patterns below over the LDS banks (measured by a bank model: at
+// most 5 lanes per 4-bank group for the fragment reads, ideal 4).
+// All products use the 32x32x16 bf16 matrix core, which on gfx950 runs at twice the rate of
+// the 16x16 shapes.
+//  * logits: S^T (32 rows x 32 heads) = KV_tile . Q^T, the Dqk/16 steps split over the four
+//    wavefronts (each keeps its steps' query fragments in registers); the four fp32 partial
+//    sums are exchanged through LDS and added in a fixed order, so every wavefront holds the
+//    same logits.  With rows as the M dimension each lane holds 16 rows of one head, which is
+//    exactly the A-operand layout of the value product.
+//  * online softmax in fp32, computed identically by every wavefront: base-2 exponentials
+//    (log2(e) folded into the scale), one permlane swap per reduction; the running sum adds
+//    the bf16-rounded probabilities, so the normalisation matches what the value product sees.
+//    The reference maximum moves only when a head's maximum exceeds it by more than 2^8 (the
+//    result is the same for any reference; this only bounds the exponentials), so the output
+//    accumulators are normally never rescaled.
+//  * values: each wavefront accumulates O (32 heads x Dv/4 columns) += P . V; each B operand
+//    (8 rows of one column per lane) comes from two LDS transpose reads (ds_read_b64_tr_b16).
+//  * several workgroups per query row (decode with few rows) write fp32 partials that a
+//    combine kernel merges with log-sum-exp weights.
 #include <algorithm>
 
 #include "lsa_internal.h"
@@ -32,25 +39,44 @@
 namespace lsa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kTile = 32;       // latent rows per tile
-constexpr int kHeadGroup = 32;  // heads per workgroup (matrix-core M)
+constexpr int kThreads = 256;     // 4 wavefronts
+constexpr int kTile = 32;         // latent rows per tile
+constexpr int kStages = 3;        // LDS ring depth (two tiles in flight)
+constexpr int kHeadGroup = 32;    // heads per workgroup (matrix-core M/N)
 constexpr int kMaxSplits = 64;
+constexpr int kMaxRowsPerSplit = 2048;  // row positions of a split staged in LDS
+constexpr float kRescaleSlack = 8.0f;   // log2 units the running max may exceed the reference
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
 template <int DQK, int DV>
 struct Cfg {
-  static constexpr int NC = DQK / 16;           // matrix-core steps over Dqk
-  static constexpr int NCW = (NC + 3) / 4;      // steps per wavefront (max)
-  static constexpr int NB = DV / 32;            // 32-column output blocks
-  static constexpr int NBW = (NB + 3) / 4;      // output blocks per wavefront (max)
-  static constexpr int PITCH = DQK + 8;         // LDS row pitch in bf16 elements
-  static constexpr int CPR = DQK / 8;           // 16-byte pieces per latent row
-  static constexpr int TILE_PIECES = kTile * CPR;
-  static constexpr int PPT = (TILE_PIECES + kThreads - 1) / kThreads;  // pieces per thread
+  static constexpr int UNITS = DQK / 8;                  // 16-byte units per latent row
+  static constexpr int KS = DQK / 16;                    // 32x32x16 steps over Dqk
+  static constexpr int KSW = (KS + 3) / 4;               // steps per wavefront (max)
+  static constexpr int NB = DV / 32;                     // 32-column output blocks
+  static constexpr int NBW = (NB + 3) / 4;               // blocks per wavefront (max)
+  static constexpr int QUARTER_UNITS = 8 * UNITS;        // 8 rows, loaded by one wavefront
+  static constexpr int DPW = (QUARTER_UNITS + kWave - 1) / kWave;  // DMA instr. per wavefront
+  static constexpr int REGION = DPW * kWave;             // LDS units per 8-row region (padded)
+  static constexpr int STAGE_UNITS = 4 * REGION;
   static_assert(DQK % 16 == 0 && DV % 32 == 0 && DV <= DQK, "unsupported head dims");
-  static_assert(((PITCH * 2 / 16) & 1) == 1, "pitch must be an odd number of 16-byte units");
+  // LDS unit holding logical unit c of tile row r (rows rotated by r units)
+  __device__ static constexpr int slot(int r, int c) {
+    int u = c + r % UNITS;
+    u -= u >= UNITS ? UNITS : 0;
+    return (r >> 3) * REGION + (r & 7) * UNITS + u;
+  }
+  // logical unit stored at LDS unit u of row r
+  __device__ static constexpr int logical(int r, int u) {
+    int c = u - (r % UNITS);
+    return c < 0 ? c + UNITS : c;
+  }
 };
 
 struct MlaParams {
@@ -65,16 +91,56 @@ struct MlaParams {
   uint16_t* out;
   float* lse;
   float* ws_o;   // [rows][hgroups][splits][32][DV] partial outputs
-  float* ws_ml;  // [rows][hgroups][splits][32][2]  running max (base 2) and sum
+  float* ws_ml;  // [rows][hgroups][splits][32][2]  reference max (base 2) and sum
 };
 
-template <int DQK, int DV>
-__global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
-  using C = Cfg<DQK, DV>;
-  __shared__ __attribute__((aligned(16))) uint16_t kvt[kTile * C::PITCH];
-  __shared__ __attribute__((aligned(16))) float spart[4][4][kWave][4];
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// One LDS-DMA load: each lane's 16 bytes at `src` land at LDS byte address
+// lds_base + 16 * lane.  It is issued from inline assembly on purpose: the compiler's waitcnt
+// pass would otherwise treat every later LDS transpose read as possibly aliasing an unfinished
+// DMA and drain the whole ring (vmcnt(0)) before it.  This kernel tracks the ring itself with
+// explicit vmcnt waits and barriers, and uses M0 for nothing else.  The instruction has no
+// destination registers.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_base)
+               : "memory");
+}
+
+// Workgroup barrier for the DMA ring.  __syncthreads() also releases this wavefront's pending
+// global->LDS DMA writes, i.e. waits for vmcnt(0), which would drain the ring every step.  Here
+// the caller has already waited for exactly the DMA loads the next phase reads (wait_vmcnt<N>),
+// so only this wavefront's own LDS accesses are drained before the hardware barrier.  The empty
+// asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Value of lane ^ 32 via the gfx950 permlane swap (VALU, no LDS round trip).
+__device__ __forceinline__ float xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(((threadIdx.x >> 5) & 1) ? r[0] : r[1]);
+}
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams P) {
+  using C = Cfg<DQK, DV>;
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[kStages][C::STAGE_UNITS * 8];
+  __shared__ __attribute__((aligned(16))) float spart[4][4][kWave][4];  // partial logits
+  __shared__ int32_t slice[kMaxRowsPerSplit];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
   const int col = lane & 31, g = lane >> 5;
   int bid = blockIdx.x;
   const int split = bid % P.splits;
@@ -83,200 +149,259 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
   const int row = bid / P.hgroups;
   const int b = row / P.Lq;
   const int n = min(P.seqlens[b] - P.Lq + (row - b * P.Lq) + 1, P.S_max);
-  const int32_t* ilist = P.indices ? P.indices + static_cast<size_t>(row) * P.topk : nullptr;
-  const int cnt = ilist ? min(P.n_sel[row], P.topk) : max(n, 0);
+  const bool sparse = P.indices != nullptr;
+  const int cnt = sparse ? min(P.n_sel[row], P.topk) : max(n, 0);
   const int j0 = split * P.kps;
   const int j1 = min(cnt, j0 + P.kps);
+  const int ntiles = j1 > j0 ? (j1 - j0 + kTile - 1) / kTile : 0;
   const uint16_t* kv_b = P.kv + static_cast<size_t>(b) * P.S_max * DQK;
 
+  // this split's row positions (clamped into the cache) staged in LDS
+  if (sparse) {
+    const int32_t* ilist = P.indices + static_cast<size_t>(row) * P.topk;
+    for (int j = tid; j < j1 - j0; j += kThreads) slice[j] = min(max(ilist[j0 + j], 0), P.S_max - 1);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // DMA pieces of this wavefront: rows 8*wave .. 8*wave+7 of each tile
+  int dma_rr[C::DPW], dma_c[C::DPW];
+#pragma unroll
+  for (int k = 0; k < C::DPW; ++k) {
+    const int u = k * kWave + lane;
+    const int rr = u < C::QUARTER_UNITS ? u / C::UNITS : 0;  // padding re-reads row 0, unit 0
+    const int us = u < C::QUARTER_UNITS ? u - rr * C::UNITS : 0;
+    dma_rr[k] = rr;
+    dma_c[k] = u < C::QUARTER_UNITS ? C::logical(8 * wave + rr, us) : 0;
+  }
+  auto issue = [&](int tile) {
+    uint16_t* stage = ring[tile % kStages];
+    const int jb = tile * kTile + 8 * wave;  // relative to j0
+    int pos[C::DPW];
+#pragma unroll
+    for (int k = 0; k < C::DPW; ++k) {
+      const int j = min(jb + dma_rr[k], j1 - j0 - 1);  // rows past the slice repeat its last row
+      pos[k] = sparse ? slice[j] : j0 + j;
+    }
+#pragma unroll
+    for (int k = 0; k < C::DPW; ++k) {
+      const uint16_t* src = kv_b + static_cast<size_t>(pos[k]) * DQK + 8 * dma_c[k];
+      dma16(src, static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                     (lds_void*)(stage + (wave * C::REGION + k * kWave) * 8))));
+    }
+  };
+
+  if (ntiles > 0) issue(0);
   // query fragments of this wavefront's Dqk steps (B operand: column = head, k = 8g..8g+7)
   const int head = hg * kHeadGroup + col;
-  bf16x8 qf[C::NCW];
+  bf16x8 qf[C::KSW];
 #pragma unroll
-  for (int cc = 0; cc < C::NCW; ++cc) {
-    const int c = wave + 4 * cc;
-    qf[cc] = (head < P.H && c < C::NC)
-                 ? load_bf16x8(P.q + (static_cast<size_t>(row) * P.H + head) * DQK + 16 * c + 8 * g)
-                 : zero_bf16x8();
+  for (int i = 0; i < C::KSW; ++i) {
+    const int ks = wave + 4 * i;
+    qf[i] = (head < P.H && ks < C::KS)
+                ? load_bf16x8(P.q + (static_cast<size_t>(row) * P.H + head) * DQK + 16 * ks + 8 * g)
+                : zero_bf16x8();
   }
+  // retire the query loads here (this also lands the first tile): a wait left to the compiler
+  // would sit inside the loop and drain the ring on every step
+  wait_vmcnt<0>();
+  if (ntiles > 1) issue(1);
 
-  float m_run = -INFINITY, l_run = 0.0f;  // for head `col` (same in both lane halves)
+  float m_ref = -INFINITY, l_run = 0.0f;  // for head `col` (identical in every wavefront)
   f32x16 o[C::NBW];
 #pragma unroll
   for (int i = 0; i < C::NBW; ++i) o[i] = f32x16{};
 
-  u32x4 stg[C::PPT];
-  auto gather = [&](int tile) {
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 2 < ntiles) issue(t + 2);
+    const int ahead = min(2, ntiles - 1 - t);  // tiles issued after this one
+    if (ahead >= 2) wait_vmcnt<2 * C::DPW>();
+    else if (ahead == 1) wait_vmcnt<C::DPW>();
+    else wait_vmcnt<0>();
+    ring_barrier();  // every wavefront's pieces of tile t are in LDS
+
+    const uint16_t* kvt = ring[t % kStages];
+    // ---- partial logits over this wavefront's Dqk steps: lane = (head col, rows acc_row(r, g))
+    {
+      f32x16 acc = {};
 #pragma unroll
-    for (int k = 0; k < C::PPT; ++k) {
-      const int piece = tid + kThreads * k;
-      stg[k] = u32x4{0, 0, 0, 0};
-      if (piece < C::TILE_PIECES) {
-        const int r = piece / C::CPR;
-        const int pc = piece - r * C::CPR;
-        const int j = tile + r;
-        if (j < j1) {
-          int s = ilist ? ilist[j] : j;
-          s = min(max(s, 0), P.S_max - 1);
-          stg[k] = *reinterpret_cast<const u32x4*>(kv_b + static_cast<size_t>(s) * DQK + 8 * pc);
+      for (int i = 0; i < C::KSW; ++i) {
+        const int ks = wave + 4 * i;
+        if (ks < C::KS) {
+          const bf16x8 a = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(&kvt[C::slot(col, 2 * ks + g) * 8]));
+          acc = mfma32(a, qf[i], acc);
         }
       }
-    }
-  };
-
-  if (j0 < j1) gather(j0);
-  for (int tile = j0; tile < j1; tile += kTile) {
-    __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
-    for (int k = 0; k < C::PPT; ++k) {
-      const int piece = tid + kThreads * k;
-      if (piece < C::TILE_PIECES) {
-        const int r = piece / C::CPR;
-        const int pc = piece - r * C::CPR;
-        *reinterpret_cast<u32x4*>(&kvt[r * C::PITCH + 8 * pc]) = stg[k];
-      }
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(&spart[wave][q4][lane][0]) =
+            f32x4{acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
     }
-    __syncthreads();
-    if (tile + kTile < j1) gather(tile + kTile);
-
-    // ---- logits (partial over this wavefront's Dqk steps)
-    f32x16 acc = {};
-#pragma unroll
-    for (int cc = 0; cc < C::NCW; ++cc) {
-      const int c = wave + 4 * cc;
-      if (c < C::NC) {
-        const bf16x8 a = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(&kvt[col * C::PITCH + 16 * c + 8 * g]));
-        acc = mfma32(a, qf[cc], acc);
-      }
-    }
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      *reinterpret_cast<f32x4*>(&spart[wave][q4][lane][0]) =
-          f32x4{acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
-    __syncthreads();
-    float s[16];
+    ring_barrier();  // partial logits of all wavefronts published
+    float sv[16];
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      f32x4 t = *reinterpret_cast<const f32x4*>(&spart[0][q4][lane][0]);
+      f32x4 v = *reinterpret_cast<const f32x4*>(&spart[0][q4][lane][0]);
 #pragma unroll
-      for (int w = 1; w < 4; ++w) t += *reinterpret_cast<const f32x4*>(&spart[w][q4][lane][0]);
+      for (int w = 1; w < 4; ++w) v += *reinterpret_cast<const f32x4*>(&spart[w][q4][lane][0]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[4 * q4 + e] = t[e];
+      for (int e = 0; e < 4; ++e) sv[4 * q4 + e] = v[e];
     }
 
-    // ---- online softmax for head `col` over this tile's rows acc_row(r, g)
+    // ---- online softmax for head `col` (every wavefront computes the same values)
+    const int tile_j = j0 + t * kTile;
     float mloc = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const bool ok = tile + acc_row(r, g) < j1;
-      s[r] = ok ? s[r] * P.scale_log2 : -INFINITY;
-      mloc = fmaxf(mloc, s[r]);
+      const bool ok = tile_j + acc_row(r, g) < j1;
+      sv[r] = ok ? sv[r] * P.scale_log2 : -INFINITY;
+      mloc = fmaxf(mloc, sv[r]);
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);  // finite: every tile has a valid row
-    const float alpha = exp2f(m_run - m_new);  // 0 on the first tile
-    bf16x8 pa[2];
+    mloc = fmaxf(mloc, xor32(mloc));
+    const bool grow = mloc > m_ref + kRescaleSlack;
+    if (__ballot(grow)) {
+      const float m_new = grow ? mloc : m_ref;
+      const float alpha = exp2f(m_ref - m_new);  // 0 while nothing has been accumulated
+      l_run *= alpha;
+      m_ref = m_new;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float a = __shfl(alpha, acc_row(r, g));  // heads of O held by this lane
+#pragma unroll
+        for (int i = 0; i < C::NBW; ++i) o[i][r] *= a;
+      }
+    }
+    uint32_t pw[8];
     float psum = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const uint16_t pb = bf16_bits_rne(exp2f(s[r] - m_new));
-      psum += bf16_bits_to_float(pb);
-      pa[r >> 3][r & 7] = __builtin_bit_cast(__bf16, pb);
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t lo = bf16_bits_rne(exp2f(sv[2 * i] - m_ref));
+      const uint32_t hi = bf16_bits_rne(exp2f(sv[2 * i + 1] - m_ref));
+      psum += bf16_bits_to_float(static_cast<uint16_t>(lo)) + bf16_bits_to_float(static_cast<uint16_t>(hi));
+      pw[i] = lo | (hi << 16);
     }
-    psum += __shfl_xor(psum, 32);
-    l_run = alpha * l_run + psum;
-    m_run = m_new;
+    psum += xor32(psum);
+    l_run += psum;
+    // A operand of step ks: k-slot t of lane half g is row acc_row(8ks + t, g)
+    const bf16x8 pa0 = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+    const bf16x8 pa1 = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
 
-    // ---- rescale and accumulate the value product
+    // ---- values: this wavefront's 32-column blocks nb = wave + 4i
+    {
+      const int G = lane >> 4, jl = lane & 15;  // transpose reads: 16 columns x 4 rows per group
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float a = __shfl(alpha, acc_row(r, g));
+      for (int i = 0; i < C::NBW; ++i) {
+        const int nb = wave + 4 * i;
+        if (nb < C::NB) {
+          const int dim0 = 32 * nb + 16 * (G & 1) + 4 * (jl & 3);
+          const int unit = dim0 >> 3, eoff = dim0 & 7;
 #pragma unroll
-      for (int nbw = 0; nbw < C::NBW; ++nbw) o[nbw][r] *= a;
-    }
+          for (int ks = 0; ks < 2; ++ks) {
+            u32x2 hv[2];
 #pragma unroll
-    for (int nbw = 0; nbw < C::NBW; ++nbw) {
-      const int nb = wave + 4 * nbw;
-      if (nb < C::NB) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          bf16x8 vb;
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            // the row that A's k index 8g + t refers to in step ks (rows acc_row(8ks + t, g))
-            const int vr = 16 * ks + 8 * (t >> 2) + 4 * g + (t & 3);
-            vb[t] = __builtin_bit_cast(__bf16, kvt[vr * C::PITCH + 32 * nb + col]);
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const int vr = 16 * ks + 8 * h2 + 4 * (G >> 1) + (jl >> 2);
+              hv[h2] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_s16x4*)(&kvt[C::slot(vr, unit) * 8 + eoff])));
+            }
+            o[i] = mfma32(ks ? pa1 : pa0,
+                          __builtin_bit_cast(bf16x8, u32x4{hv[0].x, hv[0].y, hv[1].x, hv[1].y}), o[i]);
           }
-          o[nbw] = mfma32(pa[ks], vb, o[nbw]);
         }
       }
     }
+    ring_barrier();  // tile t's stage and the partial logits may be overwritten
   }
+  wait_vmcnt<0>();
 
   // ---- epilogue
   if (P.splits == 1) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float lr = __shfl(l_run, acc_row(r, g));
-      const int hh = hg * kHeadGroup + acc_row(r, g);
       const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+      const int hh = hg * kHeadGroup + acc_row(r, g);
+      if (hh < P.H) {
 #pragma unroll
-      for (int nbw = 0; nbw < C::NBW; ++nbw) {
-        const int nb = wave + 4 * nbw;
-        if (nb < C::NB && hh < P.H)
-          P.out[(static_cast<size_t>(row) * P.H + hh) * DV + 32 * nb + col] =
-              bf16_bits_rne(o[nbw][r] * inv);
+        for (int i = 0; i < C::NBW; ++i) {
+          const int nb = wave + 4 * i;
+          if (nb < C::NB)
+            P.out[(static_cast<size_t>(row) * P.H + hh) * DV + 32 * nb + col] = bf16_bits_rne(o[i][r] * inv);
+        }
       }
     }
     if (wave == 0 && g == 0 && head < P.H && P.lse)
       P.lse[static_cast<size_t>(row) * P.H + head] =
-          l_run > 0.0f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+          l_run > 0.0f ? (m_ref + __log2f(l_run)) * kLn2 : -INFINITY;
   } else {
     const size_t slot = (static_cast<size_t>(row) * P.hgroups + hg) * P.splits + split;
     float* wo = P.ws_o + slot * kHeadGroup * DV;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < 16; ++r)
 #pragma unroll
-      for (int nbw = 0; nbw < C::NBW; ++nbw) {
-        const int nb = wave + 4 * nbw;
-        if (nb < C::NB) wo[acc_row(r, g) * DV + 32 * nb + col] = o[nbw][r];
+      for (int i = 0; i < C::NBW; ++i) {
+        const int nb = wave + 4 * i;
+        if (nb < C::NB) wo[acc_row(r, g) * DV + 32 * nb + col] = o[i][r];
       }
-    }
     if (wave == 0 && g == 0) {
-      P.ws_ml[slot * kHeadGroup * 2 + 2 * col] = m_run;
-      P.ws_ml[slot * kHeadGroup * 2 + 2 * col + 1] = l_run;
+      P.ws_ml[(slot * kHeadGroup + col) * 2] = m_ref;
+      P.ws_ml[(slot * kHeadGroup + col) * 2 + 1] = l_run;
     }
   }
 }
 
-// Merge the split partials of one (row, head): log-sum-exp weights in a fixed order.
+// Merge the split partials of one (row, head) with log-sum-exp weights, in a fixed order.
+// All partial maxima are read first, then every thread streams its 4 output columns of all
+// splits with independent loads.
 template <int DV>
 __global__ __launch_bounds__(128) void mla_combine_kernel(MlaParams P) {
+  __shared__ float wsh[kMaxSplits];
+  __shared__ float Lsh;
   const int row = blockIdx.x / P.H;
   const int head = blockIdx.x - row * P.H;
   const int hg = head / kHeadGroup, hl = head - hg * kHeadGroup;
   const size_t slot0 = (static_cast<size_t>(row) * P.hgroups + hg) * P.splits;
-  float mmax = -INFINITY;
-  for (int s = 0; s < P.splits; ++s) mmax = fmaxf(mmax, P.ws_ml[(slot0 + s) * kHeadGroup * 2 + 2 * hl]);
-  float L = 0.0f;
-  for (int s = 0; s < P.splits; ++s) {
-    const float ms = P.ws_ml[(slot0 + s) * kHeadGroup * 2 + 2 * hl];
-    const float ls = P.ws_ml[(slot0 + s) * kHeadGroup * 2 + 2 * hl + 1];
-    L += ms == -INFINITY ? 0.0f : exp2f(ms - mmax) * ls;
-  }
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  for (int c = threadIdx.x; c < DV; c += blockDim.x) {
-    float acc = 0.0f;
-    for (int s = 0; s < P.splits; ++s) {
-      const float ms = P.ws_ml[(slot0 + s) * kHeadGroup * 2 + 2 * hl];
-      if (ms != -INFINITY)
-        acc += exp2f(ms - mmax) * P.ws_o[((slot0 + s) * kHeadGroup + hl) * DV + c];
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const bool has = tid < P.splits;
+    const float ms = has ? P.ws_ml[(slot0 + tid) * kHeadGroup * 2 + 2 * hl] : -INFINITY;
+    const float ls = has ? P.ws_ml[(slot0 + tid) * kHeadGroup * 2 + 2 * hl + 1] : 0.0f;
+    float mmax = ms;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off));
+    const float wgt = (ms == -INFINITY) ? 0.0f : exp2f(ms - mmax);
+    float L = wgt * ls;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+    if (has) wsh[tid] = wgt;
+    if (tid == 0) {
+      Lsh = L;
+      if (P.lse)
+        P.lse[static_cast<size_t>(row) * P.H + head] =
+            L > 0.0f ? (mmax + __log2f(L)) * kLn2 : -INFINITY;
     }
-    P.out[(static_cast<size_t>(row) * P.H + head) * DV + c] = bf16_bits_rne(acc * inv);
   }
-  if (threadIdx.x == 0 && P.lse)
-    P.lse[static_cast<size_t>(row) * P.H + head] = L > 0.0f ? (mmax + __log2f(L)) * kLn2 : -INFINITY;
+  __syncthreads();
+  const float L = Lsh;
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  for (int c4 = tid; c4 < DV / 4; c4 += blockDim.x) {
+    const float* src = P.ws_o + (slot0 * kHeadGroup + hl) * DV + 4 * c4;
+    const size_t stride = static_cast<size_t>(kHeadGroup) * DV;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    int s = 0;
+    for (; s + 8 <= P.splits; s += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(src + (s + u) * stride);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += wsh[s + u] * v[u];
+    }
+    for (; s < P.splits; ++s) acc += wsh[s] * *reinterpret_cast<const f32x4*>(src + s * stride);
+    uint16_t* dst = P.out + (static_cast<size_t>(row) * P.H + head) * DV + 4 * c4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = bf16_bits_rne(acc[e] * inv);
+  }
 }
 
 struct MlaPlan {
@@ -289,9 +414,11 @@ MlaPlan make_plan(long rows, int H, int Dv, int S_max, int topk, int dense) {
   pl.hgroups = (H + kHeadGroup - 1) / kHeadGroup;
   const long keys = dense ? S_max : topk;
   const long units = rows * pl.hgroups;
-  long splits = units > 0 ? (640 + units - 1) / units : 1;
+  // one workgroup per CU is resident (LDS ring); aim to fill the 256 CUs
+  long splits = units > 0 ? (256 + units - 1) / units : 1;
   splits = std::min<long>(splits, (keys + kTile - 1) / kTile);
   splits = std::min<long>(splits, kMaxSplits);
+  if (!dense) splits = std::max<long>(splits, (keys + kMaxRowsPerSplit - 1) / kMaxRowsPerSplit);
   splits = std::max<long>(splits, 1);
   long kps = (keys + splits - 1) / splits;
   kps = ((kps + kTile - 1) / kTile) * kTile;
