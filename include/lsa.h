@@ -99,8 +99,8 @@ size_t lsa_topk_workspace_bytes(int B, int Lq, int S_max, int topk, int init_tok
  *   n_sel     int32 [B, Lq]        output
  *   workspace device buffer of at least lsa_topk_workspace_bytes(...) bytes (may be NULL when
  *             that is 0); its contents on entry do not matter.
- * Supported: 1 <= topk <= 8192, init_tokens >= 0, local_tokens >= 0,
- * init_tokens + local_tokens <= topk (else LSA_ERR_BAD_SHAPE).
+ * Supported: topk >= 1, init_tokens >= 0, local_tokens >= 0, init_tokens + local_tokens <= topk
+ * (else LSA_ERR_BAD_SHAPE); S_max <= 1048576 (else LSA_ERR_UNSUPPORTED).
  */
 lsa_status lsa_topk_select(const float* scores, const int32_t* seqlens, int B, int Lq, int S_max,
                            int topk, int init_tokens, int local_tokens, int32_t* indices,

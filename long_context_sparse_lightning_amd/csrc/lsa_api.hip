@@ -30,8 +30,6 @@ lsa_status launched(hipError_t err, const char* what) {
   return ok();
 }
 
-constexpr int kMaxTopk = 8192;
-
 }  // namespace
 
 extern "C" {
@@ -77,7 +75,8 @@ static lsa_status check_topk(int B, int Lq, int S_max, int topk, int init_tokens
     return fail(LSA_ERR_BAD_SHAPE,
                 "lsa_topk_select: need 0 <= init_tokens (%d), 0 <= local_tokens (%d), sum <= topk (%d)",
                 init_tokens, local_tokens, topk);
-  if (topk > kMaxTopk) return fail(LSA_ERR_UNSUPPORTED, "lsa_topk_select: topk=%d > %d", topk, kMaxTopk);
+  if (S_max > lsa::topk_max_positions())
+    return fail(LSA_ERR_UNSUPPORTED, "lsa_topk_select: S_max=%d > %d", S_max, lsa::topk_max_positions());
   return LSA_OK;
 }
 

@@ -56,6 +56,7 @@ hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint
                                const int32_t* seqlens, int B, int Lq, int Hi, int Di, int S_max,
                                float* scores, hipStream_t stream);
 
+int topk_max_positions();  // largest S_max the top-k kernels accept
 size_t topk_workspace_bytes(int B, int Lq, int S_max, int topk, int init_tokens, int local_tokens);
 hipError_t launch_topk(const float* scores, const int32_t* seqlens, int B, int Lq, int S_max,
                        int topk, int init_tokens, int local_tokens, int32_t* indices,

@@ -62,17 +62,17 @@ def test_topk_argument_errors_and_workspace():
     L = lsa.lib()
     p = ctypes.c_void_p(16)
     assert L.lsa_topk_select(p, p, 1, 1, 4096, 8, 5, 4, p, p, None, 0, None) == 2  # init+local>topk
-    assert L.lsa_topk_select(p, p, 1, 1, 4096, 10000, 16, 1024, p, p, None, 0, None) == 3
+    # positions beyond the LDS bitmap of one row are rejected
+    assert L.lsa_topk_select(p, p, 1, 1, (1 << 20) + 1, 2048, 16, 1024, p, p, None, 0, None) == 3
+    assert "S_max" in _err()
     assert L.lsa_topk_select(None, p, 1, 1, 4096, 256, 4, 64, p, p, None, 0, None) == 1
-    # a row longer than one chunk needs workspace
     need = L.lsa_topk_workspace_bytes(32, 1, 131072, 2048, 16, 1024)
     assert need > 0
     assert L.lsa_topk_select(p, p, 32, 1, 131072, 2048, 16, 1024, p, p, None, 0, None) == 4
     assert L.lsa_topk_select(p, p, 32, 1, 131072, 2048, 16, 1024, p, p, p, need - 1, None) == 4
     assert "need" in _err()
-    # one chunk per row: no workspace at all
-    assert L.lsa_topk_workspace_bytes(8, 1, 16384, 2048, 16, 1024) == 0
     assert L.lsa_topk_workspace_bytes(1, 1, 4096, 8, 5, 4) == 0  # invalid -> 0
+    assert L.lsa_topk_workspace_bytes(1, 1, (1 << 20) + 1, 2048, 16, 1024) == 0
 
 
 def test_mla_argument_errors_and_workspace():
