@@ -50,6 +50,14 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 
 __device__ __forceinline__ uint64_t wave_ballot(bool pred) { return __ballot(pred); }
 
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).  The compiler
+// folds it into its own wait tracking, so later waits count from here.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // ------------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error; arguments were validated by the C-ABI layer.
 hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,

@@ -94,13 +94,6 @@ struct MlaParams {
   float* ws_ml;  // [rows][hgroups][splits][32][2]  reference max (base 2) and sum
 };
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // One LDS-DMA load: each lane's 16 bytes at `src` land at LDS byte address
 // lds_base + 16 * lane.  It is issued from inline assembly on purpose: the compiler's waitcnt
 // pass would otherwise treat every later LDS transpose read as possibly aliasing an unfinished
