@@ -69,9 +69,12 @@ def cpu_baseline(wl, sample_rows):
     import oracle
     from long_context_sparse_lightning_amd.workloads import host_kv_rows, host_slice
 
-    rows = [(b, i) for b in range(wl.B) for i in range(wl.Lq)]
-    step = max(1, len(rows) // sample_rows)
-    rows = rows[::step][:sample_rows]
+    every = [(b, i) for b in range(wl.B) for i in range(wl.Lq)]
+    if sample_rows >= len(every):  # whole steps, repeated
+        rows = [every[j % len(every)] for j in range(sample_rows)]
+    else:
+        step = max(1, len(every) // sample_rows)
+        rows = every[::step][:sample_rows]
     # inputs first (not timed)
     prepared = []
     for b, i in rows:
@@ -98,9 +101,9 @@ def cpu_baseline(wl, sample_rows):
                               np.array([[m]], np.int32), np.array([m], np.int32), wl.Dv, wl.scale)
         t_total += time.perf_counter() - t0
     return {"value": len(rows) / t_total, "unit": "queries/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(rows)} of {wl.B * wl.Lq} query rows of {wl.name} (full indexer scan, "
-                      f"top-k and {wl.mla_calls} MLA call(s) each); {t_total:.2f} s wall on "
-                      f"{cores} threads"}
+            "sample": f"{len(rows)} query-row evaluations over the {len(every)} query rows of "
+                      f"{wl.name} (each: full indexer scan, top-k and {wl.mla_calls} MLA call(s)); "
+                      f"{t_total:.2f} s wall on {cores} threads"}
 
 
 def main():
@@ -113,6 +116,7 @@ def main():
     import torch
 
     from long_context_sparse_lightning_amd import lsa
+    from long_context_sparse_lightning_amd.pmc import load_traffic
     from long_context_sparse_lightning_amd.workloads import WORKLOADS, device_inputs
 
     wl = WORKLOADS[args.workload]
@@ -210,11 +214,12 @@ def main():
         "step_score_roundtrip_bytes": score_rt,
         "roofline": {"kernel": "lsa_index_scores", "bound": "hbm", "achieved": round(k1_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_launch_ms": round(k1_ms, 5),
+                     "traffic": load_traffic(wl.name), "avg_launch_ms": round(k1_ms, 5),
                      "alg_bytes_per_launch": k1_bytes},
     }
     if not args.no_cpu_baseline:
-        sample = args.cpu_sample or (16 if wl.decode else 64)
+        # about 10 s of oracle work: three passes over the 32 decode rows of the 128K step
+        sample = args.cpu_sample or (3 * B * Lq if wl.decode and B * Lq <= 64 else 64)
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, sample)
     print(json.dumps(line), flush=True)
