@@ -8,28 +8,27 @@
 // kernel: a prefill chunk is B*Lq independent query rows, each with its own selection.
 //
 // Design for gfx950.  A workgroup owns one (query row, group of 32 heads, slice of the selected
-// rows) and runs four wavefronts.  The slice is cut into 32-row tiles that stream through a
+// rows) and runs four wavefronts; its LDS stays under 80 KB so that two workgroups share a CU
+// and hide each other's latency.  The slice is cut into 16-row tiles that stream through a
 // 3-stage LDS ring filled by LDS-DMA loads (global_load_lds_dwordx4: a lane names one 16-byte
-// piece of a latent row and the hardware writes it straight into LDS), so two tiles are in
-// flight while one is computed, without holding any of it in registers.  Every 1152-byte row
-// is read whole by consecutive lanes.  Within LDS, tile row r is rotated by r 16-byte units,
-// which spreads both access patterns below over the LDS banks (measured by a bank model: at
-// most 5 lanes per 4-bank group for the fragment reads, ideal 4).
-// All products use the 32x32x16 bf16 matrix core, which on gfx950 runs at twice the rate of
-// the 16x16 shapes.
-//  * logits: S^T (32 rows x 32 heads) = KV_tile . Q^T, the Dqk/16 steps split over the four
-//    wavefronts (each keeps its steps' query fragments in registers); the four fp32 partial
-//    sums are exchanged through LDS and added in a fixed order, so every wavefront holds the
-//    same logits.  With rows as the M dimension each lane holds 16 rows of one head, which is
-//    exactly the A-operand layout of the value product.
+// piece of a latent row and the hardware writes it straight into LDS), so one to two tiles are
+// in flight while one is computed, without holding any of it in registers.  Every 1152-byte
+// row is read whole by consecutive lanes.  Within LDS, tile row r is rotated by r 16-byte
+// units, which keeps every access pattern below free of bank conflicts.
+//  * logits: S (32 heads x 16 rows) = Q . KV_tile^T on the 16x16x32 bf16 matrix core, the
+//    Dqk/32 steps split over the four wavefronts (each keeps its steps' query fragments in
+//    registers).  The four fp32 partial sums are exchanged through LDS and added in a fixed
+//    order; each lane reads back exactly the 8 logits (one head, 8 rows) it needs as the A
+//    operand of the value product, so every wavefront holds the same logits.
 //  * online softmax in fp32, computed identically by every wavefront: base-2 exponentials
 //    (log2(e) folded into the scale), one permlane swap per reduction; the running sum adds
 //    the bf16-rounded probabilities, so the normalisation matches what the value product sees.
 //    The reference maximum moves only when a head's maximum exceeds it by more than 2^8 (the
 //    result is the same for any reference; this only bounds the exponentials), so the output
 //    accumulators are normally never rescaled.
-//  * values: each wavefront accumulates O (32 heads x Dv/4 columns) += P . V; each B operand
-//    (8 rows of one column per lane) comes from two LDS transpose reads (ds_read_b64_tr_b16).
+//  * values: each wavefront accumulates O (32 heads x Dv/4 columns) += P . V with the 32x32x16
+//    matrix core (K = the tile's 16 rows); each B operand (8 rows of one column per lane) comes
+//    from two LDS transpose reads (ds_read_b64_tr_b16).
 //  * several workgroups per query row (decode with few rows) write fp32 partials that a
 //    combine kernel merges with log-sum-exp weights.
 #include <algorithm>
@@ -40,11 +39,13 @@ namespace lsa {
 namespace {
 
 constexpr int kThreads = 256;     // 4 wavefronts
-constexpr int kTile = 32;         // latent rows per tile
-constexpr int kStages = 3;        // LDS ring depth (two tiles in flight)
-constexpr int kHeadGroup = 32;    // heads per workgroup (matrix-core M/N)
+constexpr int kTile = 16;         // latent rows per tile
+constexpr int kStages = 3;        // LDS ring depth
+constexpr int kHeadGroup = 32;    // heads per workgroup
 constexpr int kMaxSplits = 64;
 constexpr int kMaxRowsPerSplit = 2048;  // row positions of a split staged in LDS
+constexpr int kPartStride = 20;   // floats per head in the partial-logit exchange (16 rows + pad)
+constexpr int kTargetWorkgroups = 512;  // two per CU
 constexpr float kRescaleSlack = 8.0f;   // log2 units the running max may exceed the reference
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -57,22 +58,22 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 template <int DQK, int DV>
 struct Cfg {
   static constexpr int UNITS = DQK / 8;                  // 16-byte units per latent row
-  static constexpr int KS = DQK / 16;                    // 32x32x16 steps over Dqk
+  static constexpr int KS = (DQK + 31) / 32;             // 16x16x32 steps over Dqk
   static constexpr int KSW = (KS + 3) / 4;               // steps per wavefront (max)
   static constexpr int NB = DV / 32;                     // 32-column output blocks
   static constexpr int NBW = (NB + 3) / 4;               // blocks per wavefront (max)
-  static constexpr int QUARTER_UNITS = 8 * UNITS;        // 8 rows, loaded by one wavefront
-  static constexpr int DPW = (QUARTER_UNITS + kWave - 1) / kWave;  // DMA instr. per wavefront
-  static constexpr int REGION = DPW * kWave;             // LDS units per 8-row region (padded)
-  static constexpr int STAGE_UNITS = 4 * REGION;
-  static_assert(DQK % 16 == 0 && DV % 32 == 0 && DV <= DQK, "unsupported head dims");
-  // LDS unit holding logical unit c of tile row r (rows rotated by r units)
+  static constexpr int TILE_UNITS = kTile * UNITS;
+  static constexpr int NI = (TILE_UNITS + kWave - 1) / kWave;  // DMA instructions per tile
+  static constexpr int DPW = (NI + 3) / 4;               // ... per wavefront
+  static constexpr int STAGE_UNITS = 4 * DPW * kWave;    // tile plus padding pieces
+  static_assert(DQK % 8 == 0 && DV % 32 == 0 && DV <= DQK, "unsupported head dims");
+  // LDS unit holding logical unit c (< UNITS) of tile row r (rows rotated by r units)
   __device__ static constexpr int slot(int r, int c) {
     int u = c + r % UNITS;
     u -= u >= UNITS ? UNITS : 0;
-    return (r >> 3) * REGION + (r & 7) * UNITS + u;
+    return r * UNITS + u;
   }
-  // logical unit stored at LDS unit u of row r
+  // logical unit stored at LDS unit u (< UNITS) of row r
   __device__ static constexpr int logical(int r, int u) {
     int c = u - (r % UNITS);
     return c < 0 ? c + UNITS : c;
@@ -125,16 +126,23 @@ __device__ __forceinline__ float xor32(float x) {
   return __uint_as_float(((threadIdx.x >> 5) & 1) ? r[0] : r[1]);
 }
 
+// D = A * B + C on the 16x16x32 bf16 matrix core.  Per lane l (c = l % 16, q = l / 16):
+//   A: row c, k = 8q .. 8q+7;  B: column c, k = 8q .. 8q+7;  C/D register r: row 4q + r, column c.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 template <int DQK, int DV>
-__global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams P) {
+__global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
   using C = Cfg<DQK, DV>;
   __shared__ __attribute__((aligned(1024))) uint16_t ring[kStages][C::STAGE_UNITS * 8];
-  __shared__ __attribute__((aligned(16))) float spart[4][4][kWave][4];  // partial logits
+  __shared__ __attribute__((aligned(16))) float spart[4][kHeadGroup * kPartStride];  // partial logits
   __shared__ int32_t slice[kMaxRowsPerSplit];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
-  const int col = lane & 31, g = lane >> 5;
+  const int col = lane & 31, g = lane >> 5;   // 32x32 layouts
+  const int c16 = lane & 15, q16 = lane >> 4;  // 16x16 layouts
   int bid = blockIdx.x;
   const int split = bid % P.splits;
   bid /= P.splits;
@@ -157,43 +165,47 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams P) {
   wait_vmcnt<0>();
   __syncthreads();
 
-  // DMA pieces of this wavefront: rows 8*wave .. 8*wave+7 of each tile
-  int dma_rr[C::DPW], dma_c[C::DPW];
+  // DMA pieces of this wavefront: instruction k covers tile units (4k + wave) * 64 + lane
+  int dma_r[C::DPW], dma_c[C::DPW];
 #pragma unroll
   for (int k = 0; k < C::DPW; ++k) {
-    const int u = k * kWave + lane;
-    const int rr = u < C::QUARTER_UNITS ? u / C::UNITS : 0;  // padding re-reads row 0, unit 0
-    const int us = u < C::QUARTER_UNITS ? u - rr * C::UNITS : 0;
-    dma_rr[k] = rr;
-    dma_c[k] = u < C::QUARTER_UNITS ? C::logical(8 * wave + rr, us) : 0;
+    const int u = (4 * k + wave) * kWave + lane;
+    const bool real = u < C::TILE_UNITS;  // padding pieces re-read row 0, unit 0
+    const int r = real ? u / C::UNITS : 0;
+    dma_r[k] = r;
+    dma_c[k] = real ? C::logical(r, u - r * C::UNITS) : 0;
   }
   auto issue = [&](int tile) {
     uint16_t* stage = ring[tile % kStages];
-    const int jb = tile * kTile + 8 * wave;  // relative to j0
+    const int jb = tile * kTile;  // relative to j0
     int pos[C::DPW];
 #pragma unroll
     for (int k = 0; k < C::DPW; ++k) {
-      const int j = min(jb + dma_rr[k], j1 - j0 - 1);  // rows past the slice repeat its last row
+      const int j = min(jb + dma_r[k], j1 - j0 - 1);  // rows past the slice repeat its last row
       pos[k] = sparse ? slice[j] : j0 + j;
     }
 #pragma unroll
     for (int k = 0; k < C::DPW; ++k) {
       const uint16_t* src = kv_b + static_cast<size_t>(pos[k]) * DQK + 8 * dma_c[k];
       dma16(src, static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-                     (lds_void*)(stage + (wave * C::REGION + k * kWave) * 8))));
+                     (lds_void*)(stage + (4 * k + wave) * kWave * 8))));
     }
   };
 
   if (ntiles > 0) issue(0);
-  // query fragments of this wavefront's Dqk steps (B operand: column = head, k = 8g..8g+7)
-  const int head = hg * kHeadGroup + col;
-  bf16x8 qf[C::KSW];
+  // query fragments of this wavefront's Dqk steps (A operand: row = head, k = dims)
+  bf16x8 qf[2][C::KSW];
 #pragma unroll
-  for (int i = 0; i < C::KSW; ++i) {
-    const int ks = wave + 4 * i;
-    qf[i] = (head < P.H && ks < C::KS)
-                ? load_bf16x8(P.q + (static_cast<size_t>(row) * P.H + head) * DQK + 16 * ks + 8 * g)
-                : zero_bf16x8();
+  for (int hb = 0; hb < 2; ++hb) {
+    const int head = hg * kHeadGroup + 16 * hb + c16;
+#pragma unroll
+    for (int i = 0; i < C::KSW; ++i) {
+      const int ks = wave + 4 * i;
+      const int dim0 = 32 * ks + 8 * q16;
+      qf[hb][i] = (head < P.H && ks < C::KS && dim0 < DQK)
+                      ? load_bf16x8(P.q + (static_cast<size_t>(row) * P.H + head) * DQK + dim0)
+                      : zero_bf16x8();
+    }
   }
   // retire the query loads here (this also lands the first tile): a wait left to the compiler
   // would sit inside the loop and drain the ring on every step
@@ -206,50 +218,64 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams P) {
   for (int i = 0; i < C::NBW; ++i) o[i] = f32x16{};
 
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 2 < ntiles) issue(t + 2);
-    const int ahead = min(2, ntiles - 1 - t);  // tiles issued after this one
-    if (ahead >= 2) wait_vmcnt<2 * C::DPW>();
-    else if (ahead == 1) wait_vmcnt<C::DPW>();
+    if (t + 1 < ntiles) wait_vmcnt<C::DPW>();  // tile t+1 may still be in flight
     else wait_vmcnt<0>();
     ring_barrier();  // every wavefront's pieces of tile t are in LDS
 
     const uint16_t* kvt = ring[t % kStages];
-    // ---- partial logits over this wavefront's Dqk steps: lane = (head col, rows acc_row(r, g))
+    // ---- partial logits over this wavefront's Dqk steps; lane = (row c16, heads 4*q16 + r)
     {
-      f32x16 acc = {};
+      f32x4 acc0 = {}, acc1 = {};
 #pragma unroll
       for (int i = 0; i < C::KSW; ++i) {
         const int ks = wave + 4 * i;
+        const int c = 4 * ks + q16;  // logical unit
         if (ks < C::KS) {
-          const bf16x8 a = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(&kvt[C::slot(col, 2 * ks + g) * 8]));
-          acc = mfma32(a, qf[i], acc);
+          const bf16x8 kb = c < C::UNITS
+                                ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                                 &kvt[C::slot(c16, c) * 8]))
+                                : zero_bf16x8();
+          acc0 = mfma16(qf[0][i], kb, acc0);
+          acc1 = mfma16(qf[1][i], kb, acc1);
         }
       }
+      float* sp = spart[wave];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<f32x4*>(&spart[wave][q4][lane][0]) =
-            f32x4{acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]};
+      for (int r = 0; r < 4; ++r) {
+        sp[(4 * q16 + r) * kPartStride + c16] = acc0[r];
+        sp[(16 + 4 * q16 + r) * kPartStride + c16] = acc1[r];
+      }
     }
     ring_barrier();  // partial logits of all wavefronts published
-    float sv[16];
+    if (t + 2 < ntiles) issue(t + 2);  // into the stage freed at the end of the previous step
+
+    // ---- logits of head `col` for the tile rows of A-operand slots e: acc_row(e, g)
+    float sv[8];
+    {
+      const float* p0 = &spart[0][col * kPartStride + 4 * g];
+      f32x4 lo = *reinterpret_cast<const f32x4*>(p0);
+      f32x4 hi = *reinterpret_cast<const f32x4*>(p0 + 8);
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      f32x4 v = *reinterpret_cast<const f32x4*>(&spart[0][q4][lane][0]);
+      for (int w = 1; w < 4; ++w) {
+        const float* pw = &spart[w][col * kPartStride + 4 * g];
+        lo += *reinterpret_cast<const f32x4*>(pw);
+        hi += *reinterpret_cast<const f32x4*>(pw + 8);
+      }
 #pragma unroll
-      for (int w = 1; w < 4; ++w) v += *reinterpret_cast<const f32x4*>(&spart[w][q4][lane][0]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sv[4 * q4 + e] = v[e];
+      for (int e = 0; e < 4; ++e) {
+        sv[e] = lo[e];
+        sv[4 + e] = hi[e];
+      }
     }
 
     // ---- online softmax for head `col` (every wavefront computes the same values)
     const int tile_j = j0 + t * kTile;
     float mloc = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const bool ok = tile_j + acc_row(r, g) < j1;
-      sv[r] = ok ? sv[r] * P.scale_log2 : -INFINITY;
-      mloc = fmaxf(mloc, sv[r]);
+    for (int e = 0; e < 8; ++e) {
+      const bool ok = tile_j + acc_row(e, g) < j1;
+      sv[e] = ok ? sv[e] * P.scale_log2 : -INFINITY;
+      mloc = fmaxf(mloc, sv[e]);
     }
     mloc = fmaxf(mloc, xor32(mloc));
     const bool grow = mloc > m_ref + kRescaleSlack;
@@ -265,10 +291,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams P) {
         for (int i = 0; i < C::NBW; ++i) o[i][r] *= a;
       }
     }
-    uint32_t pw[8];
+    uint32_t pw[4];
     float psum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const uint32_t lo = bf16_bits_rne(exp2f(sv[2 * i] - m_ref));
       const uint32_t hi = bf16_bits_rne(exp2f(sv[2 * i + 1] - m_ref));
       psum += bf16_bits_to_float(static_cast<uint16_t>(lo)) + bf16_bits_to_float(static_cast<uint16_t>(hi));
@@ -276,9 +302,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams P) {
     }
     psum += xor32(psum);
     l_run += psum;
-    // A operand of step ks: k-slot t of lane half g is row acc_row(8ks + t, g)
-    const bf16x8 pa0 = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
-    const bf16x8 pa1 = __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]});
+    // A operand: k-slot e of lane half g is tile row acc_row(e, g)
+    const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
 
     // ---- values: this wavefront's 32-column blocks nb = wave + 4i
     {
@@ -289,18 +314,14 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams P) {
         if (nb < C::NB) {
           const int dim0 = 32 * nb + 16 * (G & 1) + 4 * (jl & 3);
           const int unit = dim0 >> 3, eoff = dim0 & 7;
+          u32x2 hv[2];
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            u32x2 hv[2];
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-              const int vr = 16 * ks + 8 * h2 + 4 * (G >> 1) + (jl >> 2);
-              hv[h2] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (lds_s16x4*)(&kvt[C::slot(vr, unit) * 8 + eoff])));
-            }
-            o[i] = mfma32(ks ? pa1 : pa0,
-                          __builtin_bit_cast(bf16x8, u32x4{hv[0].x, hv[0].y, hv[1].x, hv[1].y}), o[i]);
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int vr = 8 * h2 + 4 * (G >> 1) + (jl >> 2);  // = acc_row(4*h2 + k, g) for slot k
+            hv[h2] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(&kvt[C::slot(vr, unit) * 8 + eoff])));
           }
+          o[i] = mfma32(pa, __builtin_bit_cast(bf16x8, u32x4{hv[0].x, hv[0].y, hv[1].x, hv[1].y}), o[i]);
         }
       }
     }
@@ -324,6 +345,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(MlaParams P) {
         }
       }
     }
+    const int head = hg * kHeadGroup + col;
     if (wave == 0 && g == 0 && head < P.H && P.lse)
       P.lse[static_cast<size_t>(row) * P.H + head] =
           l_run > 0.0f ? (m_ref + __log2f(l_run)) * kLn2 : -INFINITY;
@@ -407,8 +429,8 @@ MlaPlan make_plan(long rows, int H, int Dv, int S_max, int topk, int dense) {
   pl.hgroups = (H + kHeadGroup - 1) / kHeadGroup;
   const long keys = dense ? S_max : topk;
   const long units = rows * pl.hgroups;
-  // one workgroup per CU is resident (LDS ring); aim to fill the 256 CUs
-  long splits = units > 0 ? (256 + units - 1) / units : 1;
+  // two workgroups per CU are resident (LDS); aim to fill the 256 CUs twice
+  long splits = units > 0 ? (kTargetWorkgroups + units - 1) / units : 1;
   splits = std::min<long>(splits, (keys + kTile - 1) / kTile);
   splits = std::min<long>(splits, kMaxSplits);
   if (!dense) splits = std::max<long>(splits, (keys + kMaxRowsPerSplit - 1) / kMaxRowsPerSplit);
