@@ -29,8 +29,10 @@
 //  * values: each wavefront accumulates O (32 heads x Dv/4 columns) += P . V with the 32x32x16
 //    matrix core (K = the tile's 16 rows); each B operand (8 rows of one column per lane) comes
 //    from two LDS transpose reads (ds_read_b64_tr_b16).
-//  * several workgroups per query row (decode with few rows) write fp32 partials that a
-//    combine kernel merges with log-sum-exp weights.
+//  * several workgroups per query row (decode with few rows) each write their normalised
+//    partial output in bf16 (half the bytes of fp32: this traffic is written back to HBM
+//    behind later kernels) with its fp32 (max, sum); a combine kernel merges them with
+//    log-sum-exp weights in fp32.
 #include <algorithm>
 
 #include "lsa_internal.h"
@@ -91,7 +93,7 @@ struct MlaParams {
   float scale_log2;
   uint16_t* out;
   float* lse;
-  float* ws_o;   // [rows][hgroups][splits][32][DV] partial outputs
+  uint16_t* ws_o;  // [rows][hgroups][splits][32][DV] normalised partial outputs (bf16)
   float* ws_ml;  // [rows][hgroups][splits][32][2]  reference max (base 2) and sum
 };
 
@@ -351,14 +353,17 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
           l_run > 0.0f ? (m_ref + __log2f(l_run)) * kLn2 : -INFINITY;
   } else {
     const size_t slot = (static_cast<size_t>(row) * P.hgroups + hg) * P.splits + split;
-    float* wo = P.ws_o + slot * kHeadGroup * DV;
+    uint16_t* wo = P.ws_o + slot * kHeadGroup * DV;
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
+    for (int r = 0; r < 16; ++r) {
+      const float lr = __shfl(l_run, acc_row(r, g));
+      const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
 #pragma unroll
       for (int i = 0; i < C::NBW; ++i) {
         const int nb = wave + 4 * i;
-        if (nb < C::NB) wo[acc_row(r, g) * DV + 32 * nb + col] = o[i][r];
+        if (nb < C::NB) wo[acc_row(r, g) * DV + 32 * nb + col] = bf16_bits_rne(o[i][r] * inv);
       }
+    }
     if (wave == 0 && g == 0) {
       P.ws_ml[(slot * kHeadGroup + col) * 2] = m_ref;
       P.ws_ml[(slot * kHeadGroup + col) * 2 + 1] = l_run;
@@ -367,8 +372,9 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
 }
 
 // Merge the split partials of one (row, head) with log-sum-exp weights, in a fixed order.
-// All partial maxima are read first, then every thread streams its 4 output columns of all
-// splits with independent loads.
+// Partial s holds O_s / l_s (bf16) and (m_s, l_s); its weight is l_s * 2^(m_s - max).  All
+// weights are formed first, then every thread streams its 4 output columns of all splits with
+// independent loads.
 template <int DV>
 __global__ __launch_bounds__(128) void mla_combine_kernel(MlaParams P) {
   __shared__ float wsh[kMaxSplits];
@@ -385,8 +391,8 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(MlaParams P) {
     float mmax = ms;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off));
-    const float wgt = (ms == -INFINITY) ? 0.0f : exp2f(ms - mmax);
-    float L = wgt * ls;
+    const float wgt = (ms == -INFINITY) ? 0.0f : exp2f(ms - mmax) * ls;
+    float L = wgt;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
     if (has) wsh[tid] = wgt;
@@ -401,18 +407,24 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(MlaParams P) {
   const float L = Lsh;
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   for (int c4 = tid; c4 < DV / 4; c4 += blockDim.x) {
-    const float* src = P.ws_o + (slot0 * kHeadGroup + hl) * DV + 4 * c4;
+    const uint16_t* src = P.ws_o + (slot0 * kHeadGroup + hl) * DV + 4 * c4;
     const size_t stride = static_cast<size_t>(kHeadGroup) * DV;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto add = [&](float wgt, uint2 v) {
+      acc[0] += wgt * __uint_as_float(v.x << 16);
+      acc[1] += wgt * __uint_as_float(v.x & 0xffff0000u);
+      acc[2] += wgt * __uint_as_float(v.y << 16);
+      acc[3] += wgt * __uint_as_float(v.y & 0xffff0000u);
+    };
     int s = 0;
     for (; s + 8 <= P.splits; s += 8) {
-      f32x4 v[8];
+      uint2 v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(src + (s + u) * stride);
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const uint2*>(src + (s + u) * stride);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc += wsh[s + u] * v[u];
+      for (int u = 0; u < 8; ++u) add(wsh[s + u], v[u]);
     }
-    for (; s < P.splits; ++s) acc += wsh[s] * *reinterpret_cast<const f32x4*>(src + s * stride);
+    for (; s < P.splits; ++s) add(wsh[s], *reinterpret_cast<const uint2*>(src + s * stride));
     uint16_t* dst = P.out + (static_cast<size_t>(row) * P.H + head) * DV + 4 * c4;
 #pragma unroll
     for (int e = 0; e < 4; ++e) dst[e] = bf16_bits_rne(acc[e] * inv);
@@ -444,7 +456,7 @@ MlaPlan make_plan(long rows, int H, int Dv, int S_max, int topk, int dense) {
   pl.kps = static_cast<int>(std::min<long>(kps, 0x7fffffffL));
   if (pl.splits > 1) {
     const size_t slots = static_cast<size_t>(units) * pl.splits;
-    pl.ws_o_bytes = (slots * kHeadGroup * Dv * 4 + 255) & ~static_cast<size_t>(255);
+    pl.ws_o_bytes = (slots * kHeadGroup * Dv * 2 + 255) & ~static_cast<size_t>(255);
     pl.ws_ml_bytes = (slots * kHeadGroup * 2 * 4 + 255) & ~static_cast<size_t>(255);
   }
   return pl;
@@ -492,7 +504,7 @@ hipError_t launch_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indi
   P.scale_log2 = softmax_scale * kLog2e;
   P.out = out;
   P.lse = lse;
-  P.ws_o = static_cast<float*>(workspace);
+  P.ws_o = static_cast<uint16_t*>(workspace);
   P.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ws_o_bytes);
   if (Dqk == 576 && Dv == 512) return launch_dims<576, 512>(P, rows, stream);
   if (Dqk == 80 && Dv == 64) return launch_dims<80, 64>(P, rows, stream);

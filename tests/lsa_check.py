@@ -2,6 +2,8 @@
 rows against the CPU oracle on the same seeded inputs (regenerated on the host)."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -23,6 +25,9 @@ def assert_attention_close(got: np.ndarray, ref: np.ndarray, what: str) -> None:
     maxref = float(np.abs(ref).max())
     maxerr = float(np.abs(err).max())
     l2 = float(np.linalg.norm(err)) / max(float(np.linalg.norm(ref)), 1e-300)
+    if os.environ.get("LSA_ERR_LOG"):  # margin report: one line per compared tensor
+        with open(os.environ["LSA_ERR_LOG"], "a") as f:
+            f.write(f"{what}\tmax_rel {maxerr / max(maxref, 1e-300):.3e}\tl2 {l2:.3e}\n")
     assert maxerr <= ATT_MAX_REL * maxref, f"{what}: max|err| {maxerr:.3e} > 1e-2*{maxref:.3e}"
     assert l2 <= ATT_L2_REL, f"{what}: relative L2 {l2:.3e} > 5e-3"
 
