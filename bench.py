@@ -6,7 +6,12 @@ Default workload: 128K-context decode, batch 32, one index + top-k pass shared b
 two attention sub-blocks (two MLA calls).  A step is one pass of the whole path over the
 batch; inputs are generated in HBM before timing.  Prints ONE JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--path fused|split]
+                  [--no-cpu-baseline]
+
+--path fused (default) runs the indexer and the top-k in one call (lsa_index_topk: the scores
+never leave the chip); --path split runs lsa_index_scores then lsa_topk_select.  Both give the
+same indices bit for bit.
 """
 from __future__ import annotations
 
@@ -27,6 +32,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_128k")
+    ap.add_argument("--path", choices=("fused", "split"), default="fused")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="query rows the oracle times (0: auto)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -59,6 +65,17 @@ def indexer_bytes(wl):
         for i in range(wl.Lq):
             n = wl.seqlens[b] - wl.Lq + i + 1
             tot += n * wl.Di * 2 + wl.Hi * wl.Di * 2 + wl.Hi * 4 + n * 4
+    return tot
+
+
+def fused_call_bytes(wl):
+    """Algorithmic bytes of one lsa_index_topk call: keys of the visible positions, the index
+    query and weights, and the indices and n_sel written."""
+    tot = 0
+    for b in range(wl.B):
+        for i in range(wl.Lq):
+            n = wl.seqlens[b] - wl.Lq + i + 1
+            tot += n * wl.Di * 2 + wl.Hi * wl.Di * 2 + wl.Hi * 4 + wl.topk * 4 + 4
     return tot
 
 
@@ -124,11 +141,17 @@ def main():
     torch.cuda.set_device(dev)
     X = device_inputs(wl, device=dev)
     B, Lq = wl.B, wl.Lq
-    scores = torch.empty(B, Lq, wl.S_max, dtype=torch.float32, device=dev)
+    scores = None if args.path == "fused" else torch.empty(B, Lq, wl.S_max, dtype=torch.float32,
+                                                             device=dev)
     idx = torch.empty(B, Lq, wl.topk, dtype=torch.int32, device=dev)
     nsel = torch.empty(B, Lq, dtype=torch.int32, device=dev)
-    tws = torch.empty(max(1, lsa.lsa_topk_workspace_bytes(B, Lq, wl.S_max, wl.topk, wl.init,
-                                                          wl.local)), dtype=torch.uint8, device=dev)
+    fused = args.path == "fused"
+    if fused:
+        tws = torch.empty(max(1, lsa.lsa_index_topk_workspace_bytes(B, Lq, wl.S_max, wl.topk, wl.init,
+                                                                    wl.local)), dtype=torch.uint8, device=dev)
+    else:
+        tws = torch.empty(max(1, lsa.lsa_topk_workspace_bytes(B, Lq, wl.S_max, wl.topk, wl.init,
+                                                              wl.local)), dtype=torch.uint8, device=dev)
     mws = torch.empty(max(1, lsa.lsa_mla_workspace_bytes(B, Lq, wl.H, wl.Dv, wl.S_max, wl.topk,
                                                          False)), dtype=torch.uint8, device=dev)
     outs = [torch.empty(B, Lq, wl.H, wl.Dv, dtype=torch.bfloat16, device=dev)
@@ -139,11 +162,16 @@ def main():
     def step(k1_events=None):
         if k1_events is not None:
             k1_events[0].record(stream)
-        lsa.lsa_index_scores(X["qidx"], X["w"], X["kidx"], X["seqlens"], scores=scores)
+        if fused:
+            lsa.lsa_index_topk(X["qidx"], X["w"], X["kidx"], X["seqlens"], wl.topk, wl.init,
+                               wl.local, indices=idx, n_sel=nsel, workspace=tws)
+        else:
+            lsa.lsa_index_scores(X["qidx"], X["w"], X["kidx"], X["seqlens"], scores=scores)
         if k1_events is not None:
             k1_events[1].record(stream)
-        lsa.lsa_topk_select(scores, X["seqlens"], wl.topk, wl.init, wl.local, indices=idx,
-                            n_sel=nsel, workspace=tws)
+        if not fused:
+            lsa.lsa_topk_select(scores, X["seqlens"], wl.topk, wl.init, wl.local, indices=idx,
+                                n_sel=nsel, workspace=tws)
         for c in range(wl.mla_calls):
             if wl.decode:
                 lsa.lsa_sparse_mla_decode(X[f"q{c}"][:, 0], X[f"kv{c}"], idx[:, 0], nsel[:, 0],
@@ -179,7 +207,7 @@ def main():
     queries = B * Lq
     value = queries * args.steps / (elapsed_ms / 1e3)
     alg, score_rt = algorithmic_bytes(wl)
-    k1_bytes = indexer_bytes(wl)
+    k1_bytes = fused_call_bytes(wl) if fused else indexer_bytes(wl)
     k1_gbs = k1_bytes / (k1_ms / 1e3) / 1e9
     step_gbs = alg / (ms_per_step / 1e3) / 1e9
 
@@ -205,16 +233,18 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded SplitMix64; dyadic index q/k, unit-variance bf16 latent cache)",
-        "config": {"workload": wl.name, "batch": B, "context": wl.S_max, "query_tokens": Lq,
+        "config": {"workload": wl.name, "path": args.path, "batch": B, "context": wl.S_max, "query_tokens": Lq,
                    "index_heads": wl.Hi, "index_dim": wl.Di, "topk": wl.topk,
                    "init_tokens": wl.init, "local_tokens": wl.local, "mla_heads": wl.H,
                    "qk_dim": wl.Dqk, "v_dim": wl.Dv, "mla_calls_per_step": wl.mla_calls},
         "hbm_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
         "step_alg_bytes": alg,
         "step_score_roundtrip_bytes": score_rt,
-        "roofline": {"kernel": "lsa_index_scores", "bound": "hbm", "achieved": round(k1_gbs, 1),
+        "roofline": {"kernel": ("lsa_index_topk (index_scores_kernel<128,true> + topk_merge_kernel)"
+                                if fused else "lsa_index_scores (index_scores_kernel<128,false>)"),
+                     "bound": "hbm", "achieved": round(k1_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic(wl.name), "avg_launch_ms": round(k1_ms, 5),
+                     "traffic": load_traffic(wl.name, args.path), "avg_launch_ms": round(k1_ms, 5),
                      "alg_bytes_per_launch": k1_bytes},
     }
     if not args.no_cpu_baseline:

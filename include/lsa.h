@@ -6,6 +6,7 @@
  *   lsa_topk_select        top-k positions with sink/window columns forced      (stage 2)
  *   lsa_sparse_mla_decode  absorbed-MLA attention over the selected latent rows (stage 3)
  *   lsa_sparse_mla_prefill the same for a chunk of Lq query tokens, causal      (stage 3)
+ * and lsa_index_topk, stages 1 and 2 in one pass without the score array.
  *
  * Sources: the page "MLX-VLM 的 LongCat-Flash-Lite-Sparse 支持LSA 稀疏注意力、n-gram
  * 融合与预填充优化解析", sections "LSA" (indexer, top-k with forced columns, dense fallback,
@@ -105,6 +106,28 @@ size_t lsa_topk_workspace_bytes(int B, int Lq, int S_max, int topk, int init_tok
 lsa_status lsa_topk_select(const float* scores, const int32_t* seqlens, int B, int Lq, int S_max,
                            int topk, int init_tokens, int local_tokens, int32_t* indices,
                            int32_t* n_sel, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace (bytes) lsa_index_topk needs for these sizes. */
+size_t lsa_index_topk_workspace_bytes(int B, int Lq, int S_max, int topk, int init_tokens,
+                                      int local_tokens);
+
+/*
+ * Indexer scores and top-k selection in one pass: the same indices and n_sel as
+ * lsa_index_scores followed by lsa_topk_select (bit for bit), without materialising the
+ * [B, Lq, S_max] score array.  Each workgroup keeps its chunk's fp32 scores on chip and emits
+ * only a superset of that chunk's contribution to the row's top scores; a merge pass makes the
+ * exact selection ("LSA" section: indexer, forced columns, argpartition, dense fallback; the
+ * fused epilogue of "预填充优化").
+ *   q_idx, w, k_idx, seqlens  as in lsa_index_scores
+ *   topk, init_tokens, local_tokens, indices, n_sel  as in lsa_topk_select
+ *   workspace  device buffer of at least lsa_index_topk_workspace_bytes(...) bytes
+ * Supported: the union of both calls' limits (Hi <= 32, Di in {32, 64, 128}, S_max <= 1048576,
+ * init_tokens + local_tokens <= topk).
+ */
+lsa_status lsa_index_topk(const void* q_idx, const float* w, const void* k_idx,
+                          const int32_t* seqlens, int B, int Lq, int Hi, int Di, int S_max, int topk,
+                          int init_tokens, int local_tokens, int32_t* indices, int32_t* n_sel,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace (bytes) lsa_sparse_mla_decode / _prefill need for these sizes (0 is possible).
  * `dense` is 1 when the call will pass indices == NULL. */

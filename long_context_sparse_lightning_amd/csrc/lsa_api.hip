@@ -103,6 +103,45 @@ lsa_status lsa_topk_select(const float* scores, const int32_t* seqlens, int B, i
                   "lsa_topk_select");
 }
 
+static lsa_status check_index(const char* fn, int B, int Lq, int Hi, int Di, int S_max) {
+  if (B < 0 || Lq < 0) return fail(LSA_ERR_BAD_SHAPE, "%s: B=%d Lq=%d must be >= 0", fn, B, Lq);
+  if (Hi <= 0 || Di <= 0 || S_max <= 0)
+    return fail(LSA_ERR_BAD_SHAPE, "%s: Hi=%d Di=%d S_max=%d must be > 0", fn, Hi, Di, S_max);
+  if (Hi > 32) return fail(LSA_ERR_UNSUPPORTED, "%s: Hi=%d > 32", fn, Hi);
+  if (Di != 32 && Di != 64 && Di != 128)
+    return fail(LSA_ERR_UNSUPPORTED, "%s: Di=%d not in {32, 64, 128}", fn, Di);
+  return LSA_OK;
+}
+
+size_t lsa_index_topk_workspace_bytes(int B, int Lq, int S_max, int topk, int init_tokens,
+                                      int local_tokens) {
+  if (check_topk(B, Lq, S_max, topk, init_tokens, local_tokens) != LSA_OK) return 0;
+  if (B == 0 || Lq == 0) return 0;
+  return lsa::index_topk_workspace_bytes(B, Lq, S_max, topk, init_tokens, local_tokens);
+}
+
+lsa_status lsa_index_topk(const void* q_idx, const float* w, const void* k_idx,
+                          const int32_t* seqlens, int B, int Lq, int Hi, int Di, int S_max, int topk,
+                          int init_tokens, int local_tokens, int32_t* indices, int32_t* n_sel,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  lsa_status st = check_index("lsa_index_topk", B, Lq, Hi, Di, S_max);
+  if (st != LSA_OK) return st;
+  st = check_topk(B, Lq, S_max, topk, init_tokens, local_tokens);
+  if (st != LSA_OK) return st;
+  if (B == 0 || Lq == 0) return ok();
+  if (!q_idx || !w || !k_idx || !seqlens || !indices || !n_sel)
+    return fail(LSA_ERR_NULL_ARG, "lsa_index_topk: NULL q_idx/w/k_idx/seqlens/indices/n_sel");
+  const size_t need = lsa::index_topk_workspace_bytes(B, Lq, S_max, topk, init_tokens, local_tokens);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(LSA_ERR_WORKSPACE, "lsa_index_topk: workspace %zu bytes at %p, need %zu",
+                workspace_bytes, workspace, need);
+  return launched(lsa::launch_index_topk(static_cast<const uint16_t*>(q_idx), w,
+                                         static_cast<const uint16_t*>(k_idx), seqlens, B, Lq, Hi, Di,
+                                         S_max, topk, init_tokens, local_tokens, indices, n_sel,
+                                         workspace, static_cast<hipStream_t>(stream)),
+                  "lsa_index_topk");
+}
+
 static lsa_status check_mla(const char* fn, int B, int Lq, int H, int Dqk, int Dv, int S_max, int topk,
                             bool dense, float softmax_scale) {
   if (B < 0 || Lq < 0) return fail(LSA_ERR_BAD_SHAPE, "%s: B=%d Lq=%d must be >= 0", fn, B, Lq);

@@ -23,7 +23,14 @@
 // Scores are staged in LDS and written with coalesced stores after the scan: a global store in
 // the loop would make the next overwrite of its data register wait for the store -- and, since
 // loads and stores share one counter, for every prefetch issued before it.
-#include "lsa_internal.h"
+//
+// Fused variant (indexer + top-k, the scores never leave the chip): instead of writing its
+// staged scores, a workgroup turns them into its chunk's top-k candidate list (a superset of
+// the chunk's contribution to the row's top R, see lsa_select.h), and the top-k merge kernel
+// finishes the selection from those lists.
+#include <algorithm>
+
+#include "lsa_select.h"
 
 namespace lsa {
 namespace {
@@ -32,19 +39,48 @@ constexpr int kThreads = 256;             // 4 wavefronts
 constexpr int kTileKeys = 32;             // keys per wavefront step
 constexpr int kWgStride = kTileKeys * 4;  // keys per workgroup step
 constexpr int kMaxKeysPerWg = 8192;       // LDS score staging: 32 KB
+constexpr int kStageItems = kMaxKeysPerWg / kThreads;  // staged scores per thread (fused epilogue)
+constexpr size_t kFusedBudget = size_t(256) << 20;     // candidate lists of one row group
 
-template <int DI>
-__global__ __launch_bounds__(kThreads) void index_scores_kernel(
-    const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
-    const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ seqlens, int Lq, int Hi,
-    int S_max, int keys_per_wg, int chunks_per_row, float* __restrict__ scores) {
+struct IndexParams {
+  const uint16_t* q_idx;
+  const float* w;
+  const uint16_t* k_idx;
+  const int32_t* seqlens;
+  int Lq, Hi, S_max;
+  int keys_per_wg, chunks_per_row;
+  float* scores;  // plain variant
+  // fused variant: rows [row0, row0 + gridDim.x / chunks_per_row), candidate lists per chunk
+  int row0, topk, init, local, R;
+  uint32_t* count;  // [group rows][chunks]
+  uint2* cand;      // [group rows][chunks][keys_per_wg]
+};
+
+template <int DI, bool FUSED>
+__global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
   constexpr int NC = DI / 16;  // matrix-core steps over the head dimension
-  const int row = blockIdx.x / chunks_per_row;
-  const int chunk = blockIdx.x - row * chunks_per_row;
+  const uint16_t* __restrict__ q_idx = P.q_idx;
+  const float* __restrict__ w = P.w;
+  const uint16_t* __restrict__ k_idx = P.k_idx;
+  const int32_t* __restrict__ seqlens = P.seqlens;
+  const int Lq = P.Lq, Hi = P.Hi, S_max = P.S_max, keys_per_wg = P.keys_per_wg;
+  const int chunks_per_row = P.chunks_per_row;
+  const int grow = blockIdx.x / chunks_per_row;  // row within the launch
+  const int chunk = blockIdx.x - grow * chunks_per_row;
+  const int row = (FUSED ? P.row0 : 0) + grow;
   const int b = row / Lq;
   // keys visible to this query (clamped so a bad seqlens value cannot write past the row)
   const int n = min(seqlens[b] - Lq + (row - b * Lq) + 1, S_max);
   const int start = chunk * keys_per_wg;
+  if constexpr (FUSED) {
+    // chunks holding no competing position produce an empty list (and skip the scan)
+    const sel::RowGeom rg = sel::row_geom(seqlens, row, Lq, S_max, P.topk, P.init, P.local);
+    const int a = max(rg.lo, start), z = min(rg.hi, start + keys_per_wg - 1);
+    if (rg.dense || P.R == 0 || z < a) {
+      if (threadIdx.x == 0) P.count[blockIdx.x] = 0u;
+      return;
+    }
+  }
   if (start >= n) return;
   const int end = min(n, start + keys_per_wg);
 
@@ -106,29 +142,77 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(
   }
   if (i < ntiles) score_tile(ka, t);
   __syncthreads();
-  float* srow = scores + static_cast<size_t>(row) * S_max + start;
-  for (int i = threadIdx.x; i < end - start; i += kThreads) srow[i] = stage[i];
+  if constexpr (!FUSED) {
+    float* srow = P.scores + static_cast<size_t>(row) * S_max + start;
+    for (int i = threadIdx.x; i < end - start; i += kThreads) srow[i] = stage[i];
+  } else {
+    __shared__ uint32_t sh[sel::chunk_scratch_words<kThreads>()];
+    const sel::RowGeom rg = sel::row_geom(seqlens, row, Lq, S_max, P.topk, P.init, P.local);
+    const int a = max(rg.lo, start), z = min(rg.hi, end - 1);  // competing positions here
+    uint32_t key[kStageItems];
+    uint32_t valid = 0;
+#pragma unroll
+    for (int j = 0; j < kStageItems; ++j) {
+      const int s = start + j * kThreads + static_cast<int>(threadIdx.x);
+      const bool ok = s >= a && s <= z;
+      key[j] = ok ? sel::order_key(stage[s - start]) : 0u;
+      valid |= (ok ? 1u : 0u) << j;
+    }
+    __syncthreads();  // the stage is reused as the histogram
+    sel::chunk_candidates<kThreads, kStageItems>(
+        key, valid, z - a + 1, P.R, start, reinterpret_cast<uint32_t*>(stage), sh,
+        P.cand + static_cast<size_t>(blockIdx.x) * keys_per_wg, P.count + blockIdx.x);
+  }
 }
 
-template <int DI>
-hipError_t launch_di(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
-                     const int32_t* seqlens, int B, int Lq, int Hi, int S_max, float* scores,
-                     hipStream_t stream) {
-  const long rows = static_cast<long>(B) * Lq;
-  // About 512 workgroups (two per CU, all resident at once) with whole workgroup steps per
-  // chunk; long chunks amortise the query/weight loads and the ramp of each workgroup.
+// Keys per workgroup: about 512 workgroups (two per CU, all resident at once) with whole
+// workgroup steps per chunk; long chunks amortise the query/weight loads and the ramp of each
+// workgroup.  The fused variant also keeps at most 128 chunks per row (the merge's limit).
+int keys_per_workgroup(long rows, int S_max, bool fused) {
   long per = (rows * S_max + 511) / 512;
+  if (fused) per = std::max<long>(per, (S_max + 127) / 128);
   per = ((per + kWgStride - 1) / kWgStride) * kWgStride;
   if (per < kWgStride) per = kWgStride;
   if (per > kMaxKeysPerWg) per = kMaxKeysPerWg;
-  const int keys_per_wg = static_cast<int>(per);
-  const int chunks = (S_max + keys_per_wg - 1) / keys_per_wg;
-  const long grid = rows * chunks;
+  return static_cast<int>(per);
+}
+
+template <int DI, bool FUSED>
+hipError_t launch_kernel(const IndexParams& P, long grid, hipStream_t stream) {
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  const size_t lds = static_cast<size_t>(keys_per_wg) * sizeof(float);
-  hipLaunchKernelGGL(index_scores_kernel<DI>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), lds,
-                     stream, q_idx, w, k_idx, seqlens, Lq, Hi, S_max, keys_per_wg, chunks, scores);
+  size_t lds = static_cast<size_t>(P.keys_per_wg) * sizeof(float);
+  if (FUSED) lds = std::max(lds, static_cast<size_t>(2 * sel::kBins) * sizeof(uint32_t));
+  hipLaunchKernelGGL((index_scores_kernel<DI, FUSED>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+                     lds, stream, P);
   return hipGetLastError();
+}
+
+template <bool FUSED>
+hipError_t launch_any(const IndexParams& P, int Di, long grid, hipStream_t stream) {
+  switch (Di) {
+    case 32: return launch_kernel<32, FUSED>(P, grid, stream);
+    case 64: return launch_kernel<64, FUSED>(P, grid, stream);
+    case 128: return launch_kernel<128, FUSED>(P, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+struct FusedPlan {
+  int keys_per_wg = kWgStride, chunks = 1;
+  long rows = 0, group = 1;
+  size_t count_bytes = 0, cand_bytes = 0;
+};
+
+FusedPlan fused_plan(int B, int Lq, int S_max) {
+  FusedPlan pl;
+  pl.rows = static_cast<long>(B) * Lq;
+  pl.keys_per_wg = keys_per_workgroup(pl.rows, S_max, true);
+  pl.chunks = (S_max + pl.keys_per_wg - 1) / pl.keys_per_wg;
+  const size_t per_row = static_cast<size_t>(pl.chunks) * pl.keys_per_wg * sizeof(uint2);
+  pl.group = std::max<long>(1, std::min<long>(pl.rows, static_cast<long>(kFusedBudget / per_row)));
+  pl.count_bytes = (static_cast<size_t>(pl.group) * pl.chunks * 4 + 255) & ~static_cast<size_t>(255);
+  pl.cand_bytes = static_cast<size_t>(pl.group) * per_row;
+  return pl;
 }
 
 }  // namespace
@@ -136,12 +220,63 @@ hipError_t launch_di(const uint16_t* q_idx, const float* w, const uint16_t* k_id
 hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
                                const int32_t* seqlens, int B, int Lq, int Hi, int Di, int S_max,
                                float* scores, hipStream_t stream) {
-  switch (Di) {
-    case 32: return launch_di<32>(q_idx, w, k_idx, seqlens, B, Lq, Hi, S_max, scores, stream);
-    case 64: return launch_di<64>(q_idx, w, k_idx, seqlens, B, Lq, Hi, S_max, scores, stream);
-    case 128: return launch_di<128>(q_idx, w, k_idx, seqlens, B, Lq, Hi, S_max, scores, stream);
-    default: return hipErrorInvalidValue;
+  const long rows = static_cast<long>(B) * Lq;
+  IndexParams P{};
+  P.q_idx = q_idx;
+  P.w = w;
+  P.k_idx = k_idx;
+  P.seqlens = seqlens;
+  P.Lq = Lq;
+  P.Hi = Hi;
+  P.S_max = S_max;
+  P.keys_per_wg = keys_per_workgroup(rows, S_max, false);
+  P.chunks_per_row = (S_max + P.keys_per_wg - 1) / P.keys_per_wg;
+  P.scores = scores;
+  return launch_any<false>(P, Di, rows * P.chunks_per_row, stream);
+}
+
+size_t index_topk_workspace_bytes(int B, int Lq, int S_max, int topk, int init_tokens, int local_tokens) {
+  (void)topk;
+  (void)init_tokens;
+  (void)local_tokens;
+  const FusedPlan pl = fused_plan(B, Lq, S_max);
+  return pl.count_bytes + pl.cand_bytes;
+}
+
+hipError_t launch_index_topk(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+                             const int32_t* seqlens, int B, int Lq, int Hi, int Di, int S_max,
+                             int topk, int init_tokens, int local_tokens, int32_t* indices,
+                             int32_t* n_sel, void* workspace, hipStream_t stream) {
+  const FusedPlan pl = fused_plan(B, Lq, S_max);
+  if (pl.chunks > topk_merge_max_chunks()) return hipErrorInvalidConfiguration;
+  IndexParams P{};
+  P.q_idx = q_idx;
+  P.w = w;
+  P.k_idx = k_idx;
+  P.seqlens = seqlens;
+  P.Lq = Lq;
+  P.Hi = Hi;
+  P.S_max = S_max;
+  P.keys_per_wg = pl.keys_per_wg;
+  P.chunks_per_row = pl.chunks;
+  P.topk = topk;
+  P.init = init_tokens;
+  P.local = local_tokens;
+  P.R = topk - init_tokens - local_tokens;
+  char* ws = static_cast<char*>(workspace);
+  P.count = reinterpret_cast<uint32_t*>(ws);
+  P.cand = reinterpret_cast<uint2*>(ws + pl.count_bytes);
+  for (long r0 = 0; r0 < pl.rows; r0 += pl.group) {
+    const long g = std::min(pl.group, pl.rows - r0);
+    P.row0 = static_cast<int>(r0);
+    hipError_t err = launch_any<true>(P, Di, g * pl.chunks, stream);
+    if (err != hipSuccess) return err;
+    err = launch_topk_merge(seqlens, Lq, S_max, topk, init_tokens, local_tokens, static_cast<int>(r0),
+                            static_cast<int>(g), pl.chunks, pl.keys_per_wg, P.count, P.cand, indices,
+                            n_sel, stream);
+    if (err != hipSuccess) return err;
   }
+  return hipSuccess;
 }
 
 }  // namespace lsa

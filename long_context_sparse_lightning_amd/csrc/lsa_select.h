@@ -1,0 +1,188 @@
+// Device helpers of the top-k selection shared by the standalone top-k kernels and the fused
+// indexer + top-k kernel (not installed).
+//
+// Scores are ranked through order-preserving uint32 keys: a larger float gives a larger key,
+// and -0 and +0 give the same key.  A chunk keeps a superset of its own top R keys (every key
+// whose digit is at least the digit of its R-th largest), where a digit is a window of key bits
+// placed from the chunk's key range: (k >> s) - (min >> s) takes at most 2^11 + 1 values, so
+// scores concentrated in a narrow range still spread over the LDS histogram.
+#pragma once
+
+#include "lsa_internal.h"
+
+namespace lsa {
+namespace sel {
+
+constexpr int kBins = 4096;  // histogram bins (digits are at most 2^11)
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) == 0u) return 0x80000000u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Positions of one query row as the selection sees them.
+struct RowGeom {
+  int n, p;    // visible keys, query position
+  bool dense;  // n <= topk: keep everything
+  int lo, hi;  // middle positions [lo, hi] that compete for the free slots (empty if dense)
+};
+
+__device__ __forceinline__ RowGeom row_geom(const int32_t* seqlens, int row, int Lq, int S_max,
+                                            int topk, int I, int W) {
+  RowGeom g;
+  const int b = row / Lq;
+  g.n = min(seqlens[b] - Lq + (row - b * Lq) + 1, S_max);
+  g.p = g.n - 1;
+  g.dense = g.n <= topk;
+  g.lo = I;
+  g.hi = g.dense ? I - 1 : g.p - W;
+  return g;
+}
+
+// Which bin holds the target-th largest item: thread t owns bins [PER*t, PER*t + PER) with
+// counts c; afterwards out[0] = that bin, out[1] = the number of items in higher bins and
+// out[2] = the items in that bin.  Requires 1 <= target <= the sum of all counts.  Two barriers.
+template <int PER, int WAVES>
+__device__ void select_bin(const uint32_t (&c)[PER], uint32_t target, uint32_t* sh_scan,
+                           uint32_t* out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) mine += c[i];
+  uint32_t x = mine;  // inclusive suffix sum over the lanes of this wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_down(x, off);
+    if (lane + off < 64) x += y;
+  }
+  if (lane == 0) sh_scan[wave] = x;
+  __syncthreads();
+  uint32_t acc = x - mine;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) acc += w > wave ? sh_scan[w] : 0u;
+#pragma unroll
+  for (int i = PER - 1; i >= 0; --i) {
+    if (acc < target && acc + c[i] >= target) {
+      out[0] = static_cast<uint32_t>(PER * tid + i);
+      out[1] = acc;
+      out[2] = c[i];
+    }
+    acc += c[i];
+  }
+  __syncthreads();
+}
+
+// Exclusive prefix of a per-thread count over the workgroup, and the total.  One barrier.
+template <int WAVES>
+__device__ __forceinline__ uint32_t block_prefix(uint32_t mine, uint32_t* sh_scan, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sh_scan[wave] = x;
+  __syncthreads();
+  uint32_t at = x - mine, t = 0;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) {
+    at += w < wave ? sh_scan[w] : 0u;
+    t += sh_scan[w];
+  }
+  *total = t;
+  return at;
+}
+
+// Minimum and maximum of per-thread values over the workgroup.  One barrier; sh holds 2*WAVES.
+template <int WAVES>
+__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_t* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    mn = min(mn, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mn), off)));
+    mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), off)));
+  }
+  if (lane == 0) {
+    sh[wave] = mn;
+    sh[WAVES + wave] = mx;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) {
+    mn = min(mn, sh[w]);
+    mx = max(mx, sh[WAVES + w]);
+  }
+}
+
+// Shift s for keys in [mn, mx] such that (k >> s) - (mn >> s) <= 2^11 for all of them.
+__device__ __forceinline__ int digit_shift(uint32_t mn, uint32_t mx) {
+  const uint32_t d = mx - mn;
+  const int bits = d ? 32 - __clz(static_cast<int>(d)) : 0;
+  return max(0, bits - 11);
+}
+
+// LDS words chunk_candidates needs besides its histogram.
+template <int THREADS>
+constexpr int chunk_scratch_words() { return 3 * (THREADS / kWave) + 4; }
+
+// Candidates of one chunk: item j of this thread (bit j of `valid`) holds the key at position
+// base + j*THREADS + threadIdx.x; m = number of valid items in the workgroup.  Writes to `out`
+// every valid key when m <= R, else those whose digit is at least that of the chunk's R-th
+// largest (always a superset of the chunk's contribution to the row's top R), as (key,
+// position) pairs, and their number to *count.  hist: 2*kBins words of LDS, zeroed here;
+// sh: chunk_scratch_words<THREADS>() words.  Call from every thread, with m >= 1.
+template <int THREADS, int ITEMS>
+__device__ void chunk_candidates(const uint32_t (&key)[ITEMS], uint32_t valid, int m, int R,
+                                 int base, uint32_t* hist, uint32_t* sh, uint2* out,
+                                 uint32_t* count) {
+  constexpr int WAVES = THREADS / kWave;
+  uint32_t* sh_scan = sh;
+  uint32_t* sh_mm = sh + WAVES;
+  uint32_t* sh_out = sh + 3 * WAVES;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  uint32_t keep = valid;
+  if (m > R) {
+    for (int i = tid; i < 2 * kBins; i += THREADS) hist[i] = 0u;
+    uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      if (valid & (1u << j)) {
+        mn = min(mn, key[j]);
+        mx = max(mx, key[j]);
+      }
+    }
+    block_minmax<WAVES>(mn, mx, sh_mm);  // its barrier also orders the zeroing
+    const int sh_bits = digit_shift(mn, mx);
+    const uint32_t dbase = mn >> sh_bits;
+    uint32_t* hw = hist + (wave & 1) * kBins;  // one copy per half of the waves
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j)
+      if (valid & (1u << j)) atomicAdd(&hw[(key[j] >> sh_bits) - dbase], 1u);
+    __syncthreads();
+    constexpr int kPer = kBins / THREADS;
+    uint32_t c[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) c[i] = hist[kPer * tid + i] + hist[kBins + kPer * tid + i];
+    select_bin<kPer, WAVES>(c, static_cast<uint32_t>(R), sh_scan, sh_out);
+    const uint32_t dmin = sh_out[0];
+    keep = 0;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j)
+      keep |= ((valid & (1u << j)) && (key[j] >> sh_bits) - dbase >= dmin ? 1u : 0u) << j;
+  }
+  uint32_t total;
+  uint32_t at = block_prefix<WAVES>(__popc(keep), sh_scan, &total);
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    if (keep & (1u << j)) {
+      out[at] = make_uint2(key[j], static_cast<uint32_t>(base + j * THREADS + tid));
+      ++at;
+    }
+  }
+  if (tid == 0) *count = total;
+}
+
+}  // namespace sel
+}  // namespace lsa

@@ -25,152 +25,50 @@
 // Every step counts exactly, so the result does not depend on scheduling.
 #include <algorithm>
 
-#include "lsa_internal.h"
+#include "lsa_select.h"
 
 namespace lsa {
 namespace {
 
-constexpr int kBins = 4096;          // 12-bit digit histograms
-constexpr int kLowBins = 256;        // last 8-bit digit
+using sel::block_minmax;
+using sel::block_prefix;
+using sel::digit_shift;
+using sel::kBins;
+using sel::order_key;
+using sel::row_geom;
+using sel::RowGeom;
+using sel::select_bin;
+
 constexpr int kChunk = 16384;        // positions per chunk workgroup
 constexpr int kChunkThreads = 512;
 constexpr int kChunkWaves = kChunkThreads / kWave;
 constexpr int kChunkItems = kChunk / kChunkThreads;  // 32 per thread
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeWaves = kMergeThreads / kWave;
-constexpr int kRegItems = 16;        // candidates held in registers per merge thread
+constexpr int kRegItems = 20;        // candidates held in registers per merge thread
 constexpr int kMaxPositions = 1 << 20;
-constexpr int kMaxChunks = kMaxPositions / kChunk;  // 64
+constexpr int kMaxChunks = 128;      // chunk lists per row the merge accepts
 constexpr int kTieList = kMergeThreads;             // ties ranked in LDS up to this many
 constexpr size_t kWorkspaceBudget = size_t(256) << 20;
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) == 0u) return 0x80000000u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-struct RowGeom {
-  int n, p;    // visible keys, query position
-  bool dense;  // n <= topk: keep everything
-  int lo, hi;  // middle positions [lo, hi] (empty if dense)
-};
-
-__device__ __forceinline__ RowGeom row_geom(const int32_t* seqlens, int row, int Lq, int S_max,
-                                            int topk, int I, int W) {
-  RowGeom g;
-  const int b = row / Lq;
-  g.n = min(seqlens[b] - Lq + (row - b * Lq) + 1, S_max);
-  g.p = g.n - 1;
-  g.dense = g.n <= topk;
-  g.lo = I;
-  g.hi = g.dense ? I - 1 : g.p - W;
-  return g;
-}
 
 struct TopkParams {
   const float* scores;
   const int32_t* seqlens;
   int Lq, S_max, topk, init, local, R;
   int row0;          // first row of this group
-  int chunks;        // chunks per row
+  int chunks;        // chunk lists per row
+  int chunk_keys;    // positions per chunk (= capacity of its list)
   uint32_t* count;   // [group rows][chunks]
-  uint2* cand;       // [group rows][chunks][kChunk] (key, position)
+  uint2* cand;       // [group rows][chunks][chunk_keys] (key, position)
   int32_t* indices;  // [rows][topk]
   int32_t* n_sel;    // [rows]
 };
 
-// Which bin holds the target-th largest item: thread t owns bins [PER*t, PER*t + PER) with
-// counts c; afterwards out[0] = that bin, out[1] = the number of items in higher bins and
-// out[2] = the items in that bin.
-// Requires 1 <= target <= the sum of all counts.  Two barriers.
-template <int PER, int WAVES>
-__device__ void select_bin(const uint32_t (&c)[PER], uint32_t target, uint32_t* sh_scan,
-                           uint32_t* out) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t mine = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) mine += c[i];
-  uint32_t x = mine;  // inclusive suffix sum over the lanes of this wave
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_down(x, off);
-    if (lane + off < 64) x += y;
-  }
-  if (lane == 0) sh_scan[wave] = x;
-  __syncthreads();
-  uint32_t acc = x - mine;
-#pragma unroll
-  for (int w = 0; w < WAVES; ++w) acc += w > wave ? sh_scan[w] : 0u;
-#pragma unroll
-  for (int i = PER - 1; i >= 0; --i) {
-    if (acc < target && acc + c[i] >= target) {
-      out[0] = static_cast<uint32_t>(PER * tid + i);
-      out[1] = acc;
-      out[2] = c[i];
-    }
-    acc += c[i];
-  }
-  __syncthreads();
-}
-
-// Exclusive prefix of a per-thread count over the workgroup, and the total.  One barrier.
-template <int WAVES>
-__device__ __forceinline__ uint32_t block_prefix(uint32_t mine, uint32_t* sh_scan, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = mine;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) sh_scan[wave] = x;
-  __syncthreads();
-  uint32_t at = x - mine, t = 0;
-#pragma unroll
-  for (int w = 0; w < WAVES; ++w) {
-    at += w < wave ? sh_scan[w] : 0u;
-    t += sh_scan[w];
-  }
-  *total = t;
-  return at;
-}
-
-// Minimum and maximum of per-thread values over the workgroup.  One barrier; sh holds 2*WAVES.
-template <int WAVES>
-__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_t* sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    mn = min(mn, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mn), off)));
-    mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), off)));
-  }
-  if (lane == 0) {
-    sh[wave] = mn;
-    sh[WAVES + wave] = mx;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < WAVES; ++w) {
-    mn = min(mn, sh[w]);
-    mx = max(mx, sh[WAVES + w]);
-  }
-}
-
-// Shift s for keys in [mn, mx] such that (k >> s) - (mn >> s) <= 2^11 for all of them.
-__device__ __forceinline__ int digit_shift(uint32_t mn, uint32_t mx) {
-  const uint32_t d = mx - mn;
-  const int bits = d ? 32 - __clz(static_cast<int>(d)) : 0;
-  return max(0, bits - 11);
-}
-
 // ------------------------------------------------------------------ 1. per-chunk candidates
 __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(TopkParams P) {
-  __shared__ uint32_t h[2][kBins];  // one copy per half of the waves
-  __shared__ uint32_t sh_scan[kChunkWaves];
-  __shared__ uint32_t sh_mm[2 * kChunkWaves];
-  __shared__ uint32_t sh_out[4];
-  const int tid = threadIdx.x, wave = tid >> 6;
+  __shared__ uint32_t hist[2 * kBins];
+  __shared__ uint32_t sh[sel::chunk_scratch_words<kChunkThreads>()];
+  const int tid = threadIdx.x;
   const int grow = blockIdx.x / P.chunks;  // row within the group
   const int chunk = blockIdx.x - grow * P.chunks;
   const int row = P.row0 + grow;
@@ -192,49 +90,9 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(TopkParams P)
     key[j] = order_key(srow[min(max(s, a), z)]);
     valid |= ((s >= a && s <= z) ? 1u : 0u) << j;
   }
-  // keep every key when the chunk has no more than R of them, else the digits from the one
-  // holding the local R-th largest upwards
-  uint32_t keep = valid;
-  if (m > P.R) {
-    for (int i = tid; i < 2 * kBins; i += kChunkThreads) (&h[0][0])[i] = 0u;
-    uint32_t mn = 0xffffffffu, mx = 0u;
-#pragma unroll
-    for (int j = 0; j < kChunkItems; ++j) {
-      if (valid & (1u << j)) {
-        mn = min(mn, key[j]);
-        mx = max(mx, key[j]);
-      }
-    }
-    block_minmax<kChunkWaves>(mn, mx, sh_mm);  // its barrier also orders the zeroing
-    const int sh = digit_shift(mn, mx);
-    const uint32_t dbase = mn >> sh;
-    uint32_t* hw = h[wave & 1];
-#pragma unroll
-    for (int j = 0; j < kChunkItems; ++j)
-      if (valid & (1u << j)) atomicAdd(&hw[(key[j] >> sh) - dbase], 1u);
-    __syncthreads();
-    constexpr int kPer = kBins / kChunkThreads;
-    uint32_t c[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) c[i] = h[0][kPer * tid + i] + h[1][kPer * tid + i];
-    select_bin<kPer, kChunkWaves>(c, static_cast<uint32_t>(P.R), sh_scan, sh_out);
-    const uint32_t dmin = sh_out[0];
-    keep = 0;
-#pragma unroll
-    for (int j = 0; j < kChunkItems; ++j)
-      keep |= ((valid & (1u << j)) && (key[j] >> sh) - dbase >= dmin ? 1u : 0u) << j;
-  }
-  uint32_t total;
-  uint32_t at = block_prefix<kChunkWaves>(__popc(keep), sh_scan, &total);
-  uint2* out = P.cand + static_cast<size_t>(blockIdx.x) * kChunk;
-#pragma unroll
-  for (int j = 0; j < kChunkItems; ++j) {
-    if (keep & (1u << j)) {
-      out[at] = make_uint2(key[j], static_cast<uint32_t>(base + j * kChunkThreads + tid));
-      ++at;
-    }
-  }
-  if (tid == 0) P.count[blockIdx.x] = total;
+  sel::chunk_candidates<kChunkThreads, kChunkItems>(key, valid, m, P.R, base, hist, sh,
+                                                    P.cand + static_cast<size_t>(blockIdx.x) * kChunk,
+                                                    P.count + blockIdx.x);
 }
 
 // ------------------------------------------------------------------ 2. merge per row
@@ -244,6 +102,7 @@ constexpr int kMsRes = kMsScan + kMergeWaves;       // [16] results of select_bi
 constexpr int kMsCnt = kMsRes + 16;                 // [2][kMergeWaves] block_count / min-max
 constexpr int kMsOff = kMsCnt + 2 * kMergeWaves;    // [kMaxChunks + 1] candidate offsets
 constexpr int kMsHist = kMsOff + kMaxChunks + 16;   // [kBins] radix rounds, then the rank list
+static_assert(kMaxChunks <= kMergeThreads, "one thread per chunk list");
 constexpr int kMsBits = kMsHist + kBins;            // bitmap over the middle range
 static_assert(2 * kTieList <= kBins, "the rank list reuses the histogram");
 
@@ -292,22 +151,22 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
   for (int i = tid; i < mid_words; i += kMergeThreads) sh_bits[i] = 0u;
   for (int i = tid; i < kBins; i += kMergeThreads) sh_h[i] = 0u;
   if (tid == 0) sh_res[8] = 0u;  // rank-list length
-  // candidate offsets of the row's chunks (one wave: at most 64 chunks)
-  const uint32_t* cnt = P.count + static_cast<size_t>(grow) * P.chunks;
-  if (wave == 0) {
-    const uint32_t c = lane < P.chunks ? cnt[lane] : 0u;
-    uint32_t x = c;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t y = __shfl_up(x, off);
-      if (lane >= off) x += y;
+  // candidate offsets of the row's chunk lists (thread c: list c), and the longest list
+  if (tid == 0) sh_res[9] = 0u;
+  {
+    const uint32_t c = tid < P.chunks ? P.count[static_cast<size_t>(grow) * P.chunks + tid] : 0u;
+    uint32_t total;
+    const uint32_t at = block_prefix<kMergeWaves>(c, sh_scan, &total);
+    if (tid < P.chunks) {
+      sh_off[tid] = at;
+      atomicMax(&sh_res[9], c);
     }
-    sh_off[lane] = x - c;
-    if (lane == 63) sh_off[64] = x;
+    if (tid == 0) sh_off[kMaxChunks] = total;
   }
   __syncthreads();
-  const uint32_t nc = sh_off[64];
-  const uint2* crow = P.cand + static_cast<size_t>(grow) * P.chunks * kChunk;
+  const uint32_t nc = sh_off[kMaxChunks];
+  const size_t ck = static_cast<size_t>(P.chunk_keys);
+  const uint2* crow = P.cand + static_cast<size_t>(grow) * P.chunks * ck;
   // candidate q of the concatenated lists -> its pair
   auto locate = [&](uint32_t q) -> const uint2* {
     int lo = 0, hi = P.chunks - 1;  // last chunk c with sh_off[c] <= q
@@ -315,30 +174,35 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
       const int mid = (lo + hi + 1) >> 1;
       if (sh_off[mid] <= q) lo = mid; else hi = mid - 1;
     }
-    return crow + static_cast<size_t>(lo) * kChunk + (q - sh_off[lo]);
+    return crow + static_cast<size_t>(lo) * ck + (q - sh_off[lo]);
   };
-  const bool in_regs = nc <= static_cast<uint32_t>(kRegItems * kMergeThreads);
+  // in registers: list c is held by the TPL threads [c * TPL, (c + 1) * TPL), entry j of it by
+  // thread c * TPL + j % TPL in slot j / TPL -- when every list fits
+  const int tpl = kMergeThreads / P.chunks;
+  const int my_list = tid / tpl, my_j = tid - my_list * tpl;
+  const bool in_regs = sh_res[9] <= static_cast<uint32_t>(kRegItems * tpl);
   uint32_t rk[kRegItems];
   int32_t rp[kRegItems];
+  uint32_t held = 0;  // bit i: slot i holds a candidate
   if (in_regs) {
-    const uint2* src[kRegItems];
+    const uint32_t my_cnt =
+        my_list < P.chunks ? (my_list + 1 < P.chunks ? sh_off[my_list + 1] : nc) - sh_off[my_list] : 0u;
+    const uint2* lst = crow + static_cast<size_t>(my_list < P.chunks ? my_list : 0) * ck;
 #pragma unroll
-    for (int i = 0; i < kRegItems; ++i) {
-      const uint32_t q = static_cast<uint32_t>(i * kMergeThreads + tid);
-      src[i] = q < nc ? locate(q) : crow;  // crow[0] is always readable
-    }
-#pragma unroll
-    for (int i = 0; i < kRegItems; ++i) {  // all loads issued at once
-      const uint2 v = *src[i];
+    for (int i = 0; i < kRegItems; ++i) {  // all loads issued at once, from in-range addresses
+      const uint32_t j = static_cast<uint32_t>(my_j + i * tpl);
+      const bool ok = j < my_cnt;
+      const uint2 v = lst[ok ? j : 0u];
       rk[i] = v.x;
       rp[i] = static_cast<int32_t>(v.y);
+      held |= (ok ? 1u : 0u) << i;
     }
   }
   auto each = [&](auto f) {
     if (in_regs) {
 #pragma unroll
       for (int i = 0; i < kRegItems; ++i)
-        if (static_cast<uint32_t>(i * kMergeThreads + tid) < nc) f(rk[i], rp[i]);
+        if (held & (1u << i)) f(rk[i], rp[i]);
     } else {
       for (uint32_t q = tid; q < nc; q += kMergeThreads) {
         const uint2 v = *locate(q);
@@ -466,6 +330,11 @@ size_t merge_lds_bytes(int S_max) {
   return sizeof(uint32_t) * (static_cast<size_t>(kMsBits) + (S_max + 31) / 32 + 1);
 }
 
+hipError_t set_merge_lds(size_t lds) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(topk_merge_kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+}
+
 }  // namespace
 
 int topk_max_positions() { return kMaxPositions; }
@@ -480,8 +349,7 @@ hipError_t launch_topk(const float* scores, const int32_t* seqlens, int B, int L
   const Plan pl = make_plan(B, Lq, S_max, topk, init_tokens, local_tokens);
   if (pl.group * pl.chunks > 0x7fffffffL || pl.rows > 0x7fffffffL) return hipErrorInvalidConfiguration;
   const size_t lds = merge_lds_bytes(S_max);
-  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_merge_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  hipError_t err = set_merge_lds(lds);
   if (err != hipSuccess) return err;
   TopkParams P{};
   P.scores = scores;
@@ -493,6 +361,7 @@ hipError_t launch_topk(const float* scores, const int32_t* seqlens, int B, int L
   P.local = local_tokens;
   P.R = pl.R;
   P.chunks = pl.chunks;
+  P.chunk_keys = kChunk;
   char* ws = static_cast<char*>(workspace);
   P.count = reinterpret_cast<uint32_t*>(ws);
   P.cand = reinterpret_cast<uint2*>(ws + pl.count_bytes);
@@ -508,6 +377,35 @@ hipError_t launch_topk(const float* scores, const int32_t* seqlens, int B, int L
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   return hipSuccess;
+}
+
+int topk_merge_max_chunks() { return kMaxChunks; }
+
+hipError_t launch_topk_merge(const int32_t* seqlens, int Lq, int S_max, int topk, int init_tokens,
+                             int local_tokens, int row0, int rows, int chunks, int chunk_keys,
+                             uint32_t* count, uint2* cand, int32_t* indices, int32_t* n_sel,
+                             hipStream_t stream) {
+  if (chunks > kMaxChunks || rows <= 0) return hipErrorInvalidConfiguration;
+  const size_t lds = merge_lds_bytes(S_max);
+  hipError_t err = set_merge_lds(lds);
+  if (err != hipSuccess) return err;
+  TopkParams P{};
+  P.seqlens = seqlens;
+  P.Lq = Lq;
+  P.S_max = S_max;
+  P.topk = topk;
+  P.init = init_tokens;
+  P.local = local_tokens;
+  P.R = topk - init_tokens - local_tokens;
+  P.row0 = row0;
+  P.chunks = chunks;
+  P.chunk_keys = chunk_keys;
+  P.count = count;
+  P.cand = cand;
+  P.indices = indices;
+  P.n_sel = n_sel;
+  hipLaunchKernelGGL(topk_merge_kernel, dim3(static_cast<unsigned>(rows)), dim3(kMergeThreads), lds, stream, P);
+  return hipGetLastError();
 }
 
 }  // namespace lsa

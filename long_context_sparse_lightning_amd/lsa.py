@@ -20,8 +20,8 @@ STATUS = {0: "LSA_OK", 1: "LSA_ERR_NULL_ARG", 2: "LSA_ERR_BAD_SHAPE", 3: "LSA_ER
           4: "LSA_ERR_WORKSPACE", 5: "LSA_ERR_LAUNCH"}
 
 EXPORTED = ["lsa_status_str", "lsa_last_error", "lsa_index_scores", "lsa_topk_workspace_bytes",
-            "lsa_topk_select", "lsa_mla_workspace_bytes", "lsa_sparse_mla_decode",
-            "lsa_sparse_mla_prefill"]
+            "lsa_topk_select", "lsa_index_topk_workspace_bytes", "lsa_index_topk",
+            "lsa_mla_workspace_bytes", "lsa_sparse_mla_decode", "lsa_sparse_mla_prefill"]
 
 
 class LsaError(RuntimeError):
@@ -52,6 +52,10 @@ def lib():
         L.lsa_topk_workspace_bytes.restype = Z
         L.lsa_topk_select.argtypes = [P, P, I, I, I, I, I, I, P, P, P, Z, P]
         L.lsa_topk_select.restype = I
+        L.lsa_index_topk_workspace_bytes.argtypes = [I, I, I, I, I, I]
+        L.lsa_index_topk_workspace_bytes.restype = Z
+        L.lsa_index_topk.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, P, P, P, Z, P]
+        L.lsa_index_topk.restype = I
         L.lsa_mla_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
         L.lsa_mla_workspace_bytes.restype = Z
         L.lsa_sparse_mla_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, P, P, P, Z, P]
@@ -125,6 +129,35 @@ def lsa_topk_select(scores, seqlens, topk, init_tokens, local_tokens, indices=No
     _check(lib().lsa_topk_select(_ptr(scores), _ptr(seqlens), B, Lq, S_max, topk, init_tokens,
                                  local_tokens, _ptr(indices), _ptr(n_sel), _ptr(workspace), wbytes,
                                  _stream(scores)))
+    return indices, n_sel
+
+
+def lsa_index_topk_workspace_bytes(B, Lq, S_max, topk, init_tokens, local_tokens) -> int:
+    return int(lib().lsa_index_topk_workspace_bytes(B, Lq, S_max, topk, init_tokens, local_tokens))
+
+
+def lsa_index_topk(q_idx, w, k_idx, seqlens, topk, init_tokens, local_tokens, indices=None,
+                   n_sel=None, workspace=None):
+    """Indexer + top-k in one pass (no score array): the inputs of lsa_index_scores ->
+    (indices i32 [B,Lq,topk] ascending, -1 padded; n_sel i32 [B,Lq])."""
+    _want(q_idx, "q_idx", torch.bfloat16, 4)
+    _want(w, "w", torch.float32, 3)
+    _want(k_idx, "k_idx", torch.bfloat16, 3)
+    _want(seqlens, "seqlens", torch.int32, 1)
+    B, Lq, Hi, Di = q_idx.shape
+    S_max = k_idx.shape[1]
+    dev = q_idx.device
+    if indices is None:
+        indices = torch.empty(B, Lq, topk, dtype=torch.int32, device=dev)
+    if n_sel is None:
+        n_sel = torch.empty(B, Lq, dtype=torch.int32, device=dev)
+    need = lsa_index_topk_workspace_bytes(B, Lq, S_max, topk, init_tokens, local_tokens)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().lsa_index_topk(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(seqlens), B, Lq, Hi, Di,
+                                S_max, topk, init_tokens, local_tokens, _ptr(indices), _ptr(n_sel),
+                                _ptr(workspace), wbytes, _stream(q_idx)))
     return indices, n_sel
 
 

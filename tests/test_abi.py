@@ -75,6 +75,23 @@ def test_topk_argument_errors_and_workspace():
     assert L.lsa_topk_workspace_bytes(1, 1, (1 << 20) + 1, 2048, 16, 1024) == 0
 
 
+def test_index_topk_argument_errors_and_workspace():
+    L = lsa.lib()
+    p = ctypes.c_void_p(16)
+    f = L.lsa_index_topk
+    assert f(p, p, p, p, 1, 1, 33, 128, 4096, 256, 4, 64, p, p, p, 1 << 30, None) == 3  # Hi > 32
+    assert f(p, p, p, p, 1, 1, 32, 96, 4096, 256, 4, 64, p, p, p, 1 << 30, None) == 3  # Di
+    assert f(p, p, p, p, 1, 1, 32, 128, 4096, 8, 5, 4, p, p, p, 1 << 30, None) == 2  # init+local
+    assert f(p, p, p, p, 1, 1, 32, 128, (1 << 20) + 1, 2048, 16, 1024, p, p, p, 1 << 30, None) == 3
+    assert f(p, None, p, p, 1, 1, 32, 128, 4096, 256, 4, 64, p, p, p, 1 << 30, None) == 1
+    need = L.lsa_index_topk_workspace_bytes(32, 1, 131072, 2048, 16, 1024)
+    assert need > 0
+    assert f(p, p, p, p, 32, 1, 32, 128, 131072, 2048, 16, 1024, p, p, p, need - 1, None) == 4
+    assert "need" in _err()
+    assert f(None, None, None, None, 0, 1, 32, 128, 4096, 256, 4, 64, None, None, None, 0, None) == 0
+    assert L.lsa_index_topk_workspace_bytes(1, 1, 4096, 8, 5, 4) == 0  # invalid -> 0
+
+
 def test_mla_argument_errors_and_workspace():
     L = lsa.lib()
     p = ctypes.c_void_p(16)
@@ -102,8 +119,9 @@ def test_workspace_sizes_are_modest(name):
 
     wl = WORKLOADS[name]
     t = lsa.lsa_topk_workspace_bytes(wl.B, wl.Lq, wl.S_max, wl.topk, wl.init, wl.local)
+    f = lsa.lsa_index_topk_workspace_bytes(wl.B, wl.Lq, wl.S_max, wl.topk, wl.init, wl.local)
     m = lsa.lsa_mla_workspace_bytes(wl.B, wl.Lq, wl.H, wl.Dv, wl.S_max, wl.topk, False)
-    assert 0 <= t <= 512 << 20 and 0 <= m <= 256 << 20
+    assert 0 <= t <= 512 << 20 and 0 < f <= 512 << 20 and 0 <= m <= 256 << 20
 
 
 def test_binding_rejects_host_tensors():
