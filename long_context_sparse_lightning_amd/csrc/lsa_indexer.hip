@@ -53,6 +53,7 @@ struct IndexParams {
   // fused variant: rows [row0, row0 + gridDim.x / chunks_per_row), candidate lists per chunk
   int row0, topk, init, local, R;
   uint32_t* count;  // [group rows][chunks]
+  uint32_t* range;  // [group rows][chunks][2]
   uint2* cand;      // [group rows][chunks][keys_per_wg]
 };
 
@@ -161,7 +162,8 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
     __syncthreads();  // the stage is reused as the histogram
     sel::chunk_candidates<kThreads, kStageItems>(
         key, valid, z - a + 1, P.R, start, reinterpret_cast<uint32_t*>(stage), sh,
-        P.cand + static_cast<size_t>(blockIdx.x) * keys_per_wg, P.count + blockIdx.x);
+        P.cand + static_cast<size_t>(blockIdx.x) * keys_per_wg, P.count + blockIdx.x,
+        P.range + 2 * blockIdx.x);
   }
 }
 
@@ -200,7 +202,7 @@ hipError_t launch_any(const IndexParams& P, int Di, long grid, hipStream_t strea
 struct FusedPlan {
   int keys_per_wg = kWgStride, chunks = 1;
   long rows = 0, group = 1;
-  size_t count_bytes = 0, cand_bytes = 0;
+  size_t count_bytes = 0, range_bytes = 0, cand_bytes = 0;
 };
 
 FusedPlan fused_plan(int B, int Lq, int S_max) {
@@ -211,6 +213,7 @@ FusedPlan fused_plan(int B, int Lq, int S_max) {
   const size_t per_row = static_cast<size_t>(pl.chunks) * pl.keys_per_wg * sizeof(uint2);
   pl.group = std::max<long>(1, std::min<long>(pl.rows, static_cast<long>(kFusedBudget / per_row)));
   pl.count_bytes = (static_cast<size_t>(pl.group) * pl.chunks * 4 + 255) & ~static_cast<size_t>(255);
+  pl.range_bytes = (static_cast<size_t>(pl.group) * pl.chunks * 8 + 255) & ~static_cast<size_t>(255);
   pl.cand_bytes = static_cast<size_t>(pl.group) * per_row;
   return pl;
 }
@@ -240,7 +243,7 @@ size_t index_topk_workspace_bytes(int B, int Lq, int S_max, int topk, int init_t
   (void)init_tokens;
   (void)local_tokens;
   const FusedPlan pl = fused_plan(B, Lq, S_max);
-  return pl.count_bytes + pl.cand_bytes;
+  return pl.count_bytes + pl.range_bytes + pl.cand_bytes;
 }
 
 hipError_t launch_index_topk(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
@@ -265,15 +268,16 @@ hipError_t launch_index_topk(const uint16_t* q_idx, const float* w, const uint16
   P.R = topk - init_tokens - local_tokens;
   char* ws = static_cast<char*>(workspace);
   P.count = reinterpret_cast<uint32_t*>(ws);
-  P.cand = reinterpret_cast<uint2*>(ws + pl.count_bytes);
+  P.range = reinterpret_cast<uint32_t*>(ws + pl.count_bytes);
+  P.cand = reinterpret_cast<uint2*>(ws + pl.count_bytes + pl.range_bytes);
   for (long r0 = 0; r0 < pl.rows; r0 += pl.group) {
     const long g = std::min(pl.group, pl.rows - r0);
     P.row0 = static_cast<int>(r0);
     hipError_t err = launch_any<true>(P, Di, g * pl.chunks, stream);
     if (err != hipSuccess) return err;
     err = launch_topk_merge(seqlens, Lq, S_max, topk, init_tokens, local_tokens, static_cast<int>(r0),
-                            static_cast<int>(g), pl.chunks, pl.keys_per_wg, P.count, P.cand, indices,
-                            n_sel, stream);
+                            static_cast<int>(g), pl.chunks, pl.keys_per_wg, P.count, P.range, P.cand,
+                            indices, n_sel, stream);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;

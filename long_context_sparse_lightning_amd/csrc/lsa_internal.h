@@ -73,12 +73,13 @@ hipError_t launch_topk(const float* scores, const int32_t* seqlens, int B, int L
 // Exact merge of per-chunk candidate lists into the selection of rows [row0, row0 + rows):
 // count[r][c] pairs (key, position) at cand[r][c][0 .. count), r relative to row0, each list the
 // candidates of positions [c * chunk_keys, (c + 1) * chunk_keys) (a superset of that chunk's
-// contribution to the row's top R, or all of its middle positions).
+// contribution to the row's top R, or all of its middle positions), with range[r][c][0..1]
+// bounding its keys.
 int topk_merge_max_chunks();
 hipError_t launch_topk_merge(const int32_t* seqlens, int Lq, int S_max, int topk, int init_tokens,
                              int local_tokens, int row0, int rows, int chunks, int chunk_keys,
-                             uint32_t* count, uint2* cand, int32_t* indices, int32_t* n_sel,
-                             hipStream_t stream);
+                             uint32_t* count, uint32_t* range, uint2* cand, int32_t* indices,
+                             int32_t* n_sel, hipStream_t stream);
 
 // Indexer and top-k in one pass: the scores never leave the chip.
 size_t index_topk_workspace_bytes(int B, int Lq, int S_max, int topk, int init_tokens, int local_tokens);

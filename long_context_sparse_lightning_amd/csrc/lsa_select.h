@@ -131,29 +131,32 @@ constexpr int chunk_scratch_words() { return 3 * (THREADS / kWave) + 4; }
 // base + j*THREADS + threadIdx.x; m = number of valid items in the workgroup.  Writes to `out`
 // every valid key when m <= R, else those whose digit is at least that of the chunk's R-th
 // largest (always a superset of the chunk's contribution to the row's top R), as (key,
-// position) pairs, and their number to *count.  hist: 2*kBins words of LDS, zeroed here;
-// sh: chunk_scratch_words<THREADS>() words.  Call from every thread, with m >= 1.
+// position) pairs, their number to *count, and bounds lo <= every written key <= hi to
+// range[0], range[1].  hist: 2*kBins words of LDS, zeroed here; sh:
+// chunk_scratch_words<THREADS>() words.  Call from every thread, with m >= 1.
 template <int THREADS, int ITEMS>
 __device__ void chunk_candidates(const uint32_t (&key)[ITEMS], uint32_t valid, int m, int R,
                                  int base, uint32_t* hist, uint32_t* sh, uint2* out,
-                                 uint32_t* count) {
+                                 uint32_t* count, uint32_t* range) {
   constexpr int WAVES = THREADS / kWave;
   uint32_t* sh_scan = sh;
   uint32_t* sh_mm = sh + WAVES;
   uint32_t* sh_out = sh + 3 * WAVES;
   const int tid = threadIdx.x, wave = tid >> 6;
   uint32_t keep = valid;
-  if (m > R) {
+  if (m > R)
     for (int i = tid; i < 2 * kBins; i += THREADS) hist[i] = 0u;
-    uint32_t mn = 0xffffffffu, mx = 0u;
+  uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
-      if (valid & (1u << j)) {
-        mn = min(mn, key[j]);
-        mx = max(mx, key[j]);
-      }
+  for (int j = 0; j < ITEMS; ++j) {
+    if (valid & (1u << j)) {
+      mn = min(mn, key[j]);
+      mx = max(mx, key[j]);
     }
-    block_minmax<WAVES>(mn, mx, sh_mm);  // its barrier also orders the zeroing
+  }
+  block_minmax<WAVES>(mn, mx, sh_mm);  // its barrier also orders the zeroing
+  uint32_t lo = mn;
+  if (m > R) {
     const int sh_bits = digit_shift(mn, mx);
     const uint32_t dbase = mn >> sh_bits;
     uint32_t* hw = hist + (wave & 1) * kBins;  // one copy per half of the waves
@@ -167,6 +170,7 @@ __device__ void chunk_candidates(const uint32_t (&key)[ITEMS], uint32_t valid, i
     for (int i = 0; i < kPer; ++i) c[i] = hist[kPer * tid + i] + hist[kBins + kPer * tid + i];
     select_bin<kPer, WAVES>(c, static_cast<uint32_t>(R), sh_scan, sh_out);
     const uint32_t dmin = sh_out[0];
+    lo = (dbase + dmin) << sh_bits;  // no kept key is below the first kept digit
     keep = 0;
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j)
@@ -181,7 +185,11 @@ __device__ void chunk_candidates(const uint32_t (&key)[ITEMS], uint32_t valid, i
       ++at;
     }
   }
-  if (tid == 0) *count = total;
+  if (tid == 0) {
+    *count = total;
+    range[0] = lo;
+    range[1] = mx;
+  }
 }
 
 }  // namespace sel

@@ -59,6 +59,7 @@ struct TopkParams {
   int chunks;        // chunk lists per row
   int chunk_keys;    // positions per chunk (= capacity of its list)
   uint32_t* count;   // [group rows][chunks]
+  uint32_t* range;   // [group rows][chunks][2] bounds of each list's keys
   uint2* cand;       // [group rows][chunks][chunk_keys] (key, position)
   int32_t* indices;  // [rows][topk]
   int32_t* n_sel;    // [rows]
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(TopkParams P)
   }
   sel::chunk_candidates<kChunkThreads, kChunkItems>(key, valid, m, P.R, base, hist, sh,
                                                     P.cand + static_cast<size_t>(blockIdx.x) * kChunk,
-                                                    P.count + blockIdx.x);
+                                                    P.count + blockIdx.x, P.range + 2 * blockIdx.x);
 }
 
 // ------------------------------------------------------------------ 2. merge per row
@@ -151,22 +152,34 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
   for (int i = tid; i < mid_words; i += kMergeThreads) sh_bits[i] = 0u;
   for (int i = tid; i < kBins; i += kMergeThreads) sh_h[i] = 0u;
   if (tid == 0) sh_res[8] = 0u;  // rank-list length
-  // candidate offsets of the row's chunk lists (thread c: list c), and the longest list
-  if (tid == 0) sh_res[9] = 0u;
+  // list lengths and key bounds (thread c: list c), requested first: loads complete in order
+  const size_t lc = static_cast<size_t>(grow) * P.chunks + tid;
+  const uint32_t c_len = tid < P.chunks ? P.count[lc] : 0u;
+  const uint32_t c_lo = tid < P.chunks ? P.range[2 * lc] : 0xffffffffu;
+  const uint32_t c_hi = tid < P.chunks ? P.range[2 * lc + 1] : 0u;
+  const size_t ck = static_cast<size_t>(P.chunk_keys);
+  const uint2* crow = P.cand + static_cast<size_t>(grow) * P.chunks * ck;
+  // candidate offsets of the row's lists (thread c: list c), the longest list, the key bounds
+  if (tid == 0) {
+    sh_res[9] = 0u;
+    sh_res[10] = 0xffffffffu;
+    sh_res[11] = 0u;
+  }
   {
-    const uint32_t c = tid < P.chunks ? P.count[static_cast<size_t>(grow) * P.chunks + tid] : 0u;
     uint32_t total;
-    const uint32_t at = block_prefix<kMergeWaves>(c, sh_scan, &total);
+    const uint32_t at = block_prefix<kMergeWaves>(c_len, sh_scan, &total);
     if (tid < P.chunks) {
       sh_off[tid] = at;
-      atomicMax(&sh_res[9], c);
+      atomicMax(&sh_res[9], c_len);
+      if (c_len > 0) {
+        atomicMin(&sh_res[10], c_lo);
+        atomicMax(&sh_res[11], c_hi);
+      }
     }
     if (tid == 0) sh_off[kMaxChunks] = total;
   }
   __syncthreads();
   const uint32_t nc = sh_off[kMaxChunks];
-  const size_t ck = static_cast<size_t>(P.chunk_keys);
-  const uint2* crow = P.cand + static_cast<size_t>(grow) * P.chunks * ck;
   // candidate q of the concatenated lists -> its pair
   auto locate = [&](uint32_t q) -> const uint2* {
     int lo = 0, hi = P.chunks - 1;  // last chunk c with sh_off[c] <= q
@@ -212,13 +225,9 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
   };
   // radix rounds over adaptive digits.  Keys still in play are those with (k >> s_in) == pref
   // (all of them while s_in == 32); a round histograms the digit (k >> s) - dbase of those keys,
-  // finds the digit of the need-th largest and narrows to it.
-  uint32_t mn = 0xffffffffu, mx = 0u;
-  each([&](uint32_t k, int32_t) {
-    mn = min(mn, k);
-    mx = max(mx, k);
-  });
-  block_minmax<kMergeWaves>(mn, mx, sh_cnt);
+  // finds the digit of the need-th largest and narrows to it.  The first window comes from the
+  // key bounds the chunk lists carry.
+  const uint32_t mn = sh_res[10], mx = sh_res[11];
   int s_in = 32, s = digit_shift(mn, mx);
   uint32_t pref = 0, dbase = mn >> s;
   uint32_t need = static_cast<uint32_t>(R), pop;
@@ -308,8 +317,8 @@ struct Plan {
   long rows = 0;
   int R = 0, chunks = 1;
   long group = 1;  // rows per launch pair
-  size_t count_bytes = 0, cand_bytes = 0;
-  size_t total() const { return count_bytes + cand_bytes; }
+  size_t count_bytes = 0, range_bytes = 0, cand_bytes = 0;
+  size_t total() const { return count_bytes + range_bytes + cand_bytes; }
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -322,6 +331,7 @@ Plan make_plan(int B, int Lq, int S_max, int topk, int init_tokens, int local_to
   const size_t per_row = static_cast<size_t>(pl.chunks) * kChunk * sizeof(uint2);
   pl.group = std::max<long>(1, std::min<long>(pl.rows, static_cast<long>(kWorkspaceBudget / per_row)));
   pl.count_bytes = align256(static_cast<size_t>(pl.group) * pl.chunks * 4);
+  pl.range_bytes = align256(static_cast<size_t>(pl.group) * pl.chunks * 8);
   pl.cand_bytes = static_cast<size_t>(pl.group) * per_row;
   return pl;
 }
@@ -364,7 +374,8 @@ hipError_t launch_topk(const float* scores, const int32_t* seqlens, int B, int L
   P.chunk_keys = kChunk;
   char* ws = static_cast<char*>(workspace);
   P.count = reinterpret_cast<uint32_t*>(ws);
-  P.cand = reinterpret_cast<uint2*>(ws + pl.count_bytes);
+  P.range = reinterpret_cast<uint32_t*>(ws + pl.count_bytes);
+  P.cand = reinterpret_cast<uint2*>(ws + pl.count_bytes + pl.range_bytes);
   P.indices = indices;
   P.n_sel = n_sel;
   for (long r0 = 0; r0 < pl.rows; r0 += pl.group) {
@@ -383,8 +394,8 @@ int topk_merge_max_chunks() { return kMaxChunks; }
 
 hipError_t launch_topk_merge(const int32_t* seqlens, int Lq, int S_max, int topk, int init_tokens,
                              int local_tokens, int row0, int rows, int chunks, int chunk_keys,
-                             uint32_t* count, uint2* cand, int32_t* indices, int32_t* n_sel,
-                             hipStream_t stream) {
+                             uint32_t* count, uint32_t* range, uint2* cand, int32_t* indices,
+                             int32_t* n_sel, hipStream_t stream) {
   if (chunks > kMaxChunks || rows <= 0) return hipErrorInvalidConfiguration;
   const size_t lds = merge_lds_bytes(S_max);
   hipError_t err = set_merge_lds(lds);
@@ -401,6 +412,7 @@ hipError_t launch_topk_merge(const int32_t* seqlens, int Lq, int S_max, int topk
   P.chunks = chunks;
   P.chunk_keys = chunk_keys;
   P.count = count;
+  P.range = range;
   P.cand = cand;
   P.indices = indices;
   P.n_sel = n_sel;
