@@ -9,9 +9,10 @@ batch; inputs are generated in HBM before timing.  Prints ONE JSON line.
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--path fused|split]
                   [--no-cpu-baseline]
 
---path fused (default) runs the indexer and the top-k in one call (lsa_index_topk: the scores
-never leave the chip); --path split runs lsa_index_scores then lsa_topk_select.  Both give the
-same indices bit for bit.
+--path fused (the default for decode workloads) runs the indexer and the top-k in one call
+(lsa_index_topk: the scores never leave the chip); --path split (the default for prefill
+workloads, where the query-blocked scan is the faster indexer) runs lsa_index_scores then
+lsa_topk_select.  Both give the same indices bit for bit.
 """
 from __future__ import annotations
 
@@ -32,7 +33,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_128k")
-    ap.add_argument("--path", choices=("fused", "split"), default="fused")
+    ap.add_argument("--path", choices=("fused", "split"), default=None,
+                    help="default: fused for decode workloads, split for prefill ones (the "
+                         "query-blocked prefill scan writes the scores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="query rows the oracle times (0: auto)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -137,6 +140,8 @@ def main():
     from long_context_sparse_lightning_amd.workloads import WORKLOADS, device_inputs
 
     wl = WORKLOADS[args.workload]
+    if args.path is None:
+        args.path = "fused" if wl.decode else "split"
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     X = device_inputs(wl, device=dev)

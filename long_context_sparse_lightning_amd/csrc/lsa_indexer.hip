@@ -24,6 +24,16 @@
 // the loop would make the next overwrite of its data register wait for the store -- and, since
 // loads and stores share one counter, for every prefetch issued before it.
 //
+// Query-blocked variant (prefill, many query rows per sequence): the per-row scan above reads a
+// sequence's keys once per query row, which makes prefill bound by cache bandwidth.  Here a
+// workgroup of 8 wavefronts owns 16 consecutive query rows (2 per wavefront, their query
+// fragments and weights in registers) and a chunk of keys; each 32-key tile is loaded once per
+// workgroup into a double-buffered, XOR-swizzled LDS tile (one 16-byte piece per thread, three
+// tiles of register prefetch ahead) and every wavefront reuses each key fragment for both of
+// its rows.  Key chunk c goes to workgroups c, c + nchunks, ..., which the dispatcher places on
+// one XCD when nchunks is a multiple of 8, so each XCD's L2 holds one slice of the keys for
+// every query block.  The work is then bound by the matrix cores.
+//
 // Fused variant (indexer + top-k, the scores never leave the chip): instead of writing its
 // staged scores, a workgroup turns them into its chunk's top-k candidate list (a superset of
 // the chunk's contribution to the row's top R, see lsa_select.h), and the top-k merge kernel
@@ -167,6 +177,133 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
   }
 }
 
+constexpr int kQbRows = 16;        // query rows per workgroup (2 per wavefront)
+constexpr int kQbThreads = 512;    // 8 wavefronts
+constexpr int kQbMinRows = 16;     // row count from which the query-blocked scan is used
+constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3 for gfx9-family raw buffers
+constexpr int kDropOffset = 1 << 30;      // beyond any row: such stores are dropped
+
+struct QbParams {
+  const uint16_t* q_idx;
+  const float* w;
+  const uint16_t* k_idx;
+  const int32_t* seqlens;
+  int Lq, Hi, S_max;
+  int nqb;        // query blocks per sequence
+  int nkc;        // key chunks per sequence
+  int kc_keys;    // keys per chunk (multiple of 32)
+  float* scores;
+};
+
+// 16 query rows x one key chunk; Di = 128 (16 units of 16 bytes per key).
+__global__ __launch_bounds__(kQbThreads, 1) void index_scores_qb_kernel(QbParams P) {
+  constexpr int DI = 128, NC = DI / 16, UK = DI / 8;
+  static_assert(kQbThreads * 16 == kTileKeys * DI * 2, "one 16-byte piece per thread per tile");
+  __shared__ __attribute__((aligned(16))) u32x4 kt[2][kTileKeys * UK];  // two 8 KB tiles
+  const int kc = blockIdx.x % P.nkc;
+  const int rest = blockIdx.x / P.nkc;
+  const int qb = rest % P.nqb;
+  const int b = rest / P.nqb;
+  const int Lq = P.Lq, Hi = P.Hi, S_max = P.S_max;
+  const int sl = P.seqlens[b];
+  const int i_last = min(qb * kQbRows + kQbRows - 1, Lq - 1);
+  const int pmax = min(sl - Lq + i_last, S_max - 1);  // position of the block's last row
+  const int start = kc * P.kc_keys;
+  if (start > pmax) return;
+  const int end = min(start + P.kc_keys, pmax + 1);  // keys [start, end)
+  const int ntiles = (end - start + kTileKeys - 1) / kTileKeys;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, g = lane >> 5;
+
+  // this wavefront's two query rows: fragments, weights, positions
+  // Scores go out through buffer stores whose range is the row's keys [0, p]: lanes past p (and
+  // every lane of a step past the end) store out of range, which the hardware drops.  The store
+  // is therefore unconditional, so the compiler's wait counts stay exact (a store behind a branch
+  // makes it wait for the prefetch issued after it).
+  bf16x8 qa[2][NC];
+  float wr[2][16];
+  __amdgpu_buffer_rsrc_t rs[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = qb * kQbRows + 2 * wave + q;
+    const bool ok = i < Lq;
+    const size_t row = static_cast<size_t>(b) * Lq + min(i, Lq - 1);
+    const int pq = ok ? min(sl - Lq + i, S_max - 1) : -1;  // keys s <= pq are scored
+    rs[q] = __builtin_amdgcn_make_buffer_rsrc(P.scores + row * S_max, 0, 4 * (pq + 1), kBufferFlags);
+    const uint16_t* qp = P.q_idx + (row * Hi + min(col, Hi - 1)) * DI + g * (DI / 2);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const bf16x8 v = load_bf16x8(qp + 8 * c);
+      qa[q][c] = col < Hi ? v : zero_bf16x8();
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int h = acc_row(r, g);
+      const float v = P.w[row * Hi + min(h, Hi - 1)];
+      wr[q][r] = h < Hi ? v : 0.0f;
+    }
+  }
+
+  // cooperative tile loads: thread t moves unit t % 16 of key t / 16; in LDS, unit u of key k
+  // sits at slot u ^ (k % 16), so the fragment reads below hit 16 different bank groups
+  const int lkey = tid >> 4, lunit = tid & 15;
+  const uint16_t* kbase = P.k_idx + static_cast<size_t>(b) * S_max * DI + 8 * lunit;
+  auto gload = [&](int t0) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(min(t0 + lkey, S_max - 1)) * DI);
+  };
+  auto lstore = [&](int slot, u32x4 v) { kt[slot][lkey * UK + (lunit ^ (lkey & (UK - 1)))] = v; };
+  auto barrier = [] {  // LDS only: the register prefetch stays in flight
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // one tile: fragments from LDS, 8 matrix-core steps per row, fused epilogue, masked stores
+  auto step = [&](int t) {
+    const int slot = t & 1;
+    const int t0 = start + t * kTileKeys;
+    bf16x8 kb[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      kb[c] = __builtin_bit_cast(bf16x8, kt[slot][col * UK + ((g * NC + c) ^ (col & (UK - 1)))]);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc = mfma32(qa[q][c], kb[c], acc);
+      float part = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part += wr[q][r] * fmaxf(acc[r], 0.0f);
+      part += xor32(part);
+      const int key = t0 + col;  // < end within the last tile or the row's range check drops it
+      const int off = (g == 0 && t < ntiles) ? 4 * key : kDropOffset;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), rs[q], off, 0, 0);
+    }
+  };
+
+  u32x4 r0 = gload(start), r1 = gload(start + kTileKeys), r2 = gload(start + 2 * kTileKeys);
+  lstore(0, r0);
+  barrier();
+  // three tiles per iteration so the prefetch registers keep fixed roles; tiles past the end
+  // compute on clamped keys and store nothing
+  for (int t = 0; t < ntiles; t += 3) {
+    r0 = gload(start + (t + 3) * kTileKeys);
+    step(t);
+    lstore((t + 1) & 1, r1);
+    barrier();
+    r1 = gload(start + (t + 4) * kTileKeys);
+    step(t + 1);
+    lstore((t + 2) & 1, r2);
+    barrier();
+    r2 = gload(start + (t + 5) * kTileKeys);
+    step(t + 2);
+    lstore((t + 3) & 1, r0);
+    barrier();
+  }
+}
+
 // Keys per workgroup: about 512 workgroups (two per CU, all resident at once) with whole
 // workgroup steps per chunk; long chunks amortise the query/weight loads and the ramp of each
 // workgroup.  The fused variant also keeps at most 128 chunks per row (the merge's limit).
@@ -224,6 +361,26 @@ hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint
                                const int32_t* seqlens, int B, int Lq, int Hi, int Di, int S_max,
                                float* scores, hipStream_t stream) {
   const long rows = static_cast<long>(B) * Lq;
+  if (Di == 128 && Lq >= kQbMinRows) {  // prefill: query-blocked scan
+    QbParams Q{};
+    Q.q_idx = q_idx;
+    Q.w = w;
+    Q.k_idx = k_idx;
+    Q.seqlens = seqlens;
+    Q.Lq = Lq;
+    Q.Hi = Hi;
+    Q.S_max = S_max;
+    Q.nqb = (Lq + kQbRows - 1) / kQbRows;
+    Q.nkc = 8;  // one key chunk per XCD
+    Q.kc_keys = ((S_max + Q.nkc - 1) / Q.nkc + kTileKeys - 1) / kTileKeys * kTileKeys;
+    Q.nkc = (S_max + Q.kc_keys - 1) / Q.kc_keys;
+    Q.scores = scores;
+    const long grid = static_cast<long>(B) * Q.nqb * Q.nkc;
+    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(index_scores_qb_kernel, dim3(static_cast<unsigned>(grid)), dim3(kQbThreads), 0,
+                       stream, Q);
+    return hipGetLastError();
+  }
   IndexParams P{};
   P.q_idx = q_idx;
   P.w = w;

@@ -50,6 +50,12 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 
 __device__ __forceinline__ uint64_t wave_ballot(bool pred) { return __ballot(pred); }
 
+// Value of lane ^ 32 via the gfx950 permlane swap (VALU, no LDS round trip).
+__device__ __forceinline__ float xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(((threadIdx.x >> 5) & 1) ? r[0] : r[1]);
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).  The compiler
 // folds it into its own wait tracking, so later waits count from here.
 template <int N>

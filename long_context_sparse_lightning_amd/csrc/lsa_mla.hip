@@ -122,12 +122,6 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Value of lane ^ 32 via the gfx950 permlane swap (VALU, no LDS round trip).
-__device__ __forceinline__ float xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(((threadIdx.x >> 5) & 1) ? r[0] : r[1]);
-}
-
 // D = A * B + C on the 16x16x32 bf16 matrix core.  Per lane l (c = l % 16, q = l / 16):
 //   A: row c, k = 8q .. 8q+7;  B: column c, k = 8q .. 8q+7;  C/D register r: row 4q + r, column c.
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {

@@ -31,6 +31,10 @@ SMALL = [
     # topk == init + local: no free slot
     Workload("no_free_slot", B=2, S_max=2000, Lq=1, seqlens=(2000, 1500), Hi=8, Di=32, topk=96,
              init=32, local=64, H=4, Dqk=80, Dv=64, seed=80),
+    # query-blocked prefill scan (Di = 128, Lq >= 16): ragged sequences, a partial query block,
+    # a sequence as short as its chunk, odd index-head count
+    Workload("prefill_qblock", B=3, S_max=5000, Lq=21, seqlens=(5000, 2100, 21), Hi=17, Di=128,
+             topk=256, init=4, local=32, H=4, Dqk=80, Dv=64, scale=0.125, seed=83),
     # several top-k chunks (S_max > 16384) with a single merge level
     Workload("multi_chunk", B=2, S_max=40000, Lq=1, seqlens=(40000, 20000), Hi=8, Di=32, topk=256,
              init=4, local=16, H=32, seed=81),
