@@ -28,9 +28,9 @@
 // sequence's keys once per query row, which makes prefill bound by cache bandwidth.  Here a
 // workgroup of 8 wavefronts owns 16 consecutive query rows (2 per wavefront, their query
 // fragments and weights in registers) and a chunk of keys; each 32-key tile is loaded once per
-// workgroup into a double-buffered, XOR-swizzled LDS tile (one 16-byte piece per thread, three
+// workgroup into a double-buffered, XOR-swizzled LDS tile (one 16-byte piece per thread, two
 // tiles of register prefetch ahead) and every wavefront reuses each key fragment for both of
-// its rows.  Key chunk c goes to workgroups c, c + nchunks, ..., which the dispatcher places on
+// its rows; the epilogue of one tile runs next to the matrix-core work of the next.  Key chunk c goes to workgroups c, c + nchunks, ..., which the dispatcher places on
 // one XCD when nchunks is a multiple of 8, so each XCD's L2 holds one slice of the keys for
 // every query block.  The work is then bound by the matrix cores.
 //
@@ -260,46 +260,56 @@ __global__ __launch_bounds__(kQbThreads, 1) void index_scores_qb_kernel(QbParams
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  // one tile: fragments from LDS, 8 matrix-core steps per row, fused epilogue, masked stores
-  auto step = [&](int t) {
+  // one tile: fragments from LDS and 8 matrix-core steps per row into acc
+  auto mfma_tile = [&](int t, f32x16 (&acc)[2]) {
     const int slot = t & 1;
-    const int t0 = start + t * kTileKeys;
     bf16x8 kb[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c)
       kb[c] = __builtin_bit_cast(bf16x8, kt[slot][col * UK + ((g * NC + c) ^ (col & (UK - 1)))]);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      f32x16 acc = {};
+      acc[q] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) acc = mfma32(qa[q][c], kb[c], acc);
+      for (int c = 0; c < NC; ++c) acc[q] = mfma32(qa[q][c], kb[c], acc[q]);
+    }
+  };
+  // fused epilogue of tile t and the range-checked stores (tiles past the end store nothing)
+  auto epilogue = [&](int t, const f32x16 (&acc)[2]) {
+    const int key = start + t * kTileKeys + col;  // < end within the last tile or dropped
+    const int off = (g == 0 && t < ntiles) ? 4 * key : kDropOffset;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
       float part = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) part += wr[q][r] * fmaxf(acc[r], 0.0f);
+      for (int r = 0; r < 16; ++r) part += wr[q][r] * fmaxf(acc[q][r], 0.0f);
       part += xor32(part);
-      const int key = t0 + col;  // < end within the last tile or the row's range check drops it
-      const int off = (g == 0 && t < ntiles) ? 4 * key : kDropOffset;
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), rs[q], off, 0, 0);
     }
   };
 
-  u32x4 r0 = gload(start), r1 = gload(start + kTileKeys), r2 = gload(start + 2 * kTileKeys);
+  // Software pipeline over tiles: step t loads tile t+2 into registers, runs the matrix-core
+  // work of tile t (LDS slot t & 1) next to the epilogue of tile t-1, and writes tile t+1 into
+  // the other slot.  Two steps per iteration give the registers and accumulators fixed roles;
+  // steps past the end compute on clamped keys and store nothing.
+  f32x16 acc0[2], acc1[2];
+  u32x4 r0 = gload(start), r1 = gload(start + kTileKeys);
   lstore(0, r0);
   barrier();
-  // three tiles per iteration so the prefetch registers keep fixed roles; tiles past the end
-  // compute on clamped keys and store nothing
-  for (int t = 0; t < ntiles; t += 3) {
+  r0 = gload(start + 2 * kTileKeys);
+  mfma_tile(0, acc0);
+  lstore(1, r1);
+  barrier();
+  for (int t = 1; t <= ntiles; t += 2) {
+    r1 = gload(start + (t + 2) * kTileKeys);
+    mfma_tile(t, acc1);
+    epilogue(t - 1, acc0);
+    lstore(0, r0);  // tile t + 1
+    barrier();
     r0 = gload(start + (t + 3) * kTileKeys);
-    step(t);
-    lstore((t + 1) & 1, r1);
-    barrier();
-    r1 = gload(start + (t + 4) * kTileKeys);
-    step(t + 1);
-    lstore((t + 2) & 1, r2);
-    barrier();
-    r2 = gload(start + (t + 5) * kTileKeys);
-    step(t + 2);
-    lstore((t + 3) & 1, r0);
+    mfma_tile(t + 1, acc0);
+    epilogue(t, acc1);
+    lstore(1, r1);  // tile t + 2
     barrier();
   }
 }
