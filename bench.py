@@ -71,6 +71,19 @@ def indexer_bytes(wl):
     return tot
 
 
+def indexer_flops(wl):
+    """Algorithmic matrix-core flops of one indexer launch: the q.k products of every index head
+    over every visible (query, key) pair, 2*Hi*Di each (the ReLU-weighted head sum is not counted)."""
+    pairs = sum(wl.seqlens[b] - wl.Lq + i + 1 for b in range(wl.B) for i in range(wl.Lq))
+    return 2 * wl.Hi * wl.Di * pairs
+
+
+def query_blocked(wl):
+    """True when lsa_index_scores runs the query-blocked scan for this shape (16 query rows per
+    workgroup share each key tile; a dense contraction, bound by the matrix cores)."""
+    return wl.Di == 128 and wl.Lq >= 16
+
+
 def fused_call_bytes(wl):
     """Algorithmic bytes of one lsa_index_topk call: keys of the visible positions, the index
     query and weights, and the indices and n_sel written."""
@@ -215,6 +228,25 @@ def main():
     k1_bytes = fused_call_bytes(wl) if fused else indexer_bytes(wl)
     k1_gbs = k1_bytes / (k1_ms / 1e3) / 1e9
     step_gbs = alg / (ms_per_step / 1e3) / 1e9
+    if fused:
+        roofline = {"kernel": "lsa_index_topk (index_scores_kernel<128,true> + topk_merge_kernel)",
+                    "bound": "hbm", "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
+                    "traffic": load_traffic(wl.name, args.path), "avg_launch_ms": round(k1_ms, 5),
+                    "alg_bytes_per_launch": k1_bytes}
+    elif query_blocked(wl):
+        flops = indexer_flops(wl)
+        tfs = flops / (k1_ms / 1e3) / 1e12
+        roofline = {"kernel": "lsa_index_scores (index_scores_qb_kernel)", "bound": "mfma",
+                    "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "avg_launch_ms": round(k1_ms, 5), "alg_flops_per_launch": flops}
+    else:
+        roofline = {"kernel": "lsa_index_scores (index_scores_kernel<128,false>)", "bound": "hbm",
+                    "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
+                    "traffic": load_traffic(wl.name, args.path), "avg_launch_ms": round(k1_ms, 5),
+                    "alg_bytes_per_launch": k1_bytes}
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -242,16 +274,14 @@ def main():
                    "index_heads": wl.Hi, "index_dim": wl.Di, "topk": wl.topk,
                    "init_tokens": wl.init, "local_tokens": wl.local, "mla_heads": wl.H,
                    "qk_dim": wl.Dqk, "v_dim": wl.Dv, "mla_calls_per_step": wl.mla_calls},
-        "hbm_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
-        "step_alg_bytes": alg,
-        "step_score_roundtrip_bytes": score_rt,
-        "roofline": {"kernel": ("lsa_index_topk (index_scores_kernel<128,true> + topk_merge_kernel)"
-                                if fused else "lsa_index_scores (index_scores_kernel<128,false>)"),
-                     "bound": "hbm", "achieved": round(k1_gbs, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic(wl.name, args.path), "avg_launch_ms": round(k1_ms, 5),
-                     "alg_bytes_per_launch": k1_bytes},
+        "roofline": roofline,
     }
+    if wl.decode:
+        # per-row byte accounting; in prefill the rows of one sequence share their keys, so a
+        # per-row sum would count every key Lq times and is not reported
+        line["hbm_frac_step"] = round(step_gbs / HBM_PEAK_GBS, 4)
+        line["step_alg_bytes"] = alg
+        line["step_score_roundtrip_bytes"] = score_rt
     if not args.no_cpu_baseline:
         # about 10 s of oracle work: three passes over the 32 decode rows of the 128K step
         sample = args.cpu_sample or (3 * B * Lq if wl.decode and B * Lq <= 64 else 64)

@@ -177,8 +177,7 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
   }
 }
 
-constexpr int kQbRows = 16;        // query rows per workgroup (2 per wavefront)
-constexpr int kQbThreads = 512;    // 8 wavefronts
+constexpr int kQbWaves = 8;        // wavefronts per workgroup, two query rows each
 constexpr int kQbMinRows = 16;     // row count from which the query-blocked scan is used
 constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3 for gfx9-family raw buffers
 constexpr int kDropOffset = 1 << 30;      // beyond any row: such stores are dropped
@@ -195,18 +194,23 @@ struct QbParams {
   float* scores;
 };
 
-// 16 query rows x one key chunk; Di = 128 (16 units of 16 bytes per key).
-__global__ __launch_bounds__(kQbThreads, 1) void index_scores_qb_kernel(QbParams P) {
+// 2 * WAVES query rows x one key chunk; Di = 128 (16 units of 16 bytes per key).  Workgroups of
+// four wavefronts run two to a CU, so while one waits at its per-tile barrier the other keeps
+// the matrix cores busy.
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void index_scores_qb_kernel(QbParams P) {
   constexpr int DI = 128, NC = DI / 16, UK = DI / 8;
-  static_assert(kQbThreads * 16 == kTileKeys * DI * 2, "one 16-byte piece per thread per tile");
-  __shared__ __attribute__((aligned(16))) u32x4 kt[2][kTileKeys * UK];  // two 8 KB tiles
+  constexpr int THREADS = 64 * WAVES, ROWS = 2 * WAVES;
+  constexpr int LOADS = kTileKeys * UK / THREADS;  // 16-byte pieces per thread per tile
+  static_assert(LOADS * THREADS == kTileKeys * UK, "whole tiles per load round");
+  __shared__ __attribute__((aligned(16))) u32x4 kt[4][kTileKeys * UK];  // ring of four 8 KB tiles
   const int kc = blockIdx.x % P.nkc;
   const int rest = blockIdx.x / P.nkc;
   const int qb = rest % P.nqb;
   const int b = rest / P.nqb;
   const int Lq = P.Lq, Hi = P.Hi, S_max = P.S_max;
   const int sl = P.seqlens[b];
-  const int i_last = min(qb * kQbRows + kQbRows - 1, Lq - 1);
+  const int i_last = min(qb * ROWS + ROWS - 1, Lq - 1);
   const int pmax = min(sl - Lq + i_last, S_max - 1);  // position of the block's last row
   const int start = kc * P.kc_keys;
   if (start > pmax) return;
@@ -227,7 +231,7 @@ __global__ __launch_bounds__(kQbThreads, 1) void index_scores_qb_kernel(QbParams
   __amdgpu_buffer_rsrc_t rs[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const int i = qb * kQbRows + 2 * wave + q;
+    const int i = qb * ROWS + 2 * wave + q;
     const bool ok = i < Lq;
     const size_t row = static_cast<size_t>(b) * Lq + min(i, Lq - 1);
     const int pq = ok ? min(sl - Lq + i, S_max - 1) : -1;  // keys s <= pq are scored
@@ -246,72 +250,133 @@ __global__ __launch_bounds__(kQbThreads, 1) void index_scores_qb_kernel(QbParams
     }
   }
 
-  // cooperative tile loads: thread t moves unit t % 16 of key t / 16; in LDS, unit u of key k
-  // sits at slot u ^ (k % 16), so the fragment reads below hit 16 different bank groups
+  // cooperative tile loads: piece j of thread t is unit t % 16 of key t / 16 + j * THREADS / 16;
+  // in LDS, unit u of key k sits at slot u ^ (k % 16), so the fragment reads below hit 16
+  // different bank groups
   const int lkey = tid >> 4, lunit = tid & 15;
   const uint16_t* kbase = P.k_idx + static_cast<size_t>(b) * S_max * DI + 8 * lunit;
-  auto gload = [&](int t0) -> u32x4 {
-    return *reinterpret_cast<const u32x4*>(kbase + static_cast<size_t>(min(t0 + lkey, S_max - 1)) * DI);
+  struct Piece { u32x4 v[LOADS]; };
+  auto gload = [&](int t0) {
+    Piece x;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j)
+      x.v[j] = *reinterpret_cast<const u32x4*>(
+          kbase + static_cast<size_t>(min(t0 + lkey + j * (THREADS / 16), S_max - 1)) * DI);
+    return x;
   };
-  auto lstore = [&](int slot, u32x4 v) { kt[slot][lkey * UK + (lunit ^ (lkey & (UK - 1)))] = v; };
+  auto lstore = [&](int slot, const Piece& x) {
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int k = lkey + j * (THREADS / 16);
+      kt[slot][k * UK + (lunit ^ (k & (UK - 1)))] = x.v[j];
+    }
+  };
   auto barrier = [] {  // LDS only: the register prefetch stays in flight
     __builtin_amdgcn_s_waitcnt(0xC07F);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
   };
-  // one tile: fragments from LDS and 8 matrix-core steps per row into acc
-  auto mfma_tile = [&](int t, f32x16 (&acc)[2]) {
-    const int slot = t & 1;
-    bf16x8 kb[NC];
+  // key fragments of the tile in LDS slot `slot`
+  auto kread = [&](int slot, bf16x8 (&kb)[NC]) {
 #pragma unroll
     for (int c = 0; c < NC; ++c)
       kb[c] = __builtin_bit_cast(bf16x8, kt[slot][col * UK + ((g * NC + c) ^ (col & (UK - 1)))]);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      acc[q] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < NC; ++c) acc[q] = mfma32(qa[q][c], kb[c], acc[q]);
-    }
   };
-  // fused epilogue of tile t and the range-checked stores (tiles past the end store nothing)
-  auto epilogue = [&](int t, const f32x16 (&acc)[2]) {
+  // one epilogue element: weight x ReLU.  ReLU is a signed-integer max on the bit pattern:
+  // negative floats (and -0) have negative patterns, so it gives max(x, 0) for finite x in one
+  // instruction.
+  auto relu_w = [&](int q, int r, float x) {
+    return wr[q][r] * __int_as_float(max(__float_as_int(x), 0));
+  };
+  // head sum across the lane pair and the range-checked store of query row q on tile t (tiles
+  // outside [0, ntiles) store nothing)
+  auto store_row = [&](int q, int t, float part) {
+    part += xor32(part);
     const int key = start + t * kTileKeys + col;  // < end within the last tile or dropped
-    const int off = (g == 0 && t < ntiles) ? 4 * key : kDropOffset;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      float part = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) part += wr[q][r] * fmaxf(acc[q][r], 0.0f);
-      part += xor32(part);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), rs[q], off, 0, 0);
-    }
+    const int off = (g == 0 && static_cast<unsigned>(t) < static_cast<unsigned>(ntiles)) ? 4 * key
+                                                                                         : kDropOffset;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), rs[q], off, 0, 0);
   };
 
-  // Software pipeline over tiles: step t loads tile t+2 into registers, runs the matrix-core
-  // work of tile t (LDS slot t & 1) next to the epilogue of tile t-1, and writes tile t+1 into
-  // the other slot.  Two steps per iteration give the registers and accumulators fixed roles;
-  // steps past the end compute on clamped keys and store nothing.
-  f32x16 acc0[2], acc1[2];
-  u32x4 r0 = gload(start), r1 = gload(start + kTileKeys);
-  lstore(0, r0);
+  // Software pipeline.  Step t, with LDS slots rotating over 4:
+  //   - reads tile t+1's fragments from LDS into registers (written one step earlier),
+  //   - loads tile t+3 from memory into registers,
+  //   - runs row 0's 8 dependent matrix-core steps on tile t, each followed by two elements of
+  //     row 1's epilogue of tile t-1; then row 1's steps on tile t next to row 0's epilogue of
+  //     tile t (one step behind, so its accumulator is complete),
+  //   - writes tile t+2 (loaded two steps earlier) into its slot, then a barrier.
+  // After the barrier the matrix cores start at once on fragments already in registers.  The
+  // instruction order is fixed with scheduling barriers.  Four steps per iteration give every
+  // register and slot a fixed role; steps past the end compute on clamped keys and store nothing.
+  f32x16 acc0, acc1 = f32x16{};
+  bf16x8 kx[NC], ky[NC];
+  Piece rx = gload(start), ry = gload(start + kTileKeys);
+  lstore(0, rx);  // tile 0
+  rx = gload(start + 2 * kTileKeys);
+  lstore(1, ry);  // tile 1
   barrier();
-  r0 = gload(start + 2 * kTileKeys);
-  mfma_tile(0, acc0);
-  lstore(1, r1);
-  barrier();
-  for (int t = 1; t <= ntiles; t += 2) {
-    r1 = gload(start + (t + 2) * kTileKeys);
-    mfma_tile(t, acc1);
-    epilogue(t - 1, acc0);
-    lstore(0, r0);  // tile t + 1
+  kread(0, kx);
+  auto step = [&](int t, int slot, const bf16x8 (&kc)[NC], bf16x8 (&kn)[NC], Piece& rl, Piece& rn) {
+    kread(slot, kn);
+    rn = gload(start + (t + 3) * kTileKeys);
+    float p1 = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      acc0 = mfma32(qa[0][c], kc[c], c == 0 ? f32x16{} : acc0);
+      p1 += relu_w(1, 2 * c, acc1[2 * c]);
+      p1 += relu_w(1, 2 * c + 1, acc1[2 * c + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    store_row(1, t - 1, p1);
+    float p0 = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      acc1 = mfma32(qa[1][c], kc[c], c == 0 ? f32x16{} : acc1);
+      if (c > 0) {
+        p0 += relu_w(0, 2 * c - 2, acc0[2 * c - 2]);
+        p0 += relu_w(0, 2 * c - 1, acc0[2 * c - 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    p0 += relu_w(0, 14, acc0[14]);
+    p0 += relu_w(0, 15, acc0[15]);
+    store_row(0, t, p0);
+    lstore(slot == 3 ? 0 : slot + 1, rl);
     barrier();
-    r0 = gload(start + (t + 3) * kTileKeys);
-    mfma_tile(t + 1, acc0);
-    epilogue(t, acc1);
-    lstore(1, r1);  // tile t + 2
-    barrier();
+  };
+  for (int t = 0; t <= ntiles; t += 4) {
+    step(t, 1, kx, ky, rx, ry);
+    step(t + 1, 2, ky, kx, ry, rx);
+    step(t + 2, 3, kx, ky, rx, ry);
+    step(t + 3, 0, ky, kx, ry, rx);
   }
+}
+
+template <int WAVES>
+hipError_t launch_qb(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+                     const int32_t* seqlens, int B, int Lq, int Hi, int S_max, float* scores,
+                     hipStream_t stream) {
+  constexpr int ROWS = 2 * WAVES;
+  QbParams Q{};
+  Q.q_idx = q_idx;
+  Q.w = w;
+  Q.k_idx = k_idx;
+  Q.seqlens = seqlens;
+  Q.Lq = Lq;
+  Q.Hi = Hi;
+  Q.S_max = S_max;
+  Q.nqb = (Lq + ROWS - 1) / ROWS;
+  Q.nkc = 8;  // one key chunk per XCD
+  Q.kc_keys = ((S_max + Q.nkc - 1) / Q.nkc + kTileKeys - 1) / kTileKeys * kTileKeys;
+  Q.nkc = (S_max + Q.kc_keys - 1) / Q.kc_keys;
+  Q.scores = scores;
+  const long grid = static_cast<long>(B) * Q.nqb * Q.nkc;
+  if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(index_scores_qb_kernel<WAVES>, dim3(static_cast<unsigned>(grid)),
+                     dim3(64 * WAVES), 0, stream, Q);
+  return hipGetLastError();
 }
 
 // Keys per workgroup: about 512 workgroups (two per CU, all resident at once) with whole
@@ -371,26 +436,8 @@ hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint
                                const int32_t* seqlens, int B, int Lq, int Hi, int Di, int S_max,
                                float* scores, hipStream_t stream) {
   const long rows = static_cast<long>(B) * Lq;
-  if (Di == 128 && Lq >= kQbMinRows) {  // prefill: query-blocked scan
-    QbParams Q{};
-    Q.q_idx = q_idx;
-    Q.w = w;
-    Q.k_idx = k_idx;
-    Q.seqlens = seqlens;
-    Q.Lq = Lq;
-    Q.Hi = Hi;
-    Q.S_max = S_max;
-    Q.nqb = (Lq + kQbRows - 1) / kQbRows;
-    Q.nkc = 8;  // one key chunk per XCD
-    Q.kc_keys = ((S_max + Q.nkc - 1) / Q.nkc + kTileKeys - 1) / kTileKeys * kTileKeys;
-    Q.nkc = (S_max + Q.kc_keys - 1) / Q.kc_keys;
-    Q.scores = scores;
-    const long grid = static_cast<long>(B) * Q.nqb * Q.nkc;
-    if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(index_scores_qb_kernel, dim3(static_cast<unsigned>(grid)), dim3(kQbThreads), 0,
-                       stream, Q);
-    return hipGetLastError();
-  }
+  if (Di == 128 && Lq >= kQbMinRows)  // prefill: query-blocked scan
+    return launch_qb<kQbWaves>(q_idx, w, k_idx, seqlens, B, Lq, Hi, S_max, scores, stream);
   IndexParams P{};
   P.q_idx = q_idx;
   P.w = w;
