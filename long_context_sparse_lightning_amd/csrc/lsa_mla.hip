@@ -153,11 +153,28 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
   const int ntiles = j1 > j0 ? (j1 - j0 + kTile - 1) / kTile : 0;
   const uint16_t* kv_b = P.kv + static_cast<size_t>(b) * P.S_max * DQK;
 
+  // query fragments of this wavefront's Dqk steps (B operand: column = head, k = dims); they
+  // do not depend on the selection, so they are requested first
+  bf16x8 qf[2][C::KSW];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int head = hg * kHeadGroup + 16 * hb + c16;
+#pragma unroll
+    for (int i = 0; i < C::KSW; ++i) {
+      const int ks = wave + 4 * i;
+      const int dim0 = 32 * ks + 8 * q16;
+      qf[hb][i] = (head < P.H && ks < C::KS && dim0 < DQK)
+                      ? load_bf16x8(P.q + (static_cast<size_t>(row) * P.H + head) * DQK + dim0)
+                      : zero_bf16x8();
+    }
+  }
   // this split's row positions (clamped into the cache) staged in LDS
   if (sparse) {
     const int32_t* ilist = P.indices + static_cast<size_t>(row) * P.topk;
     for (int j = tid; j < j1 - j0; j += kThreads) slice[j] = min(max(ilist[j0 + j], 0), P.S_max - 1);
   }
+  // retire the query and index loads here: a wait left to the compiler would sit inside the
+  // loop and drain the ring on every step
   wait_vmcnt<0>();
   __syncthreads();
 
@@ -187,25 +204,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
                      (lds_void*)(stage + (4 * k + wave) * kWave * 8))));
     }
   };
-
   if (ntiles > 0) issue(0);
-  // query fragments of this wavefront's Dqk steps (A operand: row = head, k = dims)
-  bf16x8 qf[2][C::KSW];
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const int head = hg * kHeadGroup + 16 * hb + c16;
-#pragma unroll
-    for (int i = 0; i < C::KSW; ++i) {
-      const int ks = wave + 4 * i;
-      const int dim0 = 32 * ks + 8 * q16;
-      qf[hb][i] = (head < P.H && ks < C::KS && dim0 < DQK)
-                      ? load_bf16x8(P.q + (static_cast<size_t>(row) * P.H + head) * DQK + dim0)
-                      : zero_bf16x8();
-    }
-  }
-  // retire the query loads here (this also lands the first tile): a wait left to the compiler
-  // would sit inside the loop and drain the ring on every step
-  wait_vmcnt<0>();
   if (ntiles > 1) issue(1);
 
   float m_ref = -INFINITY, l_run = 0.0f;  // for head `col` (identical in every wavefront)
@@ -219,7 +218,9 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
     ring_barrier();  // every wavefront's pieces of tile t are in LDS
 
     const uint16_t* kvt = ring[t % kStages];
-    // ---- partial logits over this wavefront's Dqk steps; lane = (row c16, heads 4*q16 + r)
+    // ---- partial logits over this wavefront's Dqk steps, as S^T = KV_tile . Q^T so that a
+    // lane holds one head (c16) for four consecutive tile rows (4*q16 + r): one 16-byte LDS
+    // write per head block
     {
       f32x4 acc0 = {}, acc1 = {};
 #pragma unroll
@@ -231,16 +232,13 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
                                 ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
                                                                  &kvt[C::slot(c16, c) * 8]))
                                 : zero_bf16x8();
-          acc0 = mfma16(qf[0][i], kb, acc0);
-          acc1 = mfma16(qf[1][i], kb, acc1);
+          acc0 = mfma16(kb, qf[0][i], acc0);
+          acc1 = mfma16(kb, qf[1][i], acc1);
         }
       }
       float* sp = spart[wave];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sp[(4 * q16 + r) * kPartStride + c16] = acc0[r];
-        sp[(16 + 4 * q16 + r) * kPartStride + c16] = acc1[r];
-      }
+      *reinterpret_cast<f32x4*>(&sp[c16 * kPartStride + 4 * q16]) = acc0;
+      *reinterpret_cast<f32x4*>(&sp[(16 + c16) * kPartStride + 4 * q16]) = acc1;
     }
     ring_barrier();  // partial logits of all wavefronts published
     if (t + 2 < ntiles) issue(t + 2);  // into the stage freed at the end of the previous step
@@ -287,14 +285,17 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
         for (int i = 0; i < C::NBW; ++i) o[i][r] *= a;
       }
     }
+    // probabilities: the hardware exponential (results below 2^-126 of the reference flush to
+    // zero; every row's largest probability is at least 2^-8) and the paired round-to-nearest-
+    // even conversion to bf16
     uint32_t pw[4];
     float psum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = bf16_bits_rne(exp2f(sv[2 * i] - m_ref));
-      const uint32_t hi = bf16_bits_rne(exp2f(sv[2 * i + 1] - m_ref));
-      psum += bf16_bits_to_float(static_cast<uint16_t>(lo)) + bf16_bits_to_float(static_cast<uint16_t>(hi));
-      pw[i] = lo | (hi << 16);
+      const bf16x2 pr = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[2 * i] - m_ref)),
+                         static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[2 * i + 1] - m_ref))};
+      pw[i] = __builtin_bit_cast(uint32_t, pr);
+      psum += __uint_as_float(pw[i] << 16) + __uint_as_float(pw[i] & 0xffff0000u);
     }
     psum += xor32(psum);
     l_run += psum;
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
 #pragma unroll
       for (int i = 0; i < C::NBW; ++i) {
         const int nb = wave + 4 * i;
-        if (nb < C::NB) {
+        if (C::NB % 4 == 0 || nb < C::NB) {  // statically true when the blocks divide evenly
           const int dim0 = 32 * nb + 16 * (G & 1) + 4 * (jl & 3);
           const int unit = dim0 >> 3, eoff = dim0 & 7;
           u32x2 hv[2];
