@@ -49,7 +49,7 @@ constexpr int kRegItems = 20;        // candidates held in registers per merge t
 constexpr int kMaxPositions = 1 << 20;
 constexpr int kMaxChunks = 128;      // chunk lists per row the merge accepts
 constexpr int kTieList = kMergeThreads;             // ties ranked in LDS up to this many
-constexpr size_t kWorkspaceBudget = size_t(256) << 20;
+constexpr size_t kWorkspaceBudget = size_t(1024) << 20;
 
 struct TopkParams {
   const float* scores;
@@ -66,7 +66,8 @@ struct TopkParams {
 };
 
 // ------------------------------------------------------------------ 1. per-chunk candidates
-__global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(TopkParams P) {
+// at most 128 VGPRs, so two 512-thread workgroups share a CU and overlap their load waits
+__global__ __launch_bounds__(kChunkThreads, 4) void topk_chunk_kernel(TopkParams P) {
   __shared__ uint32_t hist[2 * kBins];
   __shared__ uint32_t sh[sel::chunk_scratch_words<kChunkThreads>()];
   const int tid = threadIdx.x;

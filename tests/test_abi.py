@@ -121,7 +121,9 @@ def test_workspace_sizes_are_modest(name):
     t = lsa.lsa_topk_workspace_bytes(wl.B, wl.Lq, wl.S_max, wl.topk, wl.init, wl.local)
     f = lsa.lsa_index_topk_workspace_bytes(wl.B, wl.Lq, wl.S_max, wl.topk, wl.init, wl.local)
     m = lsa.lsa_mla_workspace_bytes(wl.B, wl.Lq, wl.H, wl.Dv, wl.S_max, wl.topk, False)
-    assert 0 <= t <= 512 << 20 and 0 < f <= 512 << 20 and 0 <= m <= 256 << 20
+    # the standalone top-k groups rows under a 1 GiB candidate budget (plus list lengths and
+    # bounds); the fused call and the attention stay far smaller
+    assert 0 <= t <= (1 << 30) + (16 << 20) and 0 < f <= 512 << 20 and 0 <= m <= 256 << 20
 
 
 def test_binding_rejects_host_tensors():
