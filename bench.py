@@ -177,19 +177,23 @@ def main():
     lses = [torch.empty(B, Lq, wl.H, dtype=torch.float32, device=dev) for _ in range(wl.mla_calls)]
     stream = torch.cuda.current_stream(dev)
 
-    def step(k1_events=None):
-        if k1_events is not None:
-            k1_events[0].record(stream)
+    def step(ev=None):
+        # ev: events recorded on the launch stream at the stage boundaries of this step:
+        # [start, after the indexer call, after top-k, after each attention call]
+        if ev is not None:
+            ev[0].record(stream)
         if fused:
             lsa.lsa_index_topk(X["qidx"], X["w"], X["kidx"], X["seqlens"], wl.topk, wl.init,
                                wl.local, indices=idx, n_sel=nsel, workspace=tws)
         else:
             lsa.lsa_index_scores(X["qidx"], X["w"], X["kidx"], X["seqlens"], scores=scores)
-        if k1_events is not None:
-            k1_events[1].record(stream)
+        if ev is not None:
+            ev[1].record(stream)
         if not fused:
             lsa.lsa_topk_select(scores, X["seqlens"], wl.topk, wl.init, wl.local, indices=idx,
                                 n_sel=nsel, workspace=tws)
+        if ev is not None:
+            ev[2].record(stream)
         for c in range(wl.mla_calls):
             if wl.decode:
                 lsa.lsa_sparse_mla_decode(X[f"q{c}"][:, 0], X[f"kv{c}"], idx[:, 0], nsel[:, 0],
@@ -198,28 +202,43 @@ def main():
             else:
                 lsa.lsa_sparse_mla_prefill(X[f"q{c}"], X[f"kv{c}"], idx, nsel, X["seqlens"], wl.Dv,
                                            wl.scale, out=outs[c], lse=lses[c], workspace=mws)
+            if ev is not None:
+                ev[3 + c].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     print(f"[bench] {wl.name}: warmup done", file=sys.stderr, flush=True)
 
-    k1_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(args.steps)]
+    # Pass 1 (the headline): K steps between two events and nothing else on the stream.  A
+    # timing event between kernels costs a few microseconds of queue bubble on this stack, so
+    # the per-call boundaries are taken in pass 2.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for s in range(args.steps):
-        step(k1_ev[s])
+        step()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     elapsed_ms = t_start.elapsed_time(t_end)
-    k1_ms = sum(a.elapsed_time(b) for a, b in k1_ev) / args.steps
     print(f"[bench] timed {args.steps} steps: {elapsed_ms:.3f} ms (host wall {wall * 1e3:.3f} ms)",
           file=sys.stderr, flush=True)
+
+    # Pass 2: the same K steps with an event at every call boundary, for the per-call durations
+    # (roofline, stages) and the spread of step times.  The last stage of step s ends where step
+    # s+1's first event is recorded (the same stream position).
+    n_ev = 3 + wl.mla_calls
+    step_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        step(step_ev[s])
+    torch.cuda.synchronize()
+    stage_ms = [[ev[j].elapsed_time(ev[j + 1]) for j in range(n_ev - 1)] for ev in step_ev]
+    k1_ms = sum(st[0] for st in stage_ms) / args.steps
+    step_list = sorted(step_ev[s][0].elapsed_time(step_ev[s + 1][0]) for s in range(args.steps - 1))
 
     ms_per_step = elapsed_ms / args.steps
     queries = B * Lq
@@ -257,6 +276,36 @@ def main():
         torch.cuda.synchronize()
         del a, bcopy
 
+    def mean(j):
+        return sum(st[j] for st in stage_ms) / args.steps
+
+    def pct(q):
+        return round(step_list[min(len(step_list) - 1, int(q * len(step_list)))], 5) if step_list else None
+
+    # per-stage algorithmic bytes: the indexer call as in the roofline; top-k (split path) reads
+    # the visible scores and writes the indices; an attention call gathers the selected rows and
+    # moves q, out and the index list
+    mla_bytes = sum(min(wl.seqlens[b] - wl.Lq + i + 1, wl.topk) * wl.Dqk * 2 + wl.H * wl.Dqk * 2
+                    + wl.H * wl.Dv * 2 + wl.topk * 4 for b in range(wl.B) for i in range(wl.Lq))
+    topk_bytes = sum((wl.seqlens[b] - wl.Lq + i + 1) * 4 + wl.topk * 4 + 4
+                     for b in range(wl.B) for i in range(wl.Lq))
+    # (rates only for decode: prefill rows share keys and selected rows, so per-row byte counts
+    # do not measure HBM there)
+    stages = {"index_call_ms": round(mean(0), 5)}
+    if wl.decode:
+        stages["index_call_gbs"] = round(k1_bytes / (mean(0) / 1e3) / 1e9, 1)
+    if not fused:
+        stages["topk_call_ms"] = round(mean(1), 5)
+        stages["topk_call_gbs"] = round(topk_bytes / (mean(1) / 1e3) / 1e9, 1)
+    for c in range(wl.mla_calls):
+        stages[f"mla{c}_call_ms"] = round(mean(2 + c), 5)
+        if wl.decode:
+            stages[f"mla{c}_call_gbs"] = round(mla_bytes / (mean(2 + c) / 1e3) / 1e9, 1)
+    # the same step with one attention call (the shape of configurations with one sub-block)
+    stages["one_mla_step_ms"] = round(mean(0) + mean(1) + mean(2), 5)
+    # spread of step times in pass 2 (which carries the boundary events)
+    stages["instrumented_step_ms_p10_p50_p90"] = [pct(0.1), pct(0.5), pct(0.9)]
+
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -275,6 +324,7 @@ def main():
                    "init_tokens": wl.init, "local_tokens": wl.local, "mla_heads": wl.H,
                    "qk_dim": wl.Dqk, "v_dim": wl.Dv, "mla_calls_per_step": wl.mla_calls},
         "roofline": roofline,
+        "stages": stages,
     }
     if wl.decode:
         # per-row byte accounting; in prefill the rows of one sequence share their keys, so a
