@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
   wait_vmcnt<0>();  // the query and weights are in: only key tiles are in flight below
 
   const uint16_t* kb_base = k_idx + static_cast<size_t>(b) * S_max * DI + g * (DI / 2);
-  extern __shared__ float stage[];  // [keys_per_wg] scores of this workgroup's chunk
+  extern __shared__ __attribute__((aligned(16))) float stage[];  // [keys_per_wg] scores of this chunk
 
   auto load_tile = [&](bf16x8 (&dst)[NC], int t0) {
     const uint16_t* kp = kb_base + static_cast<size_t>(min(t0 + col, S_max - 1)) * DI;
@@ -164,9 +164,12 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
     uint32_t valid = 0;
 #pragma unroll
     for (int j = 0; j < kStageItems; ++j) {
+      // read unconditionally (the dynamic LDS holds at least kStageItems * kThreads words), so
+      // no read waits behind a branch
+      const float v = stage[j * kThreads + static_cast<int>(threadIdx.x)];
       const int s = start + j * kThreads + static_cast<int>(threadIdx.x);
       const bool ok = s >= a && s <= z;
-      key[j] = ok ? sel::order_key(stage[s - start]) : 0u;
+      key[j] = ok ? sel::order_key(v) : 0u;
       valid |= (ok ? 1u : 0u) << j;
     }
     __syncthreads();  // the stage is reused as the histogram

@@ -40,6 +40,16 @@ __device__ __forceinline__ RowGeom row_geom(const int32_t* seqlens, int row, int
   return g;
 }
 
+// LDS word of histogram bin d when each of THREADS threads owns PER = kBins / THREADS
+// consecutive bins: bin PER*t + i sits at word i*THREADS + t, so when every owner reads its
+// i-th bin the workgroup reads consecutive words (no bank conflicts).
+template <int THREADS>
+__device__ __forceinline__ uint32_t bin_slot(uint32_t d) {
+  constexpr uint32_t PER = kBins / THREADS;
+  static_assert(PER * THREADS == kBins && (PER & (PER - 1)) == 0, "power-of-two split");
+  return (d % PER) * THREADS + d / PER;
+}
+
 // Which bin holds the target-th largest item: thread t owns bins [PER*t, PER*t + PER) with
 // counts c; afterwards out[0] = that bin, out[1] = the number of items in higher bins and
 // out[2] = the items in that bin.  Requires 1 <= target <= the sum of all counts.  Two barriers.
@@ -144,8 +154,8 @@ __device__ void chunk_candidates(const uint32_t (&key)[ITEMS], uint32_t valid, i
   uint32_t* sh_out = sh + 3 * WAVES;
   const int tid = threadIdx.x, wave = tid >> 6;
   uint32_t keep = valid;
-  if (m > R)
-    for (int i = tid; i < 2 * kBins; i += THREADS) hist[i] = 0u;
+  if (m > R)  // hist is 16-byte aligned
+    for (int i = tid; i < 2 * kBins / 4; i += THREADS) reinterpret_cast<u32x4*>(hist)[i] = u32x4{0u, 0u, 0u, 0u};
   uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j) {
@@ -162,12 +172,12 @@ __device__ void chunk_candidates(const uint32_t (&key)[ITEMS], uint32_t valid, i
     uint32_t* hw = hist + (wave & 1) * kBins;  // one copy per half of the waves
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j)
-      if (valid & (1u << j)) atomicAdd(&hw[(key[j] >> sh_bits) - dbase], 1u);
+      if (valid & (1u << j)) atomicAdd(&hw[bin_slot<THREADS>((key[j] >> sh_bits) - dbase)], 1u);
     __syncthreads();
     constexpr int kPer = kBins / THREADS;
     uint32_t c[kPer];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) c[i] = hist[kPer * tid + i] + hist[kBins + kPer * tid + i];
+    for (int i = 0; i < kPer; ++i) c[i] = hist[i * THREADS + tid] + hist[kBins + i * THREADS + tid];
     select_bin<kPer, WAVES>(c, static_cast<uint32_t>(R), sh_scan, sh_out);
     const uint32_t dmin = sh_out[0];
     lo = (dbase + dmin) << sh_bits;  // no kept key is below the first kept digit
@@ -176,14 +186,25 @@ __device__ void chunk_candidates(const uint32_t (&key)[ITEMS], uint32_t valid, i
     for (int j = 0; j < ITEMS; ++j)
       keep |= ((valid & (1u << j)) && (key[j] >> sh_bits) - dbase >= dmin ? 1u : 0u) << j;
   }
-  uint32_t total;
-  uint32_t at = block_prefix<WAVES>(__popc(keep), sh_scan, &total);
+  // Stores: the kept items of one wavefront and one item index j go to one contiguous run
+  // (ordered by wavefront, then j, then lane; the list is a set).
+  uint32_t mine = 0;  // this wavefront's kept items
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) mine += static_cast<uint32_t>(__popcll(wave_ballot((keep >> j) & 1u)));
+  if ((tid & (kWave - 1)) == 0) sh_scan[wave] = mine;
+  __syncthreads();
+  uint32_t at = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) {
+    at += w < wave ? sh_scan[w] : 0u;
+    total += sh_scan[w];
+  }
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j) {
-    if (keep & (1u << j)) {
-      out[at] = make_uint2(key[j], static_cast<uint32_t>(base + j * THREADS + tid));
-      ++at;
-    }
+    const uint64_t bj = wave_ballot((keep >> j) & 1u);
+    if ((keep >> j) & 1u)
+      out[at + lanes_below(bj)] = make_uint2(key[j], static_cast<uint32_t>(base + j * THREADS + tid));
+    at += static_cast<uint32_t>(__popcll(bj));
   }
   if (tid == 0) {
     *count = total;

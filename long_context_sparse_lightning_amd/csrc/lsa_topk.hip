@@ -30,6 +30,7 @@
 namespace lsa {
 namespace {
 
+using sel::bin_slot;
 using sel::block_minmax;
 using sel::block_prefix;
 using sel::digit_shift;
@@ -68,7 +69,7 @@ struct TopkParams {
 // ------------------------------------------------------------------ 1. per-chunk candidates
 // at most 128 VGPRs, so two 512-thread workgroups share a CU and overlap their load waits
 __global__ __launch_bounds__(kChunkThreads, 4) void topk_chunk_kernel(TopkParams P) {
-  __shared__ uint32_t hist[2 * kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[2 * kBins];
   __shared__ uint32_t sh[sel::chunk_scratch_words<kChunkThreads>()];
   const int tid = threadIdx.x;
   const int grow = blockIdx.x / P.chunks;  // row within the group
@@ -235,13 +236,13 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
   auto in_play = [&](uint32_t k) { return s_in >= 32 || (k >> s_in) == pref; };
   for (;;) {
     each([&](uint32_t k, int32_t) {
-      if (in_play(k)) atomicAdd(&sh_h[(k >> s) - dbase], 1u);
+      if (in_play(k)) atomicAdd(&sh_h[bin_slot<kMergeThreads>((k >> s) - dbase)], 1u);
     });
     __syncthreads();
     constexpr int kPer = kBins / kMergeThreads;
     uint32_t c[kPer];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) c[i] = sh_h[kPer * tid + i];
+    for (int i = 0; i < kPer; ++i) c[i] = sh_h[i * kMergeThreads + tid];
     select_bin<kPer, kMergeWaves>(c, need, sh_scan, sh_res);
     need -= sh_res[1];
     pop = sh_res[2];
