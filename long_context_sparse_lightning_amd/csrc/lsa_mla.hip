@@ -326,40 +326,43 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
   }
   wait_vmcnt<0>();
 
-  // ---- epilogue
-  if (P.splits == 1) {
+  // ---- epilogue: normalise, round to bf16 and stage this workgroup's [32 heads x DV] block in
+  // LDS (the ring is free now), then write it out with 16-byte stores: rows of the output for
+  // one split, or this head group's rows of `out` when there is a single split
+  {
+    const float inv_c = l_run > 0.0f ? 1.0f / l_run : 0.0f;  // head `col`
+    uint16_t* tb = &ring[0][0];
+    static_assert(kStages * C::STAGE_UNITS * 8 >= kHeadGroup * DV, "the ring holds the block");
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float lr = __shfl(l_run, acc_row(r, g));
-      const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
-      const int hh = hg * kHeadGroup + acc_row(r, g);
-      if (hh < P.H) {
-#pragma unroll
-        for (int i = 0; i < C::NBW; ++i) {
-          const int nb = wave + 4 * i;
-          if (nb < C::NB)
-            P.out[(static_cast<size_t>(row) * P.H + hh) * DV + 32 * nb + col] = bf16_bits_rne(o[i][r] * inv);
-        }
-      }
-    }
-    const int head = hg * kHeadGroup + col;
-    if (wave == 0 && g == 0 && head < P.H && P.lse)
-      P.lse[static_cast<size_t>(row) * P.H + head] =
-          l_run > 0.0f ? (m_ref + __log2f(l_run)) * kLn2 : -INFINITY;
-  } else {
-    const size_t slot = (static_cast<size_t>(row) * P.hgroups + hg) * P.splits + split;
-    uint16_t* wo = P.ws_o + slot * kHeadGroup * DV;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float lr = __shfl(l_run, acc_row(r, g));
-      const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+      const int hr = acc_row(r, g);
+      const float inv = __shfl(inv_c, hr);
 #pragma unroll
       for (int i = 0; i < C::NBW; ++i) {
         const int nb = wave + 4 * i;
-        if (nb < C::NB) wo[acc_row(r, g) * DV + 32 * nb + col] = bf16_bits_rne(o[i][r] * inv);
+        if (C::NB % 4 == 0 || nb < C::NB)
+          tb[hr * DV + 32 * nb + col] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(o[i][r] * inv));
       }
     }
-    if (wave == 0 && g == 0) {
+    __syncthreads();
+    const bool direct = P.splits == 1;
+    const size_t slot = (static_cast<size_t>(row) * P.hgroups + hg) * P.splits + split;
+    uint16_t* dst = direct ? P.out + (static_cast<size_t>(row) * P.H + hg * kHeadGroup) * DV
+                           : P.ws_o + slot * kHeadGroup * DV;
+    const int rows_out = direct ? min(kHeadGroup, P.H - hg * kHeadGroup) : kHeadGroup;
+    const int n_out = rows_out * DV;  // elements of the block that exist in the destination
+    if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0u) {
+      for (int e = 8 * tid; e < n_out; e += 8 * kThreads)
+        *reinterpret_cast<u32x4*>(dst + e) = *reinterpret_cast<const u32x4*>(tb + e);
+    } else {  // a caller buffer without 16-byte alignment
+      for (int e = tid; e < n_out; e += kThreads) dst[e] = tb[e];
+    }
+    if (direct) {
+      const int head = hg * kHeadGroup + col;
+      if (wave == 0 && g == 0 && head < P.H && P.lse)
+        P.lse[static_cast<size_t>(row) * P.H + head] =
+            l_run > 0.0f ? (m_ref + __log2f(l_run)) * kLn2 : -INFINITY;
+    } else if (wave == 0 && g == 0) {
       P.ws_ml[(slot * kHeadGroup + col) * 2] = m_ref;
       P.ws_ml[(slot * kHeadGroup + col) * 2 + 1] = l_run;
     }
