@@ -194,3 +194,37 @@ def test_workspace_too_small_is_rejected_before_launch():
     with pytest.raises(lsa.LsaError) as e:
         lsa.lsa_topk_select(sc, X["seqlens"], wl.topk, wl.init, wl.local, workspace=small)
     assert e.value.status == 4
+
+
+def test_attention_buffers_without_16_byte_alignment():
+    """The attention epilogue writes 16-byte pieces when the destination allows it and falls back
+    to 2-byte stores otherwise: a workspace offset by 8 bytes (split partials, decode) and an
+    `out` offset by one element (direct rows, prefill) give bit-identical results."""
+    wl = Workload("align", B=2, S_max=3000, Lq=1, seqlens=(3000, 2500), Hi=8, Di=128, topk=512,
+                  init=4, local=64, H=32, Dqk=576, Dv=512, seed=91)
+    X = device_inputs(wl)
+    _, idx, nsel, _, _ = run_path(wl, X)
+    need = lsa.lsa_mla_workspace_bytes(wl.B, 1, wl.H, wl.Dv, wl.S_max, wl.topk, False)
+    assert need > 0  # split partials go through the workspace
+    ws = torch.empty(need + 64, dtype=torch.uint8, device="cuda")
+    args = (X["q0"][:, 0], X["kv0"], idx[:, 0], nsel[:, 0], X["seqlens"], wl.Dv, wl.scale)
+    ref = lsa.lsa_sparse_mla_decode(*args, workspace=ws[:need])
+    odd = lsa.lsa_sparse_mla_decode(*args, workspace=ws[8:8 + need])
+    torch.cuda.synchronize()
+    assert torch.equal(ref, odd)
+
+    # 512 query rows: one workgroup per row, so the rows go straight to `out`
+    wp = Workload("align_p", B=1, S_max=700, Lq=512, seqlens=(700,), Hi=4, Di=32, topk=128, init=2,
+                  local=8, H=32, Dqk=576, Dv=512, seed=92)
+    Xp = device_inputs(wp)
+    _, idxp, nselp, _, _ = run_path(wp, Xp)
+    assert lsa.lsa_mla_workspace_bytes(wp.B, wp.Lq, wp.H, wp.Dv, wp.S_max, wp.topk, False) == 0
+    refp = lsa.lsa_sparse_mla_prefill(Xp["q0"], Xp["kv0"], idxp, nselp, Xp["seqlens"], wp.Dv, wp.scale)
+    n = refp.numel()
+    buf = torch.zeros(n + 1, dtype=torch.bfloat16, device="cuda")
+    outp = buf[1:].view(refp.shape)
+    assert outp.data_ptr() % 16 != 0
+    lsa.lsa_sparse_mla_prefill(Xp["q0"], Xp["kv0"], idxp, nselp, Xp["seqlens"], wp.Dv, wp.scale,
+                               out=outp)
+    torch.cuda.synchronize()
+    assert torch.equal(refp, outp)
