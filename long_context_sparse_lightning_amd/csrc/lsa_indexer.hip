@@ -83,11 +83,16 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
   // keys visible to this query (clamped so a bad seqlens value cannot write past the row)
   const int n = min(seqlens[b] - Lq + (row - b * Lq) + 1, S_max);
   const int start = chunk * keys_per_wg;
+  // fused variant: the competing positions [comp_a, comp_z] of this chunk, found before the scan
+  // so the selection after it starts without a memory access (since rg.hi <= n - 1, clipping to
+  // the chunk equals clipping to [start, end))
+  int comp_a = 0, comp_z = -1;
   if constexpr (FUSED) {
     // chunks holding no competing position produce an empty list (and skip the scan)
     const sel::RowGeom rg = sel::row_geom(seqlens, row, Lq, S_max, P.topk, P.init, P.local);
-    const int a = max(rg.lo, start), z = min(rg.hi, start + keys_per_wg - 1);
-    if (rg.dense || P.R == 0 || z < a) {
+    comp_a = max(rg.lo, start);
+    comp_z = min(rg.hi, start + keys_per_wg - 1);
+    if (rg.dense || P.R == 0 || comp_z < comp_a) {
       if (threadIdx.x == 0) P.count[blockIdx.x] = 0u;
       return;
     }
@@ -119,8 +124,10 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
   const uint16_t* kb_base = k_idx + static_cast<size_t>(b) * S_max * DI + g * (DI / 2);
   extern __shared__ __attribute__((aligned(16))) float stage[];  // [keys_per_wg] scores of this chunk
 
+  // rows past the end re-read the chunk's last key (a cache hit), so the prefetch issued in the
+  // last iteration costs the selection after the scan almost no wait
   auto load_tile = [&](bf16x8 (&dst)[NC], int t0) {
-    const uint16_t* kp = kb_base + static_cast<size_t>(min(t0 + col, S_max - 1)) * DI;
+    const uint16_t* kp = kb_base + static_cast<size_t>(min(t0 + col, end - 1)) * DI;
 #pragma unroll
     for (int c = 0; c < NC; ++c) dst[c] = load_bf16x8(kp + 8 * c);
   };
@@ -131,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
     float part = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) part += wr[r] * fmaxf(acc[r], 0.0f);
-    const float other = __shfl_xor(part, 32);
+    const float other = xor32(part);
     if (g == 0) stage[t0 - start + col] = part + other;  // t0 - start + col < keys_per_wg
   };
 
@@ -158,8 +165,7 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
     for (int i = threadIdx.x; i < end - start; i += kThreads) srow[i] = stage[i];
   } else {
     __shared__ uint32_t sh[sel::chunk_scratch_words<kThreads>()];
-    const sel::RowGeom rg = sel::row_geom(seqlens, row, Lq, S_max, P.topk, P.init, P.local);
-    const int a = max(rg.lo, start), z = min(rg.hi, end - 1);  // competing positions here
+    const int a = comp_a, z = comp_z;  // competing positions here
     uint32_t key[kStageItems];
     uint32_t valid = 0;
 #pragma unroll

@@ -57,6 +57,40 @@ __device__ __forceinline__ float xor32(float x) {
   return __uint_as_float(((threadIdx.x >> 5) & 1) ? r[0] : r[1]);
 }
 
+// Inclusive scan of op over the 64 lanes of a wavefront on the vector ALU (gfx9 DPP): shifts by
+// 1, 2, 4 and 8 lanes within each row of 16, then the last lane of row 0 / row 2 into rows 1 / 3
+// (row_bcast:15) and lane 31 into rows 2 and 3 (row_bcast:31).  Lanes with no source take
+// `identity`.  No LDS round trip, unlike the __shfl family.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x, uint32_t identity, Op op) {
+  const int id = static_cast<int>(identity);
+  x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(id, static_cast<int>(x), 0x111, 0xf, 0xf, false)));
+  x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(id, static_cast<int>(x), 0x112, 0xf, 0xf, false)));
+  x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(id, static_cast<int>(x), 0x114, 0xf, 0xf, false)));
+  x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(id, static_cast<int>(x), 0x118, 0xf, 0xf, false)));
+  x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(id, static_cast<int>(x), 0x142, 0xa, 0xf, false)));
+  x = op(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(id, static_cast<int>(x), 0x143, 0xc, 0xf, false)));
+  return x;
+}
+
+// Inclusive prefix sum over the lanes of a wavefront.
+__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t x) {
+  return wave_scan_incl(x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
+// Value of lane 63 (the wavefront total of an inclusive scan), wave-uniform.
+__device__ __forceinline__ uint32_t wave_last(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+  return wave_last(wave_scan_incl(x, 0xffffffffu, [](uint32_t a, uint32_t b) { return a < b ? a : b; }));
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  return wave_last(wave_scan_incl(x, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; }));
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).  The compiler
 // folds it into its own wait tracking, so later waits count from here.
 template <int N>

@@ -60,12 +60,9 @@ __device__ void select_bin(const uint32_t (&c)[PER], uint32_t target, uint32_t* 
   uint32_t mine = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) mine += c[i];
-  uint32_t x = mine;  // inclusive suffix sum over the lanes of this wave
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_down(x, off);
-    if (lane + off < 64) x += y;
-  }
+  // inclusive suffix sum over the lanes of this wave: the wave total minus the exclusive prefix
+  const uint32_t pre = wave_prefix_sum(mine);
+  const uint32_t x = wave_last(pre) - pre + mine;
   if (lane == 0) sh_scan[wave] = x;
   __syncthreads();
   uint32_t acc = x - mine;
@@ -87,12 +84,7 @@ __device__ void select_bin(const uint32_t (&c)[PER], uint32_t target, uint32_t* 
 template <int WAVES>
 __device__ __forceinline__ uint32_t block_prefix(uint32_t mine, uint32_t* sh_scan, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = mine;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+  const uint32_t x = wave_prefix_sum(mine);
   if (lane == 63) sh_scan[wave] = x;
   __syncthreads();
   uint32_t at = x - mine, t = 0;
@@ -109,11 +101,8 @@ __device__ __forceinline__ uint32_t block_prefix(uint32_t mine, uint32_t* sh_sca
 template <int WAVES>
 __device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_t* sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    mn = min(mn, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mn), off)));
-    mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), off)));
-  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
   if (lane == 0) {
     sh[wave] = mn;
     sh[WAVES + wave] = mx;

@@ -112,8 +112,7 @@ static_assert(2 * kTieList <= kBins, "the rank list reuses the histogram");
 // Block-wide sum of a per-thread count (one barrier; alternating slots).
 __device__ __forceinline__ uint32_t block_count(uint32_t v, uint32_t* cnt, int& parity) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  v = wave_last(wave_prefix_sum(v));
   if (lane == 0) cnt[parity * kMergeWaves + wave] = v;
   __syncthreads();
   uint32_t t = 0;
