@@ -124,8 +124,7 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
   const uint16_t* kb_base = k_idx + static_cast<size_t>(b) * S_max * DI + g * (DI / 2);
   extern __shared__ __attribute__((aligned(16))) float stage[];  // [keys_per_wg] scores of this chunk
 
-  // rows past the end re-read the chunk's last key (a cache hit), so the prefetch issued in the
-  // last iteration costs the selection after the scan almost no wait
+  // rows past the end of a partial tile re-read the chunk's last key
   auto load_tile = [&](bf16x8 (&dst)[NC], int t0) {
     const uint16_t* kp = kb_base + static_cast<size_t>(min(t0 + col, end - 1)) * DI;
 #pragma unroll
@@ -149,16 +148,25 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
   bf16x8 ka[NC], kc[NC];
   load_tile(ka, t);
   int i = 0;
-  for (; i + 2 <= ntiles; i += 2) {
+  for (; i + 3 <= ntiles; i += 2) {  // both prefetches of an iteration are tiles of this wavefront
     load_tile(kc, t + kWgStride);
     __builtin_amdgcn_sched_barrier(0);  // keep the whole prefetch ahead of the matrix-core work
     score_tile(ka, t);
-    load_tile(ka, t + 2 * kWgStride);  // past the end this re-reads a clamped row
+    load_tile(ka, t + 2 * kWgStride);
     __builtin_amdgcn_sched_barrier(0);
     score_tile(kc, t + kWgStride);
     t += 2 * kWgStride;
   }
-  if (i < ntiles) score_tile(ka, t);
+  // the last one or two tiles, with no load past the end: nothing is left in flight for the
+  // selection that follows to wait for
+  if (i + 2 <= ntiles) {
+    load_tile(kc, t + kWgStride);
+    __builtin_amdgcn_sched_barrier(0);
+    score_tile(ka, t);
+    score_tile(kc, t + kWgStride);
+  } else if (i < ntiles) {
+    score_tile(ka, t);
+  }
   __syncthreads();
   if constexpr (!FUSED) {
     float* srow = P.scores + static_cast<size_t>(row) * S_max + start;
