@@ -18,8 +18,9 @@
 // the kernel as one fp32 per key and the [heads x keys] tile never touches memory.
 // Loads for the next tile are issued before the matrix-core work of the current one, into the
 // other of two register buffers (the loop is unrolled by two, so no register copy has to wait
-// for a load in flight), and without a condition (past the end they re-read a clamped in-range
-// row): a conditional prefetch makes the compiler wait for it together with the current tile.
+// for a load in flight), and without a condition: a conditional prefetch makes the compiler
+// wait for it together with the current tile.  The last one or two tiles are peeled off the
+// loop, so no load past the chunk is left in flight when the scan ends.
 // Scores are staged in LDS and written with coalesced stores after the scan: a global store in
 // the loop would make the next overwrite of its data register wait for the store -- and, since
 // loads and stores share one counter, for every prefetch issued before it.
@@ -27,17 +28,21 @@
 // Query-blocked variant (prefill, many query rows per sequence): the per-row scan above reads a
 // sequence's keys once per query row, which makes prefill bound by cache bandwidth.  Here a
 // workgroup of 8 wavefronts owns 16 consecutive query rows (2 per wavefront, their query
-// fragments and weights in registers) and a chunk of keys; each 32-key tile is loaded once per
-// workgroup into a double-buffered, XOR-swizzled LDS tile (one 16-byte piece per thread, two
-// tiles of register prefetch ahead) and every wavefront reuses each key fragment for both of
-// its rows; the epilogue of one tile runs next to the matrix-core work of the next.  Key chunk c goes to workgroups c, c + nchunks, ..., which the dispatcher places on
-// one XCD when nchunks is a multiple of 8, so each XCD's L2 holds one slice of the keys for
-// every query block.  The work is then bound by the matrix cores.
+// fragments and weights in registers) and a chunk of keys.  Each 32-key tile is loaded once per
+// workgroup into a 4-slot, XOR-swizzled LDS ring (one 16-byte piece per thread, register
+// prefetch ahead); every wavefront reads the next tile's key fragments a step ahead and reuses
+// each fragment for both of its rows, and each row's epilogue runs next to the other row's
+// matrix-core chain, in an instruction order fixed with scheduling barriers.  Key chunk c goes
+// to workgroups c, c + nchunks, ..., which the dispatcher places on one XCD when nchunks is a
+// multiple of 8, so each XCD's L2 holds one slice of the keys for every query block.  The work
+// is then bound by the matrix cores and their LDS operand traffic.
 //
 // Fused variant (indexer + top-k, the scores never leave the chip): instead of writing its
 // staged scores, a workgroup turns them into its chunk's top-k candidate list (a superset of
 // the chunk's contribution to the row's top R, see lsa_select.h), and the top-k merge kernel
-// finishes the selection from those lists.
+// finishes the selection from those lists.  Of the two workgroups on a CU one streams first and
+// its selection overlaps the other's scan; the last selection on each CU is exposed after the
+// key stream, so that code is kept short (no memory waits, no LDS permutes, no bank conflicts).
 #include <algorithm>
 
 #include "lsa_select.h"
