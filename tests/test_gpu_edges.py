@@ -228,3 +228,25 @@ def test_attention_buffers_without_16_byte_alignment():
                                out=outp)
     torch.cuda.synchronize()
     assert torch.equal(refp, outp)
+
+
+def test_prefill_rows_equal_decode_calls():
+    """Row i of a prefill chunk (query-blocked scan, Di = 128) selects exactly what a decode call
+    at seqlen p + 1 selects for the same query, and its attention agrees within tolerance (the
+    two calls split the work differently)."""
+    wl = Workload("pd", B=1, S_max=3000, Lq=20, seqlens=(3000,), Hi=8, Di=128, topk=256, init=4,
+                  local=32, H=4, Dqk=576, Dv=512, seed=95)
+    X = device_inputs(wl)
+    _, idx, nsel, outs, _ = run_path(wl, X)
+    torch.cuda.synchronize()
+    for i in range(wl.Lq):
+        p = wl.seqlens[0] - wl.Lq + i
+        sl = torch.tensor([p + 1], dtype=torch.int32, device="cuda")
+        di, dn = lsa.lsa_index_topk(X["qidx"][:, i:i + 1].contiguous(), X["w"][:, i:i + 1].contiguous(),
+                                    X["kidx"], sl, wl.topk, wl.init, wl.local)
+        out = lsa.lsa_sparse_mla_decode(X["q0"][:, i].contiguous(), X["kv0"], di[:, 0], dn[:, 0], sl,
+                                        wl.Dv, wl.scale)
+        torch.cuda.synchronize()
+        assert int(dn[0, 0]) == int(nsel[0, i])
+        assert torch.equal(di[0, 0], idx[0, i]), f"row {i}"
+        assert_attention_close(bf16_to_f64(out[0]), bf16_to_f64(outs[0][0, i]), f"row {i}")

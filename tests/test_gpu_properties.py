@@ -1,0 +1,97 @@
+"""Property tests of the GPU path over small random shapes (hypothesis, derandomised): scores,
+the standalone and fused top-k bit-exact against the oracle, attention within tolerance.  The
+shapes span the boundaries of the method: n = topk and topk + 1, n <= init + local, all-equal
+scores (zero index queries: ReLU gives 0 everywhere), negative head weights, prefill rows on
+the query-blocked scan (Di = 128, Lq >= 16) and on the per-row scan."""
+import numpy as np
+import pytest
+import torch
+from hypothesis import HealthCheck, example, given, settings
+from hypothesis import strategies as st
+
+import oracle
+from conftest import gpu_available
+from long_context_sparse_lightning_amd import inputs as gen
+from long_context_sparse_lightning_amd import lsa
+from lsa_check import assert_attention_close
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def _dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+@st.composite
+def cases(draw):
+    Di = draw(st.sampled_from([32, 64, 128]))
+    Hi = draw(st.integers(1, 8))
+    topk = draw(st.sampled_from([8, 32, 64]))
+    init = draw(st.integers(0, topk // 2))
+    local = draw(st.integers(0, topk - init))
+    Lq = draw(st.sampled_from([1, 2, 3, 17]))
+    S = draw(st.integers(Lq, 600))
+    B = draw(st.integers(1, 3))
+    seqlens = [draw(st.integers(Lq, S)) for _ in range(B)]
+    pattern = draw(st.sampled_from(["random", "zero_queries", "negative_weights"]))
+    H = draw(st.integers(1, 5))
+    seed = draw(st.integers(0, 2**20))
+    return dict(Di=Di, Hi=Hi, topk=topk, init=init, local=local, Lq=Lq, S=S, B=B,
+                seqlens=seqlens, pattern=pattern, H=H, seed=seed)
+
+
+def _boundary(n_minus_topk, Di=32, Lq=1, pattern="random"):
+    topk, init, local = 32, 4, 8
+    n = topk + n_minus_topk
+    return dict(Di=Di, Hi=4, topk=topk, init=init, local=local, Lq=Lq, S=n, B=1,
+                seqlens=[n], pattern=pattern, H=2, seed=5)
+
+
+@settings(max_examples=30, derandomize=True, deadline=None,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
+@given(cases())
+@example(_boundary(0))                       # n == topk: dense fallback
+@example(_boundary(1))                       # n == topk + 1: the smallest sparse row
+@example(_boundary(-20))                     # n <= init + local (< topk): dense
+@example(_boundary(40, pattern="zero_queries"))  # every score 0: ties everywhere
+@example(_boundary(300, Di=128, Lq=17))      # prefill rows on the query-blocked scan
+def test_path_matches_oracle(c):
+    B, Lq, S, Hi, Di, H = c["B"], c["Lq"], c["S"], c["Hi"], c["Di"], c["H"]
+    topk, init, local, seed = c["topk"], c["init"], c["local"], c["seed"]
+    Dqk, Dv, scale = 80, 64, 1.0 / np.sqrt(80.0)
+    qidx = gen.ref_tensor(seed, gen.TAGS["qidx"], (B, Lq, Hi, Di), gen.DYADIC)
+    if c["pattern"] == "zero_queries":
+        qidx = np.zeros_like(qidx)
+    w = gen.ref_tensor(seed, gen.TAGS["w"], (B, Lq, Hi), gen.WEIGHT).astype(np.float32)
+    if c["pattern"] == "negative_weights":
+        w = w * np.where(np.arange(Hi) % 2 == 0, -1.0, 1.0).astype(np.float32)
+    kidx = gen.ref_tensor(seed, gen.TAGS["kidx"], (B, S, Di), gen.DYADIC)
+    q = gen.ref_tensor(seed, gen.TAGS["q"], (B, Lq, H, Dqk), gen.NORMAL)
+    kv = gen.ref_tensor(seed, gen.TAGS["kv0"], (B, S, Dqk), gen.NORMAL)
+    sl = np.array(c["seqlens"], np.int32)
+
+    ref_sc = oracle.index_scores(qidx, w, kidx, sl, Lq)
+    ref_idx, ref_n = oracle.topk_select(np.nan_to_num(ref_sc, nan=0.0), sl, topk, init, local)
+    ref_out, ref_lse = oracle.sparse_mla(q, kv, ref_idx, ref_n, sl, Dv, scale)
+
+    d_q, d_k, d_w = _dev_bf16(qidx), _dev_bf16(kidx), torch.from_numpy(w).cuda()
+    d_sl = torch.from_numpy(sl).cuda()
+    sc = lsa.lsa_index_scores(d_q, d_w, d_k, d_sl)
+    idx, nsel = lsa.lsa_topk_select(sc, d_sl, topk, init, local)
+    fidx, fnsel = lsa.lsa_index_topk(d_q, d_w, d_k, d_sl, topk, init, local)
+    d_qm, d_kv = _dev_bf16(q), _dev_bf16(kv)
+    if Lq == 1:
+        out = lsa.lsa_sparse_mla_decode(d_qm[:, 0], d_kv, idx[:, 0], nsel[:, 0], d_sl, Dv, scale)[:, None]
+    else:
+        out = lsa.lsa_sparse_mla_prefill(d_qm, d_kv, idx, nsel, d_sl, Dv, scale)
+    torch.cuda.synchronize()
+
+    got_sc = sc.cpu().numpy()
+    for b in range(B):
+        for i in range(Lq):
+            n = sl[b] - Lq + i + 1
+            assert np.array_equal(got_sc[b, i, :n].view(np.uint32), ref_sc[b, i, :n].view(np.uint32)), \
+                f"scores (b={b}, i={i})"
+    assert np.array_equal(idx.cpu().numpy(), ref_idx) and np.array_equal(nsel.cpu().numpy(), ref_n)
+    assert np.array_equal(fidx.cpu().numpy(), ref_idx) and np.array_equal(fnsel.cpu().numpy(), ref_n)
+    assert_attention_close(out.float().cpu().numpy().astype(np.float64), ref_out, "attention")
