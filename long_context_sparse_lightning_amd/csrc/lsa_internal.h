@@ -91,6 +91,22 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
   return wave_last(wave_scan_incl(x, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; }));
 }
 
+// Float reductions over the wavefront (the scan on the bit patterns, combined as floats).
+__device__ __forceinline__ float wave_max_f(float x) {
+  const uint32_t r = wave_last(wave_scan_incl(__float_as_uint(x), __float_as_uint(-INFINITY),
+                                              [](uint32_t a, uint32_t b) {
+                                                return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+                                              }));
+  return __uint_as_float(r);
+}
+
+__device__ __forceinline__ float wave_sum_f(float x) {
+  const uint32_t r = wave_last(wave_scan_incl(__float_as_uint(x), 0u, [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
+  return __uint_as_float(r);
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).  The compiler
 // folds it into its own wait tracking, so later waits count from here.
 template <int N>

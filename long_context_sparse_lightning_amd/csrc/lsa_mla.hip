@@ -386,13 +386,9 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(MlaParams P) {
     const bool has = tid < P.splits;
     const float ms = has ? P.ws_ml[(slot0 + tid) * kHeadGroup * 2 + 2 * hl] : -INFINITY;
     const float ls = has ? P.ws_ml[(slot0 + tid) * kHeadGroup * 2 + 2 * hl + 1] : 0.0f;
-    float mmax = ms;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off));
+    const float mmax = wave_max_f(ms);
     const float wgt = (ms == -INFINITY) ? 0.0f : exp2f(ms - mmax) * ls;
-    float L = wgt;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+    const float L = wave_sum_f(wgt);
     if (has) wsh[tid] = wgt;
     if (tid == 0) {
       Lsh = L;
