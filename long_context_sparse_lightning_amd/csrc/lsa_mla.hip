@@ -34,6 +34,7 @@
 //    behind later kernels) with its fp32 (max, sum); a combine kernel merges them with
 //    log-sum-exp weights in fp32.
 #include <algorithm>
+#include <type_traits>
 
 #include "lsa_internal.h"
 
@@ -44,10 +45,12 @@ constexpr int kThreads = 256;     // 4 wavefronts
 constexpr int kTile = 16;         // latent rows per tile
 constexpr int kStages = 3;        // LDS ring depth
 constexpr int kHeadGroup = 32;    // heads per workgroup
-constexpr int kMaxSplits = 64;
+constexpr int kMaxSplits = 64;    // one per lane in the combine
 constexpr int kMaxRowsPerSplit = 2048;  // row positions of a split staged in LDS
 constexpr int kPartStride = 20;   // floats per head in the partial-logit exchange (16 rows + pad)
 constexpr int kTargetWorkgroups = 512;  // two per CU
+constexpr int kCombineThreads = 256;   // four (row, head) pairs per workgroup
+constexpr size_t kWsAlign = 256;        // the partials start on this boundary of the workspace
 constexpr float kRescaleSlack = 8.0f;   // log2 units the running max may exceed the reference
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -90,6 +93,7 @@ struct MlaParams {
   const int32_t* seqlens;
   int Lq, H, S_max, topk;
   int hgroups, splits, kps;  // head groups, workgroups per (row, head group), rows per split
+  int pairs;                 // query rows x heads
   float scale_log2;
   uint16_t* out;
   float* lse;
@@ -128,7 +132,8 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int DQK, int DV>
+// SPARSE: the rows come from P.indices (else every position 0..p, the dense fallback).
+template <int DQK, int DV, bool SPARSE>
 __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
   using C = Cfg<DQK, DV>;
   __shared__ __attribute__((aligned(1024))) uint16_t ring[kStages][C::STAGE_UNITS * 8];
@@ -146,7 +151,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
   const int row = bid / P.hgroups;
   const int b = row / P.Lq;
   const int n = min(P.seqlens[b] - P.Lq + (row - b * P.Lq) + 1, P.S_max);
-  const bool sparse = P.indices != nullptr;
+  constexpr bool sparse = SPARSE;
   const int cnt = sparse ? min(P.n_sel[row], P.topk) : max(n, 0);
   const int j0 = split * P.kps;
   const int j1 = min(cnt, j0 + P.kps);
@@ -169,7 +174,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
     }
   }
   // this split's row positions (clamped into the cache) staged in LDS
-  if (sparse) {
+  if constexpr (sparse) {
     const int32_t* ilist = P.indices + static_cast<size_t>(row) * P.topk;
     for (int j = tid; j < j1 - j0; j += kThreads) slice[j] = min(max(ilist[j0 + j], 0), P.S_max - 1);
   }
@@ -188,15 +193,20 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
     dma_r[k] = r;
     dma_c[k] = real ? C::logical(r, u - r * C::UNITS) : 0;
   }
-  auto issue = [&](int tile) {
-    uint16_t* stage = ring[tile % kStages];
+  // cache row positions of the next tile to be issued, read from LDS one step ahead so that
+  // the issue itself waits on nothing
+  int pos[C::DPW];
+  auto fetch_pos = [&](int tile) {
     const int jb = tile * kTile;  // relative to j0
-    int pos[C::DPW];
 #pragma unroll
     for (int k = 0; k < C::DPW; ++k) {
       const int j = min(jb + dma_r[k], j1 - j0 - 1);  // rows past the slice repeat its last row
-      pos[k] = sparse ? slice[j] : j0 + j;
+      if constexpr (sparse) pos[k] = slice[j];
+      else pos[k] = j0 + j;
     }
+  };
+  auto issue = [&](int tile) {
+    uint16_t* stage = ring[tile % kStages];
 #pragma unroll
     for (int k = 0; k < C::DPW; ++k) {
       const uint16_t* src = kv_b + static_cast<size_t>(pos[k]) * DQK + 8 * dma_c[k];
@@ -204,8 +214,13 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
                      (lds_void*)(stage + (4 * k + wave) * kWave * 8))));
     }
   };
-  if (ntiles > 0) issue(0);
-  if (ntiles > 1) issue(1);
+  if (ntiles > 0) {
+    fetch_pos(0);
+    issue(0);
+    fetch_pos(1);
+    if (ntiles > 1) issue(1);
+    fetch_pos(2);
+  }
 
   float m_ref = -INFINITY, l_run = 0.0f;  // for head `col` (identical in every wavefront)
   f32x16 o[C::NBW];
@@ -215,33 +230,39 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
   for (int t = 0; t < ntiles; ++t) {
     if (t + 1 < ntiles) wait_vmcnt<C::DPW>();  // tile t+1 may still be in flight
     else wait_vmcnt<0>();
-    ring_barrier();  // every wavefront's pieces of tile t are in LDS
+    ring_barrier();  // every wavefront's pieces of tile t are in LDS; tile t - 1 is consumed
+    // tile t + 2 goes into the stage of tile t - 1: every wavefront has passed the barrier
+    // above, so all of its reads of that stage (and of the partial logits) are complete
+    if (t + 2 < ntiles) {
+      issue(t + 2);
+      fetch_pos(t + 3);
+    }
 
     const uint16_t* kvt = ring[t % kStages];
     // ---- partial logits over this wavefront's Dqk steps, as S^T = KV_tile . Q^T so that a
     // lane holds one head (c16) for four consecutive tile rows (4*q16 + r): one 16-byte LDS
     // write per head block
     {
+      // every wavefront runs KSW steps: a step past Dqk reads an in-range unit (finite cache
+      // values) against the zero query fragment loaded for it, so it adds exactly 0
       f32x4 acc0 = {}, acc1 = {};
+      bf16x8 kb[C::KSW];
 #pragma unroll
       for (int i = 0; i < C::KSW; ++i) {
-        const int ks = wave + 4 * i;
-        const int c = 4 * ks + q16;  // logical unit
-        if (ks < C::KS) {
-          const bf16x8 kb = c < C::UNITS
-                                ? __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                                 &kvt[C::slot(c16, c) * 8]))
-                                : zero_bf16x8();
-          acc0 = mfma16(kb, qf[0][i], acc0);
-          acc1 = mfma16(kb, qf[1][i], acc1);
-        }
+        const int c = 4 * (wave + 4 * i) + q16;  // logical unit
+        kb[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                               &kvt[C::slot(c16, min(c, C::UNITS - 1)) * 8]));
+      }
+#pragma unroll
+      for (int i = 0; i < C::KSW; ++i) {
+        acc0 = mfma16(kb[i], qf[0][i], acc0);
+        acc1 = mfma16(kb[i], qf[1][i], acc1);
       }
       float* sp = spart[wave];
       *reinterpret_cast<f32x4*>(&sp[c16 * kPartStride + 4 * q16]) = acc0;
       *reinterpret_cast<f32x4*>(&sp[(16 + c16) * kPartStride + 4 * q16]) = acc1;
     }
     ring_barrier();  // partial logits of all wavefronts published
-    if (t + 2 < ntiles) issue(t + 2);  // into the stage freed at the end of the previous step
 
     // ---- logits of head `col` for the tile rows of A-operand slots e: acc_row(e, g)
     float sv[8];
@@ -259,6 +280,28 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
       for (int e = 0; e < 4; ++e) {
         sv[e] = lo[e];
         sv[4 + e] = hi[e];
+      }
+    }
+
+    // ---- value-operand fragments of this wavefront's 32-column blocks: they do not depend on
+    // the probabilities, so they are requested here and arrive during the softmax.  Each B
+    // operand (8 tile rows of one column per lane) is two LDS transpose reads.
+    u32x2 hv[C::NBW][2];
+    {
+      const int G = lane >> 4, jl = lane & 15;  // transpose reads: 16 columns x 4 rows per group
+#pragma unroll
+      for (int i = 0; i < C::NBW; ++i) {
+        const int nb = wave + 4 * i;
+        if (C::NB % 4 == 0 || nb < C::NB) {  // statically true when the blocks divide evenly
+          const int dim0 = 32 * nb + 16 * (G & 1) + 4 * (jl & 3);
+          const int unit = dim0 >> 3, eoff = dim0 & 7;
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int vr = 8 * h2 + 4 * (G >> 1) + (jl >> 2);  // = acc_row(4*h2 + k, g) for slot k
+            hv[i][h2] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(&kvt[C::slot(vr, unit) * 8 + eoff])));
+          }
+        }
       }
     }
 
@@ -302,29 +345,17 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
     // A operand: k-slot e of lane half g is tile row acc_row(e, g)
     const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
 
-    // ---- values: this wavefront's 32-column blocks nb = wave + 4i
-    {
-      const int G = lane >> 4, jl = lane & 15;  // transpose reads: 16 columns x 4 rows per group
+    // ---- values: O (32 heads x this wavefront's blocks nb = wave + 4i) += P . V_tile
 #pragma unroll
-      for (int i = 0; i < C::NBW; ++i) {
-        const int nb = wave + 4 * i;
-        if (C::NB % 4 == 0 || nb < C::NB) {  // statically true when the blocks divide evenly
-          const int dim0 = 32 * nb + 16 * (G & 1) + 4 * (jl & 3);
-          const int unit = dim0 >> 3, eoff = dim0 & 7;
-          u32x2 hv[2];
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const int vr = 8 * h2 + 4 * (G >> 1) + (jl >> 2);  // = acc_row(4*h2 + k, g) for slot k
-            hv[h2] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(&kvt[C::slot(vr, unit) * 8 + eoff])));
-          }
-          o[i] = mfma32(pa, __builtin_bit_cast(bf16x8, u32x4{hv[0].x, hv[0].y, hv[1].x, hv[1].y}), o[i]);
-        }
-      }
+    for (int i = 0; i < C::NBW; ++i) {
+      const int nb = wave + 4 * i;
+      if (C::NB % 4 == 0 || nb < C::NB)
+        o[i] = mfma32(pa, __builtin_bit_cast(bf16x8, u32x4{hv[i][0].x, hv[i][0].y, hv[i][1].x, hv[i][1].y}),
+                      o[i]);
     }
-    ring_barrier();  // tile t's stage and the partial logits may be overwritten
   }
   wait_vmcnt<0>();
+  __syncthreads();  // the epilogue below reuses the ring: every wavefront's last reads are done
 
   // ---- epilogue: normalise, round to bf16 and stage this workgroup's [32 heads x DV] block in
   // LDS (the ring is free now), then write it out with 16-byte stores: rows of the output for
@@ -369,65 +400,95 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
   }
 }
 
-// Merge the split partials of one (row, head) with log-sum-exp weights, in a fixed order.
-// Partial s holds O_s / l_s (bf16) and (m_s, l_s); its weight is l_s * 2^(m_s - max).  All
-// weights are formed first, then every thread streams its 4 output columns of all splits with
-// independent loads.
+// Merge the split partials of one (row, head) with log-sum-exp weights, in a fixed order: one
+// wavefront per (row, head), lane l owning output columns [CPL*l, CPL*l + CPL).  Partial s holds
+// O_s / l_s (bf16) and (m_s, l_s); its weight is l_s * 2^(m_s - max).  Lane s reads split s's
+// (m, l) and every lane requests its columns of the first 16 splits right behind it, so the
+// weights are formed (DPP reductions, no LDS) while the partial outputs are in flight.
 template <int DV>
-__global__ __launch_bounds__(128) void mla_combine_kernel(MlaParams P) {
-  __shared__ float wsh[kMaxSplits];
-  __shared__ float Lsh;
-  const int row = blockIdx.x / P.H;
-  const int head = blockIdx.x - row * P.H;
+__global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(MlaParams P) {
+  constexpr int CPL = DV / kWave;  // output columns per lane
+  static_assert(DV % kWave == 0 && (CPL == 8 || CPL == 1), "combine handles DV = 512 or 64");
+  static_assert(kMaxSplits <= kWave && kMaxSplits % 16 == 0, "one split per lane, whole batches");
+  using Piece = typename std::conditional<CPL == 8, u32x4, uint32_t>::type;
+  constexpr int kBatch = 16;  // partial loads in flight per lane
+  const int lane = threadIdx.x & 63;
+  const int pair = static_cast<int>(blockIdx.x) * (kCombineThreads / kWave) +
+                   __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (pair >= P.pairs) return;  // whole wavefronts
+  const int row = pair / P.H, head = pair - row * P.H;
   const int hg = head / kHeadGroup, hl = head - hg * kHeadGroup;
+  const int S = P.splits;
   const size_t slot0 = (static_cast<size_t>(row) * P.hgroups + hg) * P.splits;
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    const bool has = tid < P.splits;
-    const float ms = has ? P.ws_ml[(slot0 + tid) * kHeadGroup * 2 + 2 * hl] : -INFINITY;
-    const float ls = has ? P.ws_ml[(slot0 + tid) * kHeadGroup * 2 + 2 * hl + 1] : 0.0f;
-    const float mmax = wave_max_f(ms);
-    const float wgt = (ms == -INFINITY) ? 0.0f : exp2f(ms - mmax) * ls;
-    const float L = wave_sum_f(wgt);
-    if (has) wsh[tid] = wgt;
-    if (tid == 0) {
-      Lsh = L;
-      if (P.lse)
-        P.lse[static_cast<size_t>(row) * P.H + head] =
-            L > 0.0f ? (mmax + __log2f(L)) * kLn2 : -INFINITY;
+  const size_t stride = static_cast<size_t>(kHeadGroup) * DV;
+  const uint16_t* src = P.ws_o + (slot0 * kHeadGroup + hl) * DV + CPL * lane;
+  // (m, l) of split `lane`; lanes past the last split read it too and are given weight 0
+  const float2 ml = *reinterpret_cast<const float2*>(
+      &P.ws_ml[((slot0 + min(lane, S - 1)) * kHeadGroup + hl) * 2]);
+  Piece v[kBatch];
+  auto fetch = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const uint16_t* at = src + static_cast<size_t>(min(s0 + u, S - 1)) * stride;
+      if constexpr (CPL == 8) v[u] = *reinterpret_cast<const u32x4*>(at);
+      else v[u] = *at;
     }
+  };
+  fetch(0);
+  __builtin_amdgcn_sched_barrier(0);  // keep the partial loads ahead of the weights
+  const float ms = lane < S ? ml.x : -INFINITY;
+  const float mmax = wave_max_f(ms);
+  const float wgt = (ms == -INFINITY) ? 0.0f : exp2f(ms - mmax) * ml.y;
+  const float L = wave_sum_f(wgt);
+  float acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.0f;
+  for (int s0 = 0;;) {
+    // splits past the last (s0 + u >= S < 64) have weight 0 and re-read split S - 1
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), s0 + u));
+      if constexpr (CPL == 8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += w * __uint_as_float(v[u][i] << 16);
+          acc[2 * i + 1] += w * __uint_as_float(v[u][i] & 0xffff0000u);
+        }
+      } else {
+        acc[0] += w * __uint_as_float(v[u] << 16);
+      }
+    }
+    s0 += kBatch;
+    if (s0 >= S) break;
+    fetch(s0);
   }
-  __syncthreads();
-  const float L = Lsh;
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  for (int c4 = tid; c4 < DV / 4; c4 += blockDim.x) {
-    const uint16_t* src = P.ws_o + (slot0 * kHeadGroup + hl) * DV + 4 * c4;
-    const size_t stride = static_cast<size_t>(kHeadGroup) * DV;
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    auto add = [&](float wgt, uint2 v) {
-      acc[0] += wgt * __uint_as_float(v.x << 16);
-      acc[1] += wgt * __uint_as_float(v.x & 0xffff0000u);
-      acc[2] += wgt * __uint_as_float(v.y << 16);
-      acc[3] += wgt * __uint_as_float(v.y & 0xffff0000u);
-    };
-    int s = 0;
-    for (; s + 8 <= P.splits; s += 8) {
-      uint2 v[8];
+  uint16_t* dst = P.out + (static_cast<size_t>(row) * P.H + head) * DV + CPL * lane;
+  if constexpr (CPL == 8) {
+    uint32_t w[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const uint2*>(src + (s + u) * stride);
+    for (int i = 0; i < 4; ++i)
+      w[i] = __builtin_bit_cast(uint32_t, bf16x2{static_cast<__bf16>(acc[2 * i] * inv),
+                                                 static_cast<__bf16>(acc[2 * i + 1] * inv)});
+    if ((reinterpret_cast<uintptr_t>(P.out) & 15u) == 0u) {
+      *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+    } else {  // a caller buffer without 16-byte alignment
 #pragma unroll
-      for (int u = 0; u < 8; ++u) add(wsh[s + u], v[u]);
+      for (int i = 0; i < 4; ++i) {
+        dst[2 * i] = static_cast<uint16_t>(w[i]);
+        dst[2 * i + 1] = static_cast<uint16_t>(w[i] >> 16);
+      }
     }
-    for (; s < P.splits; ++s) add(wsh[s], *reinterpret_cast<const uint2*>(src + s * stride));
-    uint16_t* dst = P.out + (static_cast<size_t>(row) * P.H + head) * DV + 4 * c4;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dst[e] = bf16_bits_rne(acc[e] * inv);
+  } else {
+    dst[0] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[0] * inv));
   }
+  if (lane == 0 && P.lse)
+    P.lse[static_cast<size_t>(row) * P.H + head] = L > 0.0f ? (mmax + __log2f(L)) * kLn2 : -INFINITY;
 }
 
 struct MlaPlan {
   int hgroups = 1, splits = 1, kps = 0;
-  size_t ws_o_bytes = 0, ws_ml_bytes = 0;
+  size_t ws_o_bytes = 0, ws_ml_bytes = 0, ws_slack = 0;
 };
 
 MlaPlan make_plan(long rows, int H, int Dv, int S_max, int topk, int dense) {
@@ -452,6 +513,7 @@ MlaPlan make_plan(long rows, int H, int Dv, int S_max, int topk, int dense) {
     const size_t slots = static_cast<size_t>(units) * pl.splits;
     pl.ws_o_bytes = (slots * kHeadGroup * Dv * 2 + 255) & ~static_cast<size_t>(255);
     pl.ws_ml_bytes = (slots * kHeadGroup * 2 * 4 + 255) & ~static_cast<size_t>(255);
+    pl.ws_slack = kWsAlign;  // the caller's buffer may start anywhere
   }
   return pl;
 }
@@ -460,12 +522,18 @@ template <int DQK, int DV>
 hipError_t launch_dims(const MlaParams& P, long rows, hipStream_t stream) {
   const long grid = rows * P.hgroups * P.splits;
   if (grid > 0x7fffffffL || rows * P.H > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((sparse_mla_kernel<DQK, DV>), dim3(static_cast<unsigned>(grid)),
-                     dim3(kThreads), 0, stream, P);
+  if (P.indices)
+    hipLaunchKernelGGL((sparse_mla_kernel<DQK, DV, true>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kThreads), 0, stream, P);
+  else
+    hipLaunchKernelGGL((sparse_mla_kernel<DQK, DV, false>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kThreads), 0, stream, P);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || P.splits == 1) return err;
-  hipLaunchKernelGGL((mla_combine_kernel<DV>), dim3(static_cast<unsigned>(rows * P.H)), dim3(128), 0,
-                     stream, P);
+  constexpr int kPairsPerGroup = kCombineThreads / kWave;
+  hipLaunchKernelGGL((mla_combine_kernel<DV>),
+                     dim3(static_cast<unsigned>((rows * P.H + kPairsPerGroup - 1) / kPairsPerGroup)),
+                     dim3(kCombineThreads), 0, stream, P);
   return hipGetLastError();
 }
 
@@ -473,7 +541,7 @@ hipError_t launch_dims(const MlaParams& P, long rows, hipStream_t stream) {
 
 size_t mla_workspace_bytes(int B, int Lq, int H, int Dv, int S_max, int topk, int dense) {
   const MlaPlan pl = make_plan(static_cast<long>(B) * Lq, H, Dv, S_max, topk, dense);
-  return pl.ws_o_bytes + pl.ws_ml_bytes;
+  return pl.ws_o_bytes + pl.ws_ml_bytes + pl.ws_slack;
 }
 
 hipError_t launch_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indices,
@@ -498,8 +566,11 @@ hipError_t launch_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indi
   P.scale_log2 = softmax_scale * kLog2e;
   P.out = out;
   P.lse = lse;
-  P.ws_o = static_cast<uint16_t*>(workspace);
-  P.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ws_o_bytes);
+  P.pairs = static_cast<int>(std::min<long>(rows * H, 0x7fffffffL));
+  char* ws = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(workspace) + kWsAlign - 1) &
+                                     ~static_cast<uintptr_t>(kWsAlign - 1));
+  P.ws_o = reinterpret_cast<uint16_t*>(ws);
+  P.ws_ml = reinterpret_cast<float*>(ws + pl.ws_o_bytes);
   if (Dqk == 576 && Dv == 512) return launch_dims<576, 512>(P, rows, stream);
   if (Dqk == 80 && Dv == 64) return launch_dims<80, 64>(P, rows, stream);
   return hipErrorInvalidValue;
