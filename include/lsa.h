@@ -33,6 +33,10 @@
  *   lsa_last_error() then describes them (thread-local).  A zero-sized batch (B == 0 or
  *   Lq == 0) is a valid no-op.  A kernel-launch failure returns LSA_ERR_LAUNCH.  Faults in
  *   device memory surface at the caller's next synchronisation, as usual for HIP.
+ * - Workspaces are device buffers of at least the size the matching *_workspace_bytes query
+ *   returns, at any address (the sizes include the slack the library needs to align its
+ *   regions inside); their contents on entry do not matter, and two calls in flight must not
+ *   share one.
  * - Results are deterministic: identical inputs give bit-identical outputs.
  * - No global mutable state except the thread-local error text.
  */

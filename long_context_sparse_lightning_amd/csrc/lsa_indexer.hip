@@ -479,7 +479,7 @@ size_t index_topk_workspace_bytes(int B, int Lq, int S_max, int topk, int init_t
   (void)init_tokens;
   (void)local_tokens;
   const FusedPlan pl = fused_plan(B, Lq, S_max);
-  return pl.count_bytes + pl.range_bytes + pl.cand_bytes;
+  return pl.count_bytes + pl.range_bytes + pl.cand_bytes + kWorkspaceAlign;
 }
 
 hipError_t launch_index_topk(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
@@ -502,7 +502,7 @@ hipError_t launch_index_topk(const uint16_t* q_idx, const float* w, const uint16
   P.init = init_tokens;
   P.local = local_tokens;
   P.R = topk - init_tokens - local_tokens;
-  char* ws = static_cast<char*>(workspace);
+  char* ws = align_workspace(workspace);
   P.count = reinterpret_cast<uint32_t*>(ws);
   P.range = reinterpret_cast<uint32_t*>(ws + pl.count_bytes);
   P.cand = reinterpret_cast<uint2*>(ws + pl.count_bytes + pl.range_bytes);

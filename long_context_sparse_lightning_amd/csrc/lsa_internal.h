@@ -115,6 +115,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// ------------------------------------------------------------------ workspaces
+// A caller's workspace may start at any address.  Every workspace size includes this much slack
+// and the launchers use the buffer from its first kWorkspaceAlign-byte boundary, so the regions
+// inside it can be read and written with 16-byte (and wider) accesses.
+constexpr size_t kWorkspaceAlign = 256;
+inline char* align_workspace(void* p) {
+  return reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(p) + kWorkspaceAlign - 1) &
+                                 ~static_cast<uintptr_t>(kWorkspaceAlign - 1));
+}
+
 // ------------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error; arguments were validated by the C-ABI layer.
 hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,

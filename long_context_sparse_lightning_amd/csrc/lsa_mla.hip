@@ -50,7 +50,6 @@ constexpr int kMaxRowsPerSplit = 2048;  // row positions of a split staged in LD
 constexpr int kPartStride = 20;   // floats per head in the partial-logit exchange (16 rows + pad)
 constexpr int kTargetWorkgroups = 512;  // two per CU
 constexpr int kCombineThreads = 256;   // four (row, head) pairs per workgroup
-constexpr size_t kWsAlign = 256;        // the partials start on this boundary of the workspace
 constexpr float kRescaleSlack = 8.0f;   // log2 units the running max may exceed the reference
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -513,7 +512,7 @@ MlaPlan make_plan(long rows, int H, int Dv, int S_max, int topk, int dense) {
     const size_t slots = static_cast<size_t>(units) * pl.splits;
     pl.ws_o_bytes = (slots * kHeadGroup * Dv * 2 + 255) & ~static_cast<size_t>(255);
     pl.ws_ml_bytes = (slots * kHeadGroup * 2 * 4 + 255) & ~static_cast<size_t>(255);
-    pl.ws_slack = kWsAlign;  // the caller's buffer may start anywhere
+    pl.ws_slack = kWorkspaceAlign;
   }
   return pl;
 }
@@ -567,8 +566,7 @@ hipError_t launch_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indi
   P.out = out;
   P.lse = lse;
   P.pairs = static_cast<int>(std::min<long>(rows * H, 0x7fffffffL));
-  char* ws = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(workspace) + kWsAlign - 1) &
-                                     ~static_cast<uintptr_t>(kWsAlign - 1));
+  char* ws = align_workspace(workspace);
   P.ws_o = reinterpret_cast<uint16_t*>(ws);
   P.ws_ml = reinterpret_cast<float*>(ws + pl.ws_o_bytes);
   if (Dqk == 576 && Dv == 512) return launch_dims<576, 512>(P, rows, stream);

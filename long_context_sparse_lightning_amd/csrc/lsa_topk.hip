@@ -319,7 +319,7 @@ struct Plan {
   int R = 0, chunks = 1;
   long group = 1;  // rows per launch pair
   size_t count_bytes = 0, range_bytes = 0, cand_bytes = 0;
-  size_t total() const { return count_bytes + range_bytes + cand_bytes; }
+  size_t total() const { return count_bytes + range_bytes + cand_bytes + kWorkspaceAlign; }
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -373,7 +373,7 @@ hipError_t launch_topk(const float* scores, const int32_t* seqlens, int B, int L
   P.R = pl.R;
   P.chunks = pl.chunks;
   P.chunk_keys = kChunk;
-  char* ws = static_cast<char*>(workspace);
+  char* ws = align_workspace(workspace);
   P.count = reinterpret_cast<uint32_t*>(ws);
   P.range = reinterpret_cast<uint32_t*>(ws + pl.count_bytes);
   P.cand = reinterpret_cast<uint2*>(ws + pl.count_bytes + pl.range_bytes);

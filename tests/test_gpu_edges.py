@@ -230,6 +230,27 @@ def test_attention_buffers_without_16_byte_alignment():
     assert torch.equal(refp, outp)
 
 
+def test_selection_workspace_at_an_odd_address():
+    """The top-k and fused calls place their candidate lists from the workspace's first 256-byte
+    boundary: a workspace that starts 3 bytes past one gives the same indices, bit for bit."""
+    wl = SMALL[5]  # several top-k chunks per row
+    X = device_inputs(wl)
+    sc = lsa.lsa_index_scores(X["qidx"], X["w"], X["kidx"], X["seqlens"])
+    for query, call in (
+            (lsa.lsa_topk_workspace_bytes,
+             lambda ws: lsa.lsa_topk_select(sc, X["seqlens"], wl.topk, wl.init, wl.local,
+                                            workspace=ws)),
+            (lsa.lsa_index_topk_workspace_bytes,
+             lambda ws: lsa.lsa_index_topk(X["qidx"], X["w"], X["kidx"], X["seqlens"], wl.topk,
+                                           wl.init, wl.local, workspace=ws))):
+        need = query(wl.B, wl.Lq, wl.S_max, wl.topk, wl.init, wl.local)
+        buf = torch.empty(need + 64, dtype=torch.uint8, device="cuda")
+        ref_idx, ref_n = call(buf[:need])
+        odd_idx, odd_n = call(buf[3:3 + need])
+        torch.cuda.synchronize()
+        assert torch.equal(ref_idx, odd_idx) and torch.equal(ref_n, odd_n)
+
+
 def test_prefill_rows_equal_decode_calls():
     """Row i of a prefill chunk (query-blocked scan, Di = 128) selects exactly what a decode call
     at seqlen p + 1 selects for the same query, and its attention agrees within tolerance (the
