@@ -138,6 +138,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
   __shared__ __attribute__((aligned(1024))) uint16_t ring[kStages][C::STAGE_UNITS * 8];
   __shared__ __attribute__((aligned(16))) float spart[4][kHeadGroup * kPartStride];  // partial logits
   __shared__ int32_t slice[kMaxRowsPerSplit];
+  __shared__ __attribute__((aligned(16))) float inv_head[kHeadGroup];  // 1 / l per head (epilogue)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
@@ -354,24 +355,39 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
     }
   }
   wait_vmcnt<0>();
+  if (wave == 0 && g == 0) inv_head[col] = l_run > 0.0f ? 1.0f / l_run : 0.0f;
   __syncthreads();  // the epilogue below reuses the ring: every wavefront's last reads are done
 
   // ---- epilogue: normalise, round to bf16 and stage this workgroup's [32 heads x DV] block in
   // LDS (the ring is free now), then write it out with 16-byte stores: rows of the output for
   // one split, or this head group's rows of `out` when there is a single split
   {
-    const float inv_c = l_run > 0.0f ? 1.0f / l_run : 0.0f;  // head `col`
     uint16_t* tb = &ring[0][0];
     static_assert(kStages * C::STAGE_UNITS * 8 >= kHeadGroup * DV, "the ring holds the block");
+    // 1 / l of the heads this lane holds: rows acc_row(r, g) = 8 (r / 4) + 4 g + r % 4
+    f32x4 inv4[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int hr = acc_row(r, g);
-      const float inv = __shfl(inv_c, hr);
+    for (int q = 0; q < 4; ++q) inv4[q] = *reinterpret_cast<const f32x4*>(&inv_head[8 * q + 4 * g]);
+    // adjacent columns live in lanes col and col ^ 1: one DPP swap per row pair lets the even
+    // lane write row r's columns (col, col + 1) and the odd lane row r + 1's (col - 1, col) as
+    // one 4-byte store each
+    const bool odd = (col & 1) != 0;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const int hrow = acc_row(r, g) + (odd ? 1 : 0);  // acc_row(r + 1, g) = acc_row(r, g) + 1
+      const float i0 = inv4[r >> 2][r & 3], i1 = inv4[r >> 2][(r & 3) + 1];
 #pragma unroll
       for (int i = 0; i < C::NBW; ++i) {
         const int nb = wave + 4 * i;
-        if (C::NB % 4 == 0 || nb < C::NB)
-          tb[hr * DV + 32 * nb + col] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(o[i][r] * inv));
+        if (C::NB % 4 == 0 || nb < C::NB) {
+          const float v0 = o[i][r] * i0, v1 = o[i][r + 1] * i1;
+          const float got = __int_as_float(__builtin_amdgcn_update_dpp(
+              0, __float_as_int(odd ? v0 : v1), 0xB1, 0xf, 0xf, false));  // quad_perm [1,0,3,2]
+          const bf16x2 pr = odd ? bf16x2{static_cast<__bf16>(got), static_cast<__bf16>(v1)}
+                                : bf16x2{static_cast<__bf16>(v0), static_cast<__bf16>(got)};
+          *reinterpret_cast<uint32_t*>(&tb[hrow * DV + 32 * nb + (col & ~1)]) =
+              __builtin_bit_cast(uint32_t, pr);
+        }
       }
     }
     __syncthreads();
