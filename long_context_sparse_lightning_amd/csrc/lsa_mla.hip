@@ -359,8 +359,9 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
   __syncthreads();  // the epilogue below reuses the ring: every wavefront's last reads are done
 
   // ---- epilogue: normalise, round to bf16 and stage this workgroup's [32 heads x DV] block in
-  // LDS (the ring is free now), then write it out with 16-byte stores: rows of the output for
-  // one split, or this head group's rows of `out` when there is a single split
+  // LDS (the ring is free now), then write it out with 16-byte nontemporal stores (read once, by
+  // the combine): rows of the output for one split, or this head group's rows of `out` when
+  // there is a single split
   {
     uint16_t* tb = &ring[0][0];
     static_assert(kStages * C::STAGE_UNITS * 8 >= kHeadGroup * DV, "the ring holds the block");
@@ -399,7 +400,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
     const int n_out = rows_out * DV;  // elements of the block that exist in the destination
     if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0u) {
       for (int e = 8 * tid; e < n_out; e += 8 * kThreads)
-        *reinterpret_cast<u32x4*>(dst + e) = *reinterpret_cast<const u32x4*>(tb + e);
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(tb + e), reinterpret_cast<u32x4*>(dst + e));
     } else {  // a caller buffer without 16-byte alignment
       for (int e = tid; e < n_out; e += kThreads) dst[e] = tb[e];
     }
@@ -445,7 +446,7 @@ __global__ __launch_bounds__(kCombineThreads) void mla_combine_kernel(MlaParams 
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const uint16_t* at = src + static_cast<size_t>(min(s0 + u, S - 1)) * stride;
-      if constexpr (CPL == 8) v[u] = *reinterpret_cast<const u32x4*>(at);
+      if constexpr (CPL == 8) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(at));
       else v[u] = *at;
     }
   };
