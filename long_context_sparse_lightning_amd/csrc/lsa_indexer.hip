@@ -124,10 +124,16 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
     const int h = acc_row(r, g);
     wr[r] = h < Hi ? w[static_cast<size_t>(row) * Hi + h] : 0.0f;
   }
+  extern __shared__ __attribute__((aligned(16))) float stage[];  // [keys_per_wg] scores of this chunk
+  // fused variant: the selection's histogram (2 * kBins words) follows the scores and is cleared
+  // now, while the query loads are in flight, so the selection after the scan starts with it
+  uint32_t* hist = reinterpret_cast<uint32_t*>(stage + keys_per_wg);  // keys_per_wg % 128 == 0
+  if constexpr (FUSED)
+    for (int i = threadIdx.x; i < 2 * sel::kBins / 4; i += kThreads)
+      reinterpret_cast<u32x4*>(hist)[i] = u32x4{0u, 0u, 0u, 0u};
   wait_vmcnt<0>();  // the query and weights are in: only key tiles are in flight below
 
   const uint16_t* kb_base = k_idx + static_cast<size_t>(b) * S_max * DI + g * (DI / 2);
-  extern __shared__ __attribute__((aligned(16))) float stage[];  // [keys_per_wg] scores of this chunk
 
   // rows past the end of a partial tile re-read the chunk's last key
   auto load_tile = [&](bf16x8 (&dst)[NC], int t0) {
@@ -135,6 +141,9 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) dst[c] = load_bf16x8(kp + 8 * c);
   };
+  // fused variant: bounds of the order keys of the competing positions this lane has scored
+  // (both lane halves hold the same score), for the selection's digit window
+  uint32_t run_mn = 0xffffffffu, run_mx = 0u;
   auto score_tile = [&](const bf16x8 (&src)[NC], int t0) {
     f32x16 acc = {};
 #pragma unroll
@@ -142,8 +151,14 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
     float part = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) part += wr[r] * fmaxf(acc[r], 0.0f);
-    const float other = xor32(part);
-    if (g == 0) stage[t0 - start + col] = part + other;  // t0 - start + col < keys_per_wg
+    const float score = part + xor32(part);
+    if (g == 0) stage[t0 - start + col] = score;  // t0 - start + col < keys_per_wg
+    if constexpr (FUSED) {
+      const uint32_t k = sel::order_key(score);
+      const bool ok = t0 + col >= comp_a && t0 + col <= comp_z;
+      run_mn = ok ? min(run_mn, k) : run_mn;
+      run_mx = ok ? max(run_mx, k) : run_mx;
+    }
   };
 
   // tiles of this wavefront: t0 + i * kWgStride for i < ntiles; two per iteration, so both
@@ -191,11 +206,10 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
       key[j] = ok ? sel::order_key(v) : 0u;
       valid |= (ok ? 1u : 0u) << j;
     }
-    __syncthreads();  // the stage is reused as the histogram
-    sel::chunk_candidates<kThreads, kStageItems>(
-        key, valid, z - a + 1, P.R, start, reinterpret_cast<uint32_t*>(stage), sh,
+    sel::chunk_candidates<kThreads, kStageItems, true>(
+        key, valid, z - a + 1, P.R, start, hist, sh,
         P.cand + static_cast<size_t>(blockIdx.x) * keys_per_wg, P.count + blockIdx.x,
-        P.range + 2 * blockIdx.x);
+        P.range + 2 * blockIdx.x, run_mn, run_mx);
   }
 }
 
@@ -417,7 +431,13 @@ template <int DI, bool FUSED>
 hipError_t launch_kernel(const IndexParams& P, long grid, hipStream_t stream) {
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
   size_t lds = static_cast<size_t>(P.keys_per_wg) * sizeof(float);
-  if (FUSED) lds = std::max(lds, static_cast<size_t>(2 * sel::kBins) * sizeof(uint32_t));
+  if (FUSED) {
+    lds += static_cast<size_t>(2 * sel::kBins) * sizeof(uint32_t);  // the selection's histogram
+    const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(index_scores_kernel<DI, FUSED>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               static_cast<int>(lds));
+    if (err != hipSuccess) return err;
+  }
   hipLaunchKernelGGL((index_scores_kernel<DI, FUSED>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
                      lds, stream, P);
   return hipGetLastError();

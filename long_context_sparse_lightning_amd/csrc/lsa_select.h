@@ -133,24 +133,29 @@ constexpr int chunk_scratch_words() { return 3 * (THREADS / kWave) + 4; }
 // position) pairs, their number to *count, and bounds lo <= every written key <= hi to
 // range[0], range[1].  hist: 2*kBins words of LDS, zeroed here; sh:
 // chunk_scratch_words<THREADS>() words.  Call from every thread, with m >= 1.
-template <int THREADS, int ITEMS>
+// PREPARED: the caller has already zeroed hist (and ordered that before this call by a
+// barrier) and passes in (mn, mx) bounds whose workgroup-wide min and max are those of the
+// valid keys -- a scan that produced the keys can track them on the way.
+template <int THREADS, int ITEMS, bool PREPARED = false>
 __device__ void chunk_candidates(const uint32_t (&key)[ITEMS], uint32_t valid, int m, int R,
                                  int base, uint32_t* hist, uint32_t* sh, uint2* out,
-                                 uint32_t* count, uint32_t* range) {
+                                 uint32_t* count, uint32_t* range, uint32_t mn = 0xffffffffu,
+                                 uint32_t mx = 0u) {
   constexpr int WAVES = THREADS / kWave;
   uint32_t* sh_scan = sh;
   uint32_t* sh_mm = sh + WAVES;
   uint32_t* sh_out = sh + 3 * WAVES;
   const int tid = threadIdx.x, wave = tid >> 6;
   uint32_t keep = valid;
-  if (m > R)  // hist is 16-byte aligned
-    for (int i = tid; i < 2 * kBins / 4; i += THREADS) reinterpret_cast<u32x4*>(hist)[i] = u32x4{0u, 0u, 0u, 0u};
-  uint32_t mn = 0xffffffffu, mx = 0u;
+  if constexpr (!PREPARED) {
+    if (m > R)  // hist is 16-byte aligned
+      for (int i = tid; i < 2 * kBins / 4; i += THREADS) reinterpret_cast<u32x4*>(hist)[i] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int j = 0; j < ITEMS; ++j) {
-    if (valid & (1u << j)) {
-      mn = min(mn, key[j]);
-      mx = max(mx, key[j]);
+    for (int j = 0; j < ITEMS; ++j) {
+      if (valid & (1u << j)) {
+        mn = min(mn, key[j]);
+        mx = max(mx, key[j]);
+      }
     }
   }
   block_minmax<WAVES>(mn, mx, sh_mm);  // its barrier also orders the zeroing
