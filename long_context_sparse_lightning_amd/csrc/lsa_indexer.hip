@@ -213,7 +213,9 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
   }
 }
 
-constexpr int kQbWaves = 8;        // wavefronts per workgroup, two query rows each
+constexpr int kQbWaves = 8;        // wavefronts per workgroup (two per SIMD)
+constexpr int kQbRowsPerWave = 2;  // query rows per wavefront (4 at one wavefront per SIMD,
+                                   // 416 registers, is 13% slower: nothing hides the barriers)
 constexpr int kQbMinRows = 16;     // row count from which the query-blocked scan is used
 constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3 for gfx9-family raw buffers
 constexpr int kDropOffset = 1 << 30;      // beyond any row: such stores are dropped
@@ -230,15 +232,15 @@ struct QbParams {
   float* scores;
 };
 
-// 2 * WAVES query rows x one key chunk; Di = 128 (16 units of 16 bytes per key).  Workgroups of
-// four wavefronts run two to a CU, so while one waits at its per-tile barrier the other keeps
-// the matrix cores busy.
-template <int WAVES>
+// RPW * WAVES query rows x one key chunk; Di = 128 (16 units of 16 bytes per key).  RPW rows per
+// wavefront share every key fragment read from LDS (RPW matrix-core steps per read).
+template <int WAVES, int RPW>
 __global__ __launch_bounds__(64 * WAVES, 1) void index_scores_qb_kernel(QbParams P) {
   constexpr int DI = 128, NC = DI / 16, UK = DI / 8;
-  constexpr int THREADS = 64 * WAVES, ROWS = 2 * WAVES;
+  constexpr int THREADS = 64 * WAVES, ROWS = RPW * WAVES;
   constexpr int LOADS = kTileKeys * UK / THREADS;  // 16-byte pieces per thread per tile
   static_assert(LOADS * THREADS == kTileKeys * UK, "whole tiles per load round");
+  static_assert(RPW >= 2, "the epilogue of one row runs beside the next row's matrix-core steps");
   __shared__ __attribute__((aligned(16))) u32x4 kt[4][kTileKeys * UK];  // ring of four 8 KB tiles
   const int kc = blockIdx.x % P.nkc;
   const int rest = blockIdx.x / P.nkc;
@@ -257,17 +259,17 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scores_qb_kernel(QbParams
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, g = lane >> 5;
 
-  // this wavefront's two query rows: fragments, weights, positions
+  // this wavefront's RPW query rows: fragments, weights, positions
   // Scores go out through buffer stores whose range is the row's keys [0, p]: lanes past p (and
   // every lane of a step past the end) store out of range, which the hardware drops.  The store
   // is therefore unconditional, so the compiler's wait counts stay exact (a store behind a branch
   // makes it wait for the prefetch issued after it).
-  bf16x8 qa[2][NC];
-  float wr[2][16];
-  __amdgpu_buffer_rsrc_t rs[2];
+  bf16x8 qa[RPW][NC];
+  float wr[RPW][16];
+  __amdgpu_buffer_rsrc_t rs[RPW];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int i = qb * ROWS + 2 * wave + q;
+  for (int q = 0; q < RPW; ++q) {
+    const int i = qb * ROWS + RPW * wave + q;
     const bool ok = i < Lq;
     const size_t row = static_cast<size_t>(b) * Lq + min(i, Lq - 1);
     const int pq = ok ? min(sl - Lq + i, S_max - 1) : -1;  // keys s <= pq are scored
@@ -340,13 +342,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scores_qb_kernel(QbParams
   //   - reads tile t+1's fragments from LDS into registers (written one step earlier),
   //   - loads tile t+3 from memory into registers,
   //   - runs row 0's 8 dependent matrix-core steps on tile t, each followed by two elements of
-  //     row 1's epilogue of tile t-1; then row 1's steps on tile t next to row 0's epilogue of
-  //     tile t (one step behind, so its accumulator is complete),
+  //     the last row's epilogue of tile t-1; then row r's steps (r >= 1) next to row r-1's
+  //     epilogue of tile t, one step behind, so that accumulator is complete,
   //   - writes tile t+2 (loaded two steps earlier) into its slot, then a barrier.
   // After the barrier the matrix cores start at once on fragments already in registers.  The
   // instruction order is fixed with scheduling barriers.  Four steps per iteration give every
   // register and slot a fixed role; steps past the end compute on clamped keys and store nothing.
-  f32x16 acc0, acc1 = f32x16{};
+  f32x16 acc[RPW];
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) acc[q] = f32x16{};
   bf16x8 kx[NC], ky[NC];
   Piece rx = gload(start), ry = gload(start + kTileKeys);
   lstore(0, rx);  // tile 0
@@ -357,28 +361,33 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scores_qb_kernel(QbParams
   auto step = [&](int t, int slot, const bf16x8 (&kc)[NC], bf16x8 (&kn)[NC], Piece& rl, Piece& rn) {
     kread(slot, kn);
     rn = gload(start + (t + 3) * kTileKeys);
-    float p1 = 0.0f;
+    {
+      float p = 0.0f;  // last row, tile t-1
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      acc0 = mfma32(qa[0][c], kc[c], c == 0 ? f32x16{} : acc0);
-      p1 += relu_w(1, 2 * c, acc1[2 * c]);
-      p1 += relu_w(1, 2 * c + 1, acc1[2 * c + 1]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    store_row(1, t - 1, p1);
-    float p0 = 0.0f;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      acc1 = mfma32(qa[1][c], kc[c], c == 0 ? f32x16{} : acc1);
-      if (c > 0) {
-        p0 += relu_w(0, 2 * c - 2, acc0[2 * c - 2]);
-        p0 += relu_w(0, 2 * c - 1, acc0[2 * c - 1]);
+      for (int c = 0; c < NC; ++c) {
+        acc[0] = mfma32(qa[0][c], kc[c], c == 0 ? f32x16{} : acc[0]);
+        p += relu_w(RPW - 1, 2 * c, acc[RPW - 1][2 * c]);
+        p += relu_w(RPW - 1, 2 * c + 1, acc[RPW - 1][2 * c + 1]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      store_row(RPW - 1, t - 1, p);
     }
-    p0 += relu_w(0, 14, acc0[14]);
-    p0 += relu_w(0, 15, acc0[15]);
-    store_row(0, t, p0);
+#pragma unroll
+    for (int q = 1; q < RPW; ++q) {
+      float p = 0.0f;  // row q - 1, tile t
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        acc[q] = mfma32(qa[q][c], kc[c], c == 0 ? f32x16{} : acc[q]);
+        if (c > 0) {
+          p += relu_w(q - 1, 2 * c - 2, acc[q - 1][2 * c - 2]);
+          p += relu_w(q - 1, 2 * c - 1, acc[q - 1][2 * c - 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      p += relu_w(q - 1, 14, acc[q - 1][14]);
+      p += relu_w(q - 1, 15, acc[q - 1][15]);
+      store_row(q - 1, t, p);
+    }
     lstore(slot == 3 ? 0 : slot + 1, rl);
     barrier();
   };
@@ -390,11 +399,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scores_qb_kernel(QbParams
   }
 }
 
-template <int WAVES>
+template <int WAVES, int RPW>
 hipError_t launch_qb(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
                      const int32_t* seqlens, int B, int Lq, int Hi, int S_max, float* scores,
                      hipStream_t stream) {
-  constexpr int ROWS = 2 * WAVES;
+  constexpr int ROWS = RPW * WAVES;
   QbParams Q{};
   Q.q_idx = q_idx;
   Q.w = w;
@@ -410,7 +419,7 @@ hipError_t launch_qb(const uint16_t* q_idx, const float* w, const uint16_t* k_id
   Q.scores = scores;
   const long grid = static_cast<long>(B) * Q.nqb * Q.nkc;
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(index_scores_qb_kernel<WAVES>, dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((index_scores_qb_kernel<WAVES, RPW>), dim3(static_cast<unsigned>(grid)),
                      dim3(64 * WAVES), 0, stream, Q);
   return hipGetLastError();
 }
@@ -479,7 +488,7 @@ hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint
                                float* scores, hipStream_t stream) {
   const long rows = static_cast<long>(B) * Lq;
   if (Di == 128 && Lq >= kQbMinRows)  // prefill: query-blocked scan
-    return launch_qb<kQbWaves>(q_idx, w, k_idx, seqlens, B, Lq, Hi, S_max, scores, stream);
+    return launch_qb<kQbWaves, kQbRowsPerWave>(q_idx, w, k_idx, seqlens, B, Lq, Hi, S_max, scores, stream);
   IndexParams P{};
   P.q_idx = q_idx;
   P.w = w;
