@@ -13,6 +13,11 @@ batch; inputs are generated in HBM before timing.  Prints ONE JSON line.
 (lsa_index_topk: the scores never leave the chip); --path split (the default for prefill
 workloads, where the query-blocked scan is the faster indexer) runs lsa_index_scores then
 lsa_topk_select.  Both give the same indices bit for bit.
+
+Passes: (1) the headline, K steps between two events; (2) the same K steps with an event at
+every call boundary (per-call durations, roofline, spread); (3) up to 50 steps each preceded by a
+1 GiB read that evicts the caches (cold-cache figure, and the read's rate as context).  The CPU-oracle leg also re-checks parity on the sampled rows of the timed
+run's output buffers.
 """
 from __future__ import annotations
 
@@ -95,8 +100,11 @@ def fused_call_bytes(wl):
     return tot
 
 
-def cpu_baseline(wl, sample_rows):
-    """Time the CPU oracle (as it stands) on a bounded sample of the same workload."""
+def cpu_baseline(wl, sample_rows, gpu=None):
+    """Time the CPU oracle (as it stands) on a bounded sample of the same workload.  With `gpu`
+    (host copies of the timed run's indices, n_sel and attention outputs) also re-check parity
+    on the sampled rows: indices bit for bit, attention within max|err| <= 1e-2 max|ref| and
+    relative L2 <= 5e-3."""
     import numpy as np
 
     import oracle
@@ -118,6 +126,7 @@ def cpu_baseline(wl, sample_rows):
                          [host_slice(wl, f"q{c}", b)[i][None, None] for c in range(wl.mla_calls)]))
     cores = oracle.max_threads()
     t_total = 0.0
+    checked, idx_equal, worst_max, worst_l2 = set(), True, 0.0, 0.0
     for b, i, p, qi, w, k, qs in prepared:
         n = p + 1
         sl = np.array([n], np.int32)
@@ -129,14 +138,31 @@ def cpu_baseline(wl, sample_rows):
         m = sel.size
         kvs = [host_kv_rows(wl, f"kv{c}", b, sel)[None] for c in range(wl.mla_calls)]
         t0 = time.perf_counter()
-        for c in range(wl.mla_calls):
-            oracle.sparse_mla(qs[c], kvs[c], np.arange(m, dtype=np.int32)[None, None],
-                              np.array([[m]], np.int32), np.array([m], np.int32), wl.Dv, wl.scale)
+        refs = [oracle.sparse_mla(qs[c], kvs[c], np.arange(m, dtype=np.int32)[None, None],
+                                  np.array([[m]], np.int32), np.array([m], np.int32), wl.Dv,
+                                  wl.scale)[0] for c in range(wl.mla_calls)]
         t_total += time.perf_counter() - t0
-    return {"value": len(rows) / t_total, "unit": "queries/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(rows)} query-row evaluations over the {len(every)} query rows of "
-                      f"{wl.name} (each: full indexer scan, top-k and {wl.mla_calls} MLA call(s)); "
-                      f"{t_total:.2f} s wall on {cores} threads"}
+        if gpu is not None and (b, i) not in checked:  # not timed
+            checked.add((b, i))
+            g_idx, g_nsel, g_outs = gpu
+            idx_equal &= bool(int(g_nsel[b, i]) == int(nsel[0, 0])
+                              and np.array_equal(g_idx[b, i].cpu().numpy(), idx[0, 0]))
+            for c in range(wl.mla_calls):
+                ref = refs[c][0, 0]
+                err = g_outs[c][b, i].float().cpu().numpy().astype(np.float64) - ref
+                worst_max = max(worst_max, float(np.abs(err).max() / max(np.abs(ref).max(), 1e-300)))
+                worst_l2 = max(worst_l2, float(np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-300)))
+    res = {"value": len(rows) / t_total, "unit": "queries/s", "cores": cores, "kind": "oracle",
+           "sample": f"{len(rows)} query-row evaluations over the {len(every)} query rows of "
+                     f"{wl.name} (each: full indexer scan, top-k and {wl.mla_calls} MLA call(s)); "
+                     f"{t_total:.2f} s wall on {cores} threads"}
+    if gpu is not None:
+        res["parity_on_timed_buffers"] = {
+            "rows": len(checked), "indices_bit_exact": idx_equal,
+            "attention_max_err_over_max_ref": float(f"{worst_max:.3e}"),
+            "attention_rel_l2": float(f"{worst_l2:.3e}"),
+            "pass": bool(idx_equal and worst_max <= 1e-2 and worst_l2 <= 5e-3)}
+    return res
 
 
 def main():
@@ -267,6 +293,27 @@ def main():
                     "traffic": load_traffic(wl.name, args.path), "avg_launch_ms": round(k1_ms, 5),
                     "alg_bytes_per_launch": k1_bytes}
 
+    # Pass 3 (cold cache): each step preceded by a 1 GiB read (torch's sum reduction) that evicts
+    # the L2 and the Infinity Cache with clean lines (a written flush would leave 1 GiB of dirty
+    # lines for the next key stream to write back), events around each step (so each figure also
+    # carries an event's queue bubble, as in pass 2).  The read's own rate is reported as
+    # context; torch's reduction is not a tuned streaming kernel.
+    flush = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    n_cold = min(args.steps, 50)
+    cold_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_cold)]
+    torch.cuda.synchronize()
+    for ev in cold_ev:
+        ev[0].record(stream)
+        torch.sum(flush, dim=0, out=sink)
+        ev[1].record(stream)
+        step()
+        ev[2].record(stream)
+    torch.cuda.synchronize()
+    cold_ms = sorted(ev[1].elapsed_time(ev[2]) for ev in cold_ev)
+    read_ms = sorted(ev[0].elapsed_time(ev[1]) for ev in cold_ev)
+    del flush
+
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
@@ -305,6 +352,9 @@ def main():
     stages["one_mla_step_ms"] = round(mean(0) + mean(1) + mean(2), 5)
     # spread of step times in pass 2 (which carries the boundary events)
     stages["instrumented_step_ms_p10_p50_p90"] = [pct(0.1), pct(0.5), pct(0.9)]
+    stages["cold_cache_step_ms_p10_p50_p90"] = [round(cold_ms[int(q * (n_cold - 1))], 5)
+                                                 for q in (0.1, 0.5, 0.9)]
+    stages["flush_torch_sum_1gib_gbs"] = round((1 << 30) / (read_ms[n_cold // 2] / 1e3) / 1e9, 1)
 
     line = {
         "metric": METRIC,
@@ -336,7 +386,7 @@ def main():
         # about 10 s of oracle work: three passes over the 32 decode rows of the 128K step
         sample = args.cpu_sample or (3 * B * Lq if wl.decode and B * Lq <= 64 else 64)
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(wl, sample)
+        line["cpu_baseline"] = cpu_baseline(wl, sample, gpu=(idx, nsel, outs))
     print(json.dumps(line), flush=True)
     return 0
 
