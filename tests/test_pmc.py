@@ -1,0 +1,88 @@
+"""Host logic of the counter summaries (no GPU): the copy-calibrated HBM traffic that bench.py
+reports as roofline.traffic, its staleness rule, and the matrix-core utilisation table."""
+import csv
+import json
+
+import pytest
+
+from long_context_sparse_lightning_amd import pmc, pmc_mfma
+
+FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp",
+          "End_Timestamp"]
+
+
+def _write_csv(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for d, (name, counter, value, t0, t1) in enumerate(rows, 1):
+            w.writerow({"Dispatch_Id": d, "Kernel_Name": name, "Counter_Name": counter,
+                        "Counter_Value": value, "Start_Timestamp": t0, "End_Timestamp": t1})
+
+
+K1 = "void lsa::(anonymous namespace)::index_scores_kernel<128, true>(lsa::(anonymous namespace)::IndexParams)"
+MERGE = "lsa::(anonymous namespace)::topk_merge_kernel(lsa::(anonymous namespace)::TopkParams)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def test_traffic_is_calibrated_by_the_copy_and_goes_stale_with_the_sources(tmp_path, monkeypatch):
+    monkeypatch.setattr(pmc, "ROOT", str(tmp_path))
+    # counters in KiB; FETCH_SIZE reads half the true bytes of the 64 MiB copy, WRITE_SIZE all
+    fetch = [(K1, "FETCH_SIZE", 1000.0, 0, 1), (MERGE, "FETCH_SIZE", 40.0, 1, 2),
+             (K1, "FETCH_SIZE", 1200.0, 2, 3), (MERGE, "FETCH_SIZE", 60.0, 3, 4),
+             (COPY, "FETCH_SIZE", 32 * 1024.0, 4, 5)]
+    write = [(K1, "WRITE_SIZE", 10.0, 0, 1), (MERGE, "WRITE_SIZE", 2.0, 1, 2),
+             (K1, "WRITE_SIZE", 14.0, 2, 3), (MERGE, "WRITE_SIZE", 4.0, 3, 4),
+             (COPY, "WRITE_SIZE", 64 * 1024.0, 4, 5)]
+    _write_csv(tmp_path / "f.csv", fetch)
+    _write_csv(tmp_path / "w.csv", write)
+    rec = pmc.summarize(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 64, "unit_wl", "fused",
+                        4_000_000, "cmd f", "cmd w")
+    # per call: mean K1 + mean merge, scaled by the copy's raw/true ratio
+    fetch_bytes = (1100.0 + 50.0) * 1024 / 0.5
+    write_bytes = (12.0 + 3.0) * 1024 / 1.0
+    assert rec["counters"]["FETCH_SIZE"]["factor"] == pytest.approx(0.5)
+    assert rec["counters"]["WRITE_SIZE"]["factor"] == pytest.approx(1.0)
+    assert rec["traffic_bytes_per_launch"] == round(fetch_bytes + write_bytes)
+    assert rec["counters"]["FETCH_SIZE"]["dispatches"] == 2
+    # bench.py reads it back while the kernel sources hash the same ...
+    assert pmc.load_traffic("unit_wl", "fused") == round(fetch_bytes + write_bytes)
+    on_disk = json.load(open(pmc.traffic_path("unit_wl", "fused")))
+    assert on_disk["commands"] == ["cmd f", "cmd w"]
+    assert (tmp_path / "profiles" / "index_topk_unit_wl_traffic.md").exists()
+    # ... and not once they differ from the recorded hash
+    monkeypatch.setattr(pmc, "sources_sha256", lambda path: "0" * 64)
+    assert pmc.load_traffic("unit_wl", "fused") is None
+
+
+def test_traffic_without_a_calibration_copy_is_refused(tmp_path, monkeypatch):
+    monkeypatch.setattr(pmc, "ROOT", str(tmp_path))
+    _write_csv(tmp_path / "f.csv", [(K1, "FETCH_SIZE", 1.0, 0, 1), (MERGE, "FETCH_SIZE", 1.0, 1, 2)])
+    _write_csv(tmp_path / "w.csv", [(K1, "WRITE_SIZE", 1.0, 0, 1), (MERGE, "WRITE_SIZE", 1.0, 1, 2)])
+    with pytest.raises(SystemExit):
+        pmc.summarize(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 64, "unit_wl", "fused", 1,
+                      "f", "w")
+
+
+def test_mfma_table(tmp_path, monkeypatch):
+    monkeypatch.setattr(pmc_mfma, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    qb = "void lsa::(anonymous namespace)::index_scores_qb_kernel<8, 2>(lsa::(anonymous namespace)::QbParams)"
+    mla = "void lsa::(anonymous namespace)::sparse_mla_kernel<576, 512, true>(lsa::(anonymous namespace)::MlaParams)"
+    rows = []
+    # two dispatches of each kernel, each with both counters (one row per counter)
+    for d, (name, util, mops, t0, t1) in enumerate([(qb, 60.0, 1000.0, 0, 3000), (qb, 64.0, 1000.0, 5000, 9000),
+                                                    (mla, 20.0, 10.0, 9000, 10000), (mla, 22.0, 30.0, 10000, 12000)], 1):
+        rows.append({"Dispatch_Id": d, "Kernel_Name": name, "Counter_Name": "MfmaUtil",
+                     "Counter_Value": util, "Start_Timestamp": t0, "End_Timestamp": t1})
+        rows.append({"Dispatch_Id": d, "Kernel_Name": name, "Counter_Name": "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                     "Counter_Value": mops, "Start_Timestamp": t0, "End_Timestamp": t1})
+    with open(tmp_path / "m.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        w.writerows(rows)
+    out = pmc_mfma.summarize(str(tmp_path / "m.csv"), "unit_wl", "the command")
+    text = open(out).read()
+    assert "    the command" in text
+    assert "| index_scores_qb_kernel<8, 2> | 2 | 62.0 | 5.12e+05 | 3.5 |" in text
+    assert "| sparse_mla_kernel<576, 512, true> | 2 | 21.0 | 1.024e+04 | 1.5 |" in text
