@@ -46,6 +46,9 @@ def lib():
         L.lsa_oracle_sparse_mla.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, ctypes.c_double,
                                             P, P]
         L.lsa_oracle_sparse_mla.restype = I
+        L.lsa_oracle_index_frontend.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I,
+                                                ctypes.c_double, ctypes.c_double, P, P, P]
+        L.lsa_oracle_index_frontend.restype = I
         L.lsa_oracle_set_threads.argtypes = [I]
         L.lsa_oracle_max_threads.restype = I
         _lib = L
@@ -121,3 +124,33 @@ def sparse_mla(q, kv, indices, n_sel, seqlens, Dv: int, scale: float):
     if rc != 0:
         raise ValueError(f"lsa_oracle_sparse_mla: bad input ({rc})")
     return out, lse
+
+
+def index_frontend(cq, hid, wq_b, wk, gain, w_proj, seqlens, Hi: int, Di: int, rope_dim: int,
+                   theta: float, eps: float):
+    """cq bf16 bits [B,Lq,q_lora]; hid bf16 bits [B,Lq,hidden]; wq_b bf16 bits [Hi*Di,q_lora];
+    wk bf16 bits [Di,hidden]; gain f32 [Di]; w_proj bf16 bits [Hi,hidden] ->
+    (q f64 [B,Lq,Hi,Di], w f64 [B,Lq,Hi], k f64 [B,Lq,Di]): the index query, head weights and
+    the key written at each token's position."""
+    cq = _c(cq, np.uint16)
+    hid = _c(hid, np.uint16)
+    wq_b = _c(wq_b, np.uint16)
+    wk = _c(wk, np.uint16)
+    gain = _c(gain, np.float32)
+    w_proj = _c(w_proj, np.uint16)
+    seqlens = _c(seqlens, np.int32)
+    B, Lq, q_lora = cq.shape
+    hidden = hid.shape[2]
+    assert hid.shape[:2] == (B, Lq) and wq_b.shape == (Hi * Di, q_lora)
+    assert wk.shape == (Di, hidden) and gain.shape == (Di,) and w_proj.shape == (Hi, hidden)
+    q = np.empty((B, Lq, Hi, Di), dtype=np.float64)
+    w = np.empty((B, Lq, Hi), dtype=np.float64)
+    k = np.empty((B, Lq, Di), dtype=np.float64)
+    rc = lib().lsa_oracle_index_frontend(cq.ctypes.data, hid.ctypes.data, wq_b.ctypes.data,
+                                         wk.ctypes.data, gain.ctypes.data, w_proj.ctypes.data,
+                                         seqlens.ctypes.data, B, Lq, q_lora, hidden, Hi, Di,
+                                         rope_dim, float(theta), float(eps), q.ctypes.data,
+                                         w.ctypes.data, k.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"lsa_oracle_index_frontend: bad input ({rc})")
+    return q, w, k

@@ -27,7 +27,12 @@
  *  - scores are rounded once to fp32, and the selection ranks the fp32 values;
  *  - a latent row is [latent (Dv values) | rope]; the value vector is its first Dv entries.
  *
- * Parity pins (tests/test_oracle.py): exact integer brute force of the scores, NumPy lexsort
+ * The indexer front end (lsa_oracle_index_frontend, at the end of this file) follows page 1's
+ * "LSA" description of wq_b, wk with RMS normalisation and weights_proj, with the attention's
+ * rotary settings; its readings are listed with the function.
+ *
+ * Parity pins (tests/test_oracle.py, tests/test_oracle_frontend.py): exact integer brute force of
+ * the scores and of the front-end projections, closed-form norms and rotations, NumPy lexsort
  * brute force of the selection, a hand-worked selection fixture (tests/golden), dense masked
  * softmax in NumPy float64, closed-form special cases and invariants.
  */
@@ -248,4 +253,84 @@ int lsa_oracle_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* 
   if (bad & 1) return -1;
   if (bad & 2) return -3;
   return 0;
+}
+
+/*
+ * Indexer front end (page 1, "LSA": the index query is the q-LoRA representation projected by
+ * wq_b to index_n_heads x index_head_dim; the index key is the hidden state projected by wk and
+ * RMS-normalised; weights_proj gives one weight per index head; index queries and keys use the
+ * attention's rotary settings, qk_rope_head_dim and rope_theta from "架构总览").  Per token
+ * (b, i) at position p = seqlens[b] - Lq + i, in fp64:
+ *   q[h][d] = sum_j cq[j] * wq_b[h*Di + d][j]
+ *   k[d]    = g[d] * x[d] / sqrt(mean_e x[e]^2 + eps),  x[d] = sum_j hid[j] * wk[d][j]
+ *   w[h]    = sum_j hid[j] * w_proj[h][j]
+ * then the rotary embedding on the last R dims of every q head and of k: pair (2m, 2m+1) of
+ * that part turns by the angle p * theta^(-2m/R):
+ *   (u, v) -> (u cos a - v sin a, u sin a + v cos a).
+ * Readings: the rotated part is the last R dims (the latent rows put rope last), pairs are
+ * adjacent, RMSNorm carries a per-dim gain and eps, no extra scale on w.
+ * cq: bf16 [B, Lq, q_lora]; hid: bf16 [B, Lq, hidden]; wq_b: bf16 [Hi*Di, q_lora];
+ * wk: bf16 [Di, hidden]; gain: fp32 [Di]; w_proj: bf16 [Hi, hidden]; outputs fp64:
+ * q_out [B, Lq, Hi, Di], w_out [B, Lq, Hi], k_out [B, Lq, Di].
+ * Returns 0, -1 on a negative position, -2 on a bad rotary size.
+ */
+static void rotate_tail(double* v, int Di, int R, long p, double theta) {
+  for (int m = 0; m < R / 2; ++m) {
+    double a = (double)p * pow(theta, -2.0 * m / R);
+    double c = cos(a), s = sin(a);
+    double* u = v + (Di - R) + 2 * m;
+    double x = u[0], y = u[1];
+    u[0] = x * c - y * s;
+    u[1] = x * s + y * c;
+  }
+}
+
+int lsa_oracle_index_frontend(const uint16_t* cq, const uint16_t* hid, const uint16_t* wq_b,
+                              const uint16_t* wk, const float* gain, const uint16_t* w_proj,
+                              const int32_t* seqlens, int B, int Lq, int q_lora, int hidden,
+                              int Hi, int Di, int R, double theta, double eps, double* q_out,
+                              double* w_out, double* k_out) {
+  if (R < 0 || R > Di || (R & 1)) return -2;
+  int bad = 0;
+  long rows = (long)B * Lq;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (long r = 0; r < rows; ++r) {
+    int b = (int)(r / Lq), i = (int)(r % Lq);
+    long p = query_position(seqlens[b], Lq, i);
+    if (p < 0) {
+      bad |= 1;
+      continue;
+    }
+    const uint16_t* c = cq + r * (long)q_lora;
+    const uint16_t* x = hid + r * (long)hidden;
+    for (int h = 0; h < Hi; ++h) {
+      double* qh = q_out + (r * Hi + h) * (long)Di;
+      for (int d = 0; d < Di; ++d) {
+        const uint16_t* wrow = wq_b + ((long)h * Di + d) * q_lora;
+        double s = 0.0;
+        for (int j = 0; j < q_lora; ++j) s += bf16_value(c[j]) * bf16_value(wrow[j]);
+        qh[d] = s;
+      }
+      rotate_tail(qh, Di, R, p, theta);
+    }
+    double* kr = k_out + r * (long)Di;
+    double ms = 0.0;
+    for (int d = 0; d < Di; ++d) {
+      const uint16_t* wrow = wk + (long)d * hidden;
+      double s = 0.0;
+      for (int j = 0; j < hidden; ++j) s += bf16_value(x[j]) * bf16_value(wrow[j]);
+      kr[d] = s;
+      ms += s * s;
+    }
+    double inv = 1.0 / sqrt(ms / Di + eps);
+    for (int d = 0; d < Di; ++d) kr[d] = (double)gain[d] * (kr[d] * inv);
+    rotate_tail(kr, Di, R, p, theta);
+    for (int h = 0; h < Hi; ++h) {
+      const uint16_t* wrow = w_proj + (long)h * hidden;
+      double s = 0.0;
+      for (int j = 0; j < hidden; ++j) s += bf16_value(x[j]) * bf16_value(wrow[j]);
+      w_out[r * Hi + h] = s;
+    }
+  }
+  return (bad & 1) ? -1 : 0;
 }
