@@ -173,6 +173,43 @@ lsa_status lsa_sparse_mla_prefill(const void* q, const void* kv, const int32_t* 
                                   float softmax_scale, void* out, float* lse, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* Workspace (bytes) lsa_index_frontend needs for these sizes (0 for invalid sizes). */
+size_t lsa_index_frontend_workspace_bytes(int B, int Lq, int q_lora, int hidden, int Hi, int Di);
+
+/*
+ * Indexer front end: the indexer inputs of the current tokens ("LSA" section: wq_b projects the
+ * q-LoRA representation to index_n_heads x index_head_dim, wk projects the hidden state to the
+ * index key, which is RMS-normalised, weights_proj gives one weight per index head; index queries
+ * and keys take the attention's rotary settings, qk_rope_head_dim and rope_theta, "架构总览").
+ * For token i of sequence b at position p = seqlens[b] - Lq + i:
+ *   q_idx[b,i,h,:] = rot_p(cq[b,i,:] . wq_b[h*Di:(h+1)*Di, :]^T)
+ *   w[b,i,h]       = hid[b,i,:] . w_proj[h, :]^T
+ *   k_cache[b,p,:] = rot_p(gain * x / sqrt(mean(x^2) + norm_eps)),  x = hid[b,i,:] . wk^T
+ * where rot_p turns pair (2m, 2m+1) of the last rope_dim entries by the angle
+ * p * rope_theta^(-2m/rope_dim): (u, v) -> (u cos - v sin, u sin + v cos).  Which entries rotate
+ * and how they pair is not given by the pages (the last rope_dim, adjacent pairs, is this
+ * library's reading).  Products are bf16 x bf16 with fp32 accumulation; the norm and the rotation
+ * run in fp32 (angles in fp64); q_idx and the key are rounded once to bf16, w stays fp32.
+ *   cq      bf16 [B, Lq, q_lora]          q-LoRA representation
+ *   hid     bf16 [B, Lq, hidden]          hidden state
+ *   wq_b    bf16 [Hi*Di, q_lora]          (rows = outputs, as a linear layer's weight)
+ *   wk      bf16 [Di, hidden]
+ *   k_norm_gain fp32 [Di]
+ *   w_proj  bf16 [Hi, hidden]
+ *   q_idx   bf16 [B, Lq, Hi, Di]  output;  w fp32 [B, Lq, Hi]  output
+ *   k_cache bf16 [B, S_max, Di]   row p of each current token is written, nothing else
+ *   workspace device buffer of at least lsa_index_frontend_workspace_bytes(...) bytes
+ * Supported: q_lora and hidden multiples of 16, Di even <= 128, Hi <= 32, rope_dim even <= Di,
+ * rope_theta > 0, norm_eps >= 0 (else LSA_ERR_BAD_SHAPE / LSA_ERR_UNSUPPORTED).  Caller
+ * precondition (device-side): 0 <= p < S_max; a token outside writes no cache row.
+ */
+lsa_status lsa_index_frontend(const void* cq, const void* hid, const void* wq_b, const void* wk,
+                              const float* k_norm_gain, const void* w_proj, const int32_t* seqlens,
+                              int B, int Lq, int q_lora, int hidden, int Hi, int Di, int rope_dim,
+                              float rope_theta, float norm_eps, int S_max, void* q_idx, float* w,
+                              void* k_cache, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -201,4 +201,56 @@ lsa_status lsa_sparse_mla_prefill(const void* q, const void* kv, const int32_t* 
                  S_max, topk, softmax_scale, out, lse, workspace, workspace_bytes, stream);
 }
 
+static lsa_status check_frontend(int B, int Lq, int q_lora, int hidden, int Hi, int Di,
+                                 int rope_dim, int S_max) {
+  const char* fn = "lsa_index_frontend";
+  if (B < 0 || Lq < 0) return fail(LSA_ERR_BAD_SHAPE, "%s: B=%d Lq=%d must be >= 0", fn, B, Lq);
+  if (q_lora <= 0 || hidden <= 0 || Hi <= 0 || Di <= 0 || S_max <= 0)
+    return fail(LSA_ERR_BAD_SHAPE, "%s: q_lora=%d hidden=%d Hi=%d Di=%d S_max=%d must be > 0", fn,
+                q_lora, hidden, Hi, Di, S_max);
+  if (rope_dim < 0 || rope_dim > Di || (rope_dim & 1) || (Di & 1))
+    return fail(LSA_ERR_BAD_SHAPE, "%s: rope_dim=%d must be even and in [0, Di=%d], Di even", fn,
+                rope_dim, Di);
+  if (q_lora % 16 || hidden % 16)
+    return fail(LSA_ERR_UNSUPPORTED, "%s: q_lora=%d and hidden=%d must be multiples of 16", fn,
+                q_lora, hidden);
+  if (Di > 128 || Hi > 32) return fail(LSA_ERR_UNSUPPORTED, "%s: Di=%d > 128 or Hi=%d > 32", fn, Di, Hi);
+  if (rope_dim > lsa::frontend_max_rot())
+    return fail(LSA_ERR_UNSUPPORTED, "%s: rope_dim=%d > %d", fn, rope_dim, lsa::frontend_max_rot());
+  return LSA_OK;
+}
+
+size_t lsa_index_frontend_workspace_bytes(int B, int Lq, int q_lora, int hidden, int Hi, int Di) {
+  if (check_frontend(B, Lq, q_lora, hidden, Hi, Di, 0, 1) != LSA_OK) return 0;
+  return lsa::frontend_workspace_bytes(B, Lq, q_lora, hidden, Hi, Di);
+}
+
+lsa_status lsa_index_frontend(const void* cq, const void* hid, const void* wq_b, const void* wk,
+                              const float* k_norm_gain, const void* w_proj, const int32_t* seqlens,
+                              int B, int Lq, int q_lora, int hidden, int Hi, int Di, int rope_dim,
+                              float rope_theta, float norm_eps, int S_max, void* q_idx, float* w,
+                              void* k_cache, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  const char* fn = "lsa_index_frontend";
+  lsa_status st = check_frontend(B, Lq, q_lora, hidden, Hi, Di, rope_dim, S_max);
+  if (st != LSA_OK) return st;
+  if (!(rope_theta > 0.0f) || rope_theta == INFINITY || !(norm_eps >= 0.0f) || norm_eps == INFINITY)
+    return fail(LSA_ERR_BAD_SHAPE, "%s: rope_theta=%g must be finite > 0, norm_eps=%g finite >= 0",
+                fn, rope_theta, norm_eps);
+  if (B == 0 || Lq == 0) return ok();
+  if (!cq || !hid || !wq_b || !wk || !k_norm_gain || !w_proj || !seqlens || !q_idx || !w || !k_cache)
+    return fail(LSA_ERR_NULL_ARG, "%s: NULL input or output", fn);
+  const size_t need = lsa::frontend_workspace_bytes(B, Lq, q_lora, hidden, Hi, Di);
+  if (!workspace || workspace_bytes < need)
+    return fail(LSA_ERR_WORKSPACE, "%s: workspace %zu bytes at %p, need %zu", fn, workspace_bytes,
+                workspace, need);
+  return launched(lsa::launch_frontend(static_cast<const uint16_t*>(cq), static_cast<const uint16_t*>(hid),
+                                       static_cast<const uint16_t*>(wq_b), static_cast<const uint16_t*>(wk),
+                                       k_norm_gain, static_cast<const uint16_t*>(w_proj), seqlens, B, Lq,
+                                       q_lora, hidden, Hi, Di, rope_dim, rope_theta, norm_eps, S_max,
+                                       static_cast<uint16_t*>(q_idx), w, static_cast<uint16_t*>(k_cache),
+                                       workspace, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
 }  // extern "C"

@@ -161,4 +161,14 @@ hipError_t launch_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indi
                       int Dv, int S_max, int topk, float softmax_scale, uint16_t* out, float* lse,
                       void* workspace, hipStream_t stream);
 
+// Indexer front end: index queries, head weights and the new keys of the current tokens.
+int frontend_max_rot();
+size_t frontend_workspace_bytes(int B, int Lq, int q_lora, int hidden, int Hi, int Di);
+hipError_t launch_frontend(const uint16_t* cq, const uint16_t* hid, const uint16_t* wq_b,
+                           const uint16_t* wk, const float* gain, const uint16_t* w_proj,
+                           const int32_t* seqlens, int B, int Lq, int q_lora, int hidden, int Hi,
+                           int Di, int rope_dim, double theta, float eps, int S_max,
+                           uint16_t* q_idx, float* w, uint16_t* k_cache, void* workspace,
+                           hipStream_t stream);
+
 }  // namespace lsa

@@ -21,7 +21,8 @@ STATUS = {0: "LSA_OK", 1: "LSA_ERR_NULL_ARG", 2: "LSA_ERR_BAD_SHAPE", 3: "LSA_ER
 
 EXPORTED = ["lsa_status_str", "lsa_last_error", "lsa_index_scores", "lsa_topk_workspace_bytes",
             "lsa_topk_select", "lsa_index_topk_workspace_bytes", "lsa_index_topk",
-            "lsa_mla_workspace_bytes", "lsa_sparse_mla_decode", "lsa_sparse_mla_prefill"]
+            "lsa_mla_workspace_bytes", "lsa_sparse_mla_decode", "lsa_sparse_mla_prefill",
+            "lsa_index_frontend_workspace_bytes", "lsa_index_frontend"]
 
 
 class LsaError(RuntimeError):
@@ -62,6 +63,11 @@ def lib():
         L.lsa_sparse_mla_decode.restype = I
         L.lsa_sparse_mla_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, P, Z, P]
         L.lsa_sparse_mla_prefill.restype = I
+        L.lsa_index_frontend_workspace_bytes.argtypes = [I, I, I, I, I, I]
+        L.lsa_index_frontend_workspace_bytes.restype = Z
+        L.lsa_index_frontend.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, F, I, P, P, P,
+                                         P, Z, P]
+        L.lsa_index_frontend.restype = I
         _lib = L
     return _lib
 
@@ -217,3 +223,46 @@ def lsa_sparse_mla_prefill(q, kv, indices, n_sel, seqlens, Dv, softmax_scale, ou
     """q bf16 [B,Lq,H,Dqk], kv bf16 [B,S_max,Dqk], indices i32 [B,Lq,topk] (or None: dense
     causal), n_sel i32 [B,Lq] -> out bf16 [B,Lq,H,Dv] (lse f32 [B,Lq,H] written if given)."""
     return _mla(False, q, kv, indices, n_sel, seqlens, Dv, softmax_scale, out, lse, workspace)
+
+
+def lsa_index_frontend_workspace_bytes(B, Lq, q_lora, hidden, Hi, Di) -> int:
+    return int(lib().lsa_index_frontend_workspace_bytes(B, Lq, q_lora, hidden, Hi, Di))
+
+
+def lsa_index_frontend(cq, hid, wq_b, wk, k_norm_gain, w_proj, seqlens, k_cache, rope_dim=64,
+                       rope_theta=1e6, norm_eps=1e-6, q_idx=None, w=None, workspace=None):
+    """cq bf16 [B,Lq,q_lora], hid bf16 [B,Lq,hidden], wq_b bf16 [Hi*Di,q_lora], wk bf16
+    [Di,hidden], k_norm_gain f32 [Di], w_proj bf16 [Hi,hidden], seqlens i32 [B], k_cache bf16
+    [B,S_max,Di] (row p of each current token is written) -> (q_idx bf16 [B,Lq,Hi,Di], w f32
+    [B,Lq,Hi])."""
+    _want(cq, "cq", torch.bfloat16, 3)
+    _want(hid, "hid", torch.bfloat16, 3)
+    _want(wq_b, "wq_b", torch.bfloat16, 2)
+    _want(wk, "wk", torch.bfloat16, 2)
+    _want(k_norm_gain, "k_norm_gain", torch.float32, 1)
+    _want(w_proj, "w_proj", torch.bfloat16, 2)
+    _want(seqlens, "seqlens", torch.int32, 1)
+    _want(k_cache, "k_cache", torch.bfloat16, 3)
+    B, Lq, q_lora = cq.shape
+    hidden = hid.shape[2]
+    Di = wk.shape[0]
+    Hi = w_proj.shape[0]
+    S_max = k_cache.shape[1]
+    if hid.shape[:2] != (B, Lq) or wq_b.shape != (Hi * Di, q_lora) or wk.shape[1] != hidden \
+            or w_proj.shape[1] != hidden or k_norm_gain.shape[0] != Di \
+            or k_cache.shape[0] != B or k_cache.shape[2] != Di or seqlens.shape[0] != B:
+        raise ValueError("lsa_index_frontend: inconsistent shapes")
+    dev = cq.device
+    if q_idx is None:
+        q_idx = torch.empty(B, Lq, Hi, Di, dtype=torch.bfloat16, device=dev)
+    if w is None:
+        w = torch.empty(B, Lq, Hi, dtype=torch.float32, device=dev)
+    need = lsa_index_frontend_workspace_bytes(B, Lq, q_lora, hidden, Hi, Di)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().lsa_index_frontend(_ptr(cq), _ptr(hid), _ptr(wq_b), _ptr(wk), _ptr(k_norm_gain),
+                                    _ptr(w_proj), _ptr(seqlens), B, Lq, q_lora, hidden, Hi, Di,
+                                    rope_dim, rope_theta, norm_eps, S_max, _ptr(q_idx), _ptr(w),
+                                    _ptr(k_cache), _ptr(workspace), wbytes, _stream(cq)))
+    return q_idx, w

@@ -54,6 +54,18 @@ int main() {
   CHECK(lsa_sparse_mla_decode(p, p, ip, ip, ip, 4, 32, 576, 512, 1000, 64, std::nanf(""), p, nullptr, p, size_t(1) << 30, nullptr) == LSA_ERR_BAD_SHAPE);
   CHECK(lsa_sparse_mla_decode(p, p, ip, ip, ip, 32, 32, 576, 512, 131072, 2048, 0.07f, p, nullptr, nullptr, 0, nullptr) == LSA_ERR_WORKSPACE && has_error());
   CHECK(lsa_sparse_mla_prefill(p, p, nullptr, nullptr, ip, 0, 10, 32, 576, 512, 100, 0, 0.1f, nullptr, nullptr, nullptr, 0, nullptr) == LSA_OK);
+  // indexer front end: sizes, rotary and norm parameters, NULLs, workspace, empty batch
+  const size_t feneed = lsa_index_frontend_workspace_bytes(32, 1, 1536, 3072, 32, 128);
+  CHECK(feneed > 0 && lsa_index_frontend_workspace_bytes(32, 1, 1530, 3072, 32, 128) == 0);
+  CHECK(lsa_index_frontend(p, p, p, p, fp, p, ip, 2, 1, 1536, 3072, 32, 128, 63, 1e6f, 1e-6f, 100, p, fp, p, p, size_t(1) << 30, nullptr) == LSA_ERR_BAD_SHAPE && has_error());
+  CHECK(lsa_index_frontend(p, p, p, p, fp, p, ip, 2, 1, 1536, 3072, 32, 128, 130, 1e6f, 1e-6f, 100, p, fp, p, p, size_t(1) << 30, nullptr) == LSA_ERR_BAD_SHAPE);
+  CHECK(lsa_index_frontend(p, p, p, p, fp, p, ip, 2, 1, 1530, 3072, 32, 128, 64, 1e6f, 1e-6f, 100, p, fp, p, p, size_t(1) << 30, nullptr) == LSA_ERR_UNSUPPORTED);
+  CHECK(lsa_index_frontend(p, p, p, p, fp, p, ip, 2, 1, 1536, 3072, 32, 256, 64, 1e6f, 1e-6f, 100, p, fp, p, p, size_t(1) << 30, nullptr) == LSA_ERR_UNSUPPORTED);
+  CHECK(lsa_index_frontend(p, p, p, p, fp, p, ip, 2, 1, 1536, 3072, 32, 128, 64, 0.0f, 1e-6f, 100, p, fp, p, p, size_t(1) << 30, nullptr) == LSA_ERR_BAD_SHAPE);
+  CHECK(lsa_index_frontend(p, p, p, p, fp, p, ip, 2, 1, 1536, 3072, 32, 128, 64, 1e6f, -1.0f, 100, p, fp, p, p, size_t(1) << 30, nullptr) == LSA_ERR_BAD_SHAPE);
+  CHECK(lsa_index_frontend(p, p, p, p, nullptr, p, ip, 2, 1, 1536, 3072, 32, 128, 64, 1e6f, 1e-6f, 100, p, fp, p, p, size_t(1) << 30, nullptr) == LSA_ERR_NULL_ARG);
+  CHECK(lsa_index_frontend(p, p, p, p, fp, p, ip, 32, 1, 1536, 3072, 32, 128, 64, 1e6f, 1e-6f, 100, p, fp, p, p, feneed - 1, nullptr) == LSA_ERR_WORKSPACE && has_error());
+  CHECK(lsa_index_frontend(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 1, 1536, 3072, 32, 128, 64, 1e6f, 1e-6f, 100, nullptr, nullptr, nullptr, nullptr, 0, nullptr) == LSA_OK && !has_error());
   std::puts("abi driver: ok");
   return 0;
 }

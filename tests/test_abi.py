@@ -112,6 +112,31 @@ def test_mla_argument_errors_and_workspace():
     assert L.lsa_mla_workspace_bytes(1, 4096, 32, 512, 131072, 2048, 0) == 0
 
 
+def test_index_frontend_argument_errors_and_workspace():
+    L = lsa.lib()
+    p = ctypes.c_void_p(16)
+    fe = L.lsa_index_frontend
+
+    def call(B=2, Lq=1, ql=1536, hd=3072, Hi=32, Di=128, R=64, theta=1e6, eps=1e-6, gain=p,
+             ws=p, wbytes=1 << 30):
+        return fe(p, p, p, p, gain, p, p, B, Lq, ql, hd, Hi, Di, R, theta, eps, 100, p, p, p, ws,
+                  wbytes, None)
+
+    assert call(R=63) == 2 and call(R=130) == 2 and call(Di=127, R=64) == 2
+    assert call(ql=1530) == 3 and call(Di=256, R=64) == 3 and call(Hi=33) == 3
+    assert call(theta=0.0) == 2 and call(theta=float("inf")) == 2 and call(eps=-1.0) == 2
+    assert call(eps=float("nan")) == 2
+    assert call(gain=None) == 1
+    need = L.lsa_index_frontend_workspace_bytes(32, 1, 1536, 3072, 32, 128)
+    assert 0 < need < 64 << 20
+    assert call(B=32, wbytes=need - 1) == 4 and call(B=32, ws=None, wbytes=0) == 4
+    assert fe(None, None, None, None, None, None, None, 0, 1, 1536, 3072, 32, 128, 64, 1e6, 1e-6,
+              100, None, None, None, None, 0, None) == 0
+    assert L.lsa_index_frontend_workspace_bytes(32, 1, 1530, 3072, 32, 128) == 0
+    # prefill-sized calls stay modest: one reduction split at 4096 tokens
+    assert L.lsa_index_frontend_workspace_bytes(1, 4096, 1536, 3072, 32, 128) <= 96 << 20
+
+
 @pytest.mark.parametrize("name", ["tiny_decode", "decode_32k", "decode_128k", "prefill_128k",
                                   "decode_1m"])
 def test_workspace_sizes_are_modest(name):

@@ -8,6 +8,8 @@ import subprocess
 
 import pytest
 
+from long_context_sparse_lightning_amd import build
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HERE = os.path.join(ROOT, "tests", "sanitize")
 CSRC = os.path.join(ROOT, "long_context_sparse_lightning_amd", "csrc")
@@ -39,7 +41,7 @@ def test_c_abi_host_side_under_asan_and_ubsan(tmp_path):
     flags = ["--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", "-Xclang", "-target-feature",
              "-Xclang", "-packed-fp32-ops", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}"] + san
     objs = []
-    for src in ("lsa_api.hip", "lsa_indexer.hip", "lsa_topk.hip", "lsa_mla.hip"):
+    for src in build.LSA_SOURCES:
         obj = str(tmp_path / src.replace(".hip", ".o"))
         _run([HIPCC] + flags + ["-c", os.path.join(CSRC, src), "-o", obj], timeout=600)
         objs.append(obj)
