@@ -16,7 +16,8 @@ lsa_topk_select.  Both give the same indices bit for bit.
 
 Passes: (1) the headline, K steps between two events; (2) the same K steps with an event at
 every call boundary (per-call durations, roofline, spread); (3) up to 50 steps each preceded by a
-1 GiB read that evicts the caches (cold-cache figure, and the read's rate as context).  The CPU-oracle leg also re-checks parity on the sampled rows of the timed
+1 GiB read that evicts the caches (cold-cache figure, and the read's rate as context); (4) the
+indexer front end (lsa_index_frontend) at the same shape, reported under `stages` only.  The CPU-oracle leg also re-checks parity on the sampled rows of the timed
 run's output buffers.
 """
 from __future__ import annotations
@@ -98,6 +99,56 @@ def fused_call_bytes(wl):
             n = wl.seqlens[b] - wl.Lq + i + 1
             tot += n * wl.Di * 2 + wl.Hi * wl.Di * 2 + wl.Hi * 4 + wl.topk * 4 + 4
     return tot
+
+
+FE_Q_LORA, FE_HIDDEN, FE_ROPE = 1536, 3072, 64  # q_lora_rank, hidden_size, qk_rope_head_dim
+
+
+def frontend_cost(wl):
+    """Algorithmic bytes and flops of one lsa_index_frontend call at the workload's shape: the
+    three weight matrices, the token activations, the outputs (q_idx, w, the new keys)."""
+    T = wl.B * wl.Lq
+    wbytes = (wl.Hi * wl.Di * FE_Q_LORA + (wl.Di + wl.Hi) * FE_HIDDEN) * 2
+    act = T * (FE_Q_LORA + FE_HIDDEN) * 2
+    out = T * (wl.Hi * wl.Di * 2 + wl.Hi * 4 + wl.Di * 2)
+    flops = 2 * T * (wl.Hi * wl.Di * FE_Q_LORA + (wl.Di + wl.Hi) * FE_HIDDEN)
+    return wbytes + act + out, flops
+
+
+def time_frontend(wl, dev, stream, calls=20):
+    """Average duration (ms) of lsa_index_frontend at the workload's shape, on its own cache."""
+    import torch
+
+    from long_context_sparse_lightning_amd import inputs as gen
+    from long_context_sparse_lightning_amd import lsa
+
+    T = (wl.B, wl.Lq)
+    t = lambda name, shape, kind: gen.device_tensor(wl.seed, gen.TAGS[name], shape, kind, device=dev)
+    cq, hid = t("cq", T + (FE_Q_LORA,), gen.NORMAL), t("hid", T + (FE_HIDDEN,), gen.NORMAL)
+    wq_b = t("wq_b", (wl.Hi * wl.Di, FE_Q_LORA), gen.NORMAL)
+    wk, w_proj = t("wk", (wl.Di, FE_HIDDEN), gen.NORMAL), t("w_proj", (wl.Hi, FE_HIDDEN), gen.NORMAL)
+    gain = t("k_gain", (wl.Di,), gen.WEIGHT)
+    seqlens = torch.tensor(wl.seqlens, dtype=torch.int32, device=dev)
+    cache = torch.empty(wl.B, wl.S_max, wl.Di, dtype=torch.bfloat16, device=dev)
+    q = torch.empty(wl.B, wl.Lq, wl.Hi, wl.Di, dtype=torch.bfloat16, device=dev)
+    w = torch.empty(wl.B, wl.Lq, wl.Hi, dtype=torch.float32, device=dev)
+    ws = torch.empty(lsa.lsa_index_frontend_workspace_bytes(wl.B, wl.Lq, FE_Q_LORA, FE_HIDDEN, wl.Hi,
+                                                            wl.Di), dtype=torch.uint8, device=dev)
+
+    def call():
+        lsa.lsa_index_frontend(cq, hid, wq_b, wk, gain, w_proj, seqlens, cache, rope_dim=FE_ROPE,
+                               q_idx=q, w=w, workspace=ws)
+
+    for _ in range(3):
+        call()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(calls):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / calls
 
 
 def cpu_baseline(wl, sample_rows, gpu=None):
@@ -314,6 +365,10 @@ def main():
     read_ms = sorted(ev[0].elapsed_time(ev[1]) for ev in cold_ev)
     del flush
 
+    # Pass 4: the indexer front end (the next row after the hot path; not part of the headline
+    # step) at the same shape, back to back
+    fe_ms = time_frontend(wl, dev, stream)
+
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
@@ -354,6 +409,13 @@ def main():
     stages["instrumented_step_ms_p10_p50_p90"] = [pct(0.1), pct(0.5), pct(0.9)]
     stages["cold_cache_step_ms_p10_p50_p90"] = [round(cold_ms[int(q * (n_cold - 1))], 5)
                                                  for q in (0.1, 0.5, 0.9)]
+    fe_bytes, fe_flops = frontend_cost(wl)
+    stages["frontend_call_ms"] = round(fe_ms, 5)
+    stages["frontend_alg_bytes"] = fe_bytes
+    if wl.decode:
+        stages["frontend_gbs"] = round(fe_bytes / (fe_ms / 1e3) / 1e9, 1)
+    else:
+        stages["frontend_tflops"] = round(fe_flops / (fe_ms / 1e3) / 1e12, 1)
     stages["flush_torch_sum_1gib_gbs"] = round((1 << 30) / (read_ms[n_cold // 2] / 1e3) / 1e9, 1)
 
     line = {

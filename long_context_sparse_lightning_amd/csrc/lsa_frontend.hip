@@ -27,10 +27,9 @@
 namespace lsa {
 namespace {
 
-constexpr int kProjThreads = 256;  // 4 wavefronts x 32 outputs
-constexpr int kTileT = 32;         // tokens per workgroup
-constexpr int kTileN = 128;        // outputs per workgroup
+constexpr int kProjThreads = 256;  // 4 wavefronts
 constexpr int kTargetGroups = 512; // two workgroups per CU
+constexpr int kMinChunk = 256;     // reduction entries per split (16 matrix-core steps)
 constexpr int kFinThreads = 256;
 constexpr int kMaxRot = 128;       // rotated dims the finalize kernel holds angles for
 
@@ -42,41 +41,78 @@ struct ProjParams {
   float* out;          // [splits, T, N]
 };
 
+// A wavefront computes TM x TN blocks of 32 tokens x 32 outputs (each loaded fragment feeds TN
+// or TM matrix-core steps); the four wavefronts of a workgroup sit side by side along the
+// outputs, so they share the token rows through the cache.  Workgroup tile: 32*TM tokens x
+// 128*TN outputs.
+template <int TM, int TN>
 __global__ __launch_bounds__(kProjThreads) void frontend_proj_kernel(ProjParams P) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, g = lane >> 5;
-  const int t0 = blockIdx.y * kTileT;
-  const int n = blockIdx.x * kTileN + wave * 32 + col;  // this lane's weight row (B column)
+  const int t0 = blockIdx.y * 32 * TM;
+  const int n0 = (blockIdx.x * 4 + wave) * 32 * TN;
   const int s = blockIdx.z;
   const int k0 = s * P.kchunk, k1 = min(P.K, k0 + P.kchunk);
   // rows past the end re-read the last row (their results are not stored)
-  const uint16_t* arow = P.A + static_cast<size_t>(min(t0 + col, P.T - 1)) * P.K + 8 * g;
-  const int nc = min(n, P.N - 1);
-  const uint16_t* wrow = (nc < P.n_split ? P.W0 + static_cast<size_t>(nc) * P.K
-                                         : P.W1 + static_cast<size_t>(nc - P.n_split) * P.K) + 8 * g;
-  f32x16 acc = {};
-  constexpr int U = 4;  // 16-wide steps whose loads are issued together
+  const uint16_t* arow[TM];
+  const uint16_t* wrow[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+    arow[i] = P.A + static_cast<size_t>(min(t0 + 32 * i + col, P.T - 1)) * P.K + 8 * g;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int nc = min(n0 + 32 * j + col, P.N - 1);
+    wrow[j] = (nc < P.n_split ? P.W0 + static_cast<size_t>(nc) * P.K
+                              : P.W1 + static_cast<size_t>(nc - P.n_split) * P.K) + 8 * g;
+  }
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+  constexpr int U = 4 / (TM * TN > 2 ? 2 : 1);  // 16-wide steps whose loads are issued together
   int k = k0;
   for (; k + 16 * U <= k1; k += 16 * U) {
-    bf16x8 a[U], b[U];
+    bf16x8 a[U][TM], b[U][TN];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      a[u] = load_bf16x8(arow + k + 16 * u);
-      b[u] = load_bf16x8(wrow + k + 16 * u);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) a[u][i] = load_bf16x8(arow[i] + k + 16 * u);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) b[u][j] = load_bf16x8(wrow[j] + k + 16 * u);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) acc = mfma32(a[u], b[u], acc);
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(a[u][i], b[u][j], acc[i][j]);
   }
-  for (; k < k1; k += 16) acc = mfma32(load_bf16x8(arow + k), load_bf16x8(wrow + k), acc);
-  // lane (col, g) holds outputs n for tokens t0 + acc_row(r, g)
-  if (n < P.N) {
-    float* o = P.out + static_cast<size_t>(s) * P.T * P.N + n;
+  for (; k < k1; k += 16) {  // K is a multiple of 16
+    bf16x8 a[TM], b[TN];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = t0 + acc_row(r, g);
-      if (t < P.T) o[static_cast<size_t>(t) * P.N] = acc[r];
-    }
+    for (int i = 0; i < TM; ++i) a[i] = load_bf16x8(arow[i] + k);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[j] = load_bf16x8(wrow[j] + k);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+  }
+  // lane (col, g) of block (i, j) holds output n0 + 32j + col for tokens t0 + 32i + acc_row(r, g)
+  float* o = P.out + static_cast<size_t>(s) * P.T * P.N;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int n = n0 + 32 * j + col;
+    if (n >= P.N) continue;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = t0 + 32 * i + acc_row(r, g);
+        if (t < P.T) o[static_cast<size_t>(t) * P.N + n] = acc[i][j][r];
+      }
   }
 }
 
@@ -138,10 +174,11 @@ __global__ __launch_bounds__(kFinThreads) void frontend_finalize_kernel(FinParam
   const int Nq = P.Hi * Di;
   for (int e = 2 * tid; e < Nq; e += 2 * kFinThreads) {
     float u = 0.0f, v = 0.0f;
+#pragma unroll 4
     for (int s = 0; s < P.sq; ++s) {
-      const float* src = P.qp + (static_cast<size_t>(s) * T + t) * Nq + e;
-      u += src[0];
-      v += src[1];
+      const float2 x = *reinterpret_cast<const float2*>(P.qp + (static_cast<size_t>(s) * T + t) * Nq + e);
+      u += x.x;
+      v += x.y;
     }
     rotate(e % Di, u, v);
     store_pair(P.q_idx + static_cast<size_t>(t) * Nq + e, u, v);
@@ -158,12 +195,14 @@ __global__ __launch_bounds__(kFinThreads) void frontend_finalize_kernel(FinParam
     const int d = 2 * tid;
     const bool mine = d < Di;
     float u = 0.0f, v = 0.0f;
-    if (mine)
+    if (mine) {
+#pragma unroll 4
       for (int s = 0; s < P.skw; ++s) {
         const float* src = P.kp + (static_cast<size_t>(s) * T + t) * Nkw + d;
         u += src[0];
         v += src[1];
       }
+    }
     const float ss = wave_sum_f(u * u + v * v);
     const float inv = 1.0f / sqrtf(ss / static_cast<float>(Di) + P.eps);
     if (mine) {
@@ -176,19 +215,26 @@ __global__ __launch_bounds__(kFinThreads) void frontend_finalize_kernel(FinParam
   }
 }
 
+// Workgroup tile: 32 tokens x 128 outputs for few tokens (decode), 64 x 256 from 64 tokens on.
+bool big_tiles(long T) { return T >= 64; }
+long tile_t(long T) { return big_tiles(T) ? 64 : 32; }
+long tile_n(long T) { return big_tiles(T) ? 256 : 128; }
+
 struct Split {
-  int splits = 1, kchunk = 16;
+  int splits = 1, kchunk = 64;
 };
 
+// Reduction split: enough workgroups to fill the CUs, but at least kMinChunk entries each; the
+// chunk is a multiple of 64 (so the kernel's unrolled steps cover every chunk but the last).
 Split plan_split(long T, long N, int K) {
   Split sp;
-  const long tiles = ((T + kTileT - 1) / kTileT) * ((N + kTileN - 1) / kTileN);
+  const long tiles = ((T + tile_t(T) - 1) / tile_t(T)) * ((N + tile_n(T) - 1) / tile_n(T));
   long s = tiles > 0 ? (kTargetGroups + tiles - 1) / tiles : 1;
-  s = std::max<long>(1, std::min<long>(s, K / 16));
+  s = std::max<long>(1, std::min<long>(s, K / kMinChunk));
   long chunk = (K + s - 1) / s;
-  chunk = (chunk + 15) / 16 * 16;
-  sp.kchunk = static_cast<int>(chunk);
-  sp.splits = static_cast<int>((K + chunk - 1) / chunk);
+  chunk = (chunk + 63) / 64 * 64;
+  sp.kchunk = static_cast<int>(std::min<long>(chunk, K));
+  sp.splits = static_cast<int>((K + sp.kchunk - 1) / sp.kchunk);
   return sp;
 }
 
@@ -220,23 +266,23 @@ hipError_t launch_frontend(const uint16_t* cq, const uint16_t* hid, const uint16
   char* ws = align_workspace(workspace);
   float* qp = reinterpret_cast<float*>(ws);
   float* kp = reinterpret_cast<float*>(ws + align_up(static_cast<size_t>(sq.splits) * T * Nq * sizeof(float)));
-  const long ty = (T + kTileT - 1) / kTileT;
+  const long ty = (T + tile_t(T) - 1) / tile_t(T);
   if (ty > 65535 || T > 0x7fffffffL) return hipErrorInvalidConfiguration;
-
+  auto proj = [&](const ProjParams& pp, long N, int splits) {
+    const dim3 grid(static_cast<unsigned>((N + tile_n(T) - 1) / tile_n(T)), static_cast<unsigned>(ty),
+                    static_cast<unsigned>(splits));
+    if (big_tiles(T))
+      hipLaunchKernelGGL((frontend_proj_kernel<2, 2>), grid, dim3(kProjThreads), 0, stream, pp);
+    else
+      hipLaunchKernelGGL((frontend_proj_kernel<1, 1>), grid, dim3(kProjThreads), 0, stream, pp);
+    return hipGetLastError();
+  };
   ProjParams pq{cq, wq_b, wq_b, static_cast<int>(Nq), static_cast<int>(T), static_cast<int>(Nq),
                 q_lora, sq.kchunk, qp};
-  hipLaunchKernelGGL(frontend_proj_kernel,
-                     dim3(static_cast<unsigned>((Nq + kTileN - 1) / kTileN), static_cast<unsigned>(ty),
-                          static_cast<unsigned>(sq.splits)),
-                     dim3(kProjThreads), 0, stream, pq);
-  hipError_t err = hipGetLastError();
+  hipError_t err = proj(pq, Nq, sq.splits);
   if (err != hipSuccess) return err;
   ProjParams pk{hid, wk, w_proj, Di, static_cast<int>(T), static_cast<int>(Nkw), hidden, skw.kchunk, kp};
-  hipLaunchKernelGGL(frontend_proj_kernel,
-                     dim3(static_cast<unsigned>((Nkw + kTileN - 1) / kTileN), static_cast<unsigned>(ty),
-                          static_cast<unsigned>(skw.splits)),
-                     dim3(kProjThreads), 0, stream, pk);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if ((err = proj(pk, Nkw, skw.splits)) != hipSuccess) return err;
   FinParams pf{qp, kp, sq.splits, skw.splits, gain, seqlens, Lq, Hi, Di, rope_dim, S_max, theta, eps,
                q_idx, w, k_cache};
   hipLaunchKernelGGL(frontend_finalize_kernel, dim3(static_cast<unsigned>(T)), dim3(kFinThreads), 0,
