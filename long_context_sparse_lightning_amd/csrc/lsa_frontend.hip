@@ -116,6 +116,116 @@ __global__ __launch_bounds__(kProjThreads) void frontend_proj_kernel(ProjParams 
   }
 }
 
+// Many tokens (prefill): a workgroup computes 128 tokens x 128 outputs, staging 32-wide steps of
+// both operands in LDS (double-buffered) so each fragment read feeds two matrix-core steps; the
+// next step's global loads are in flight during the current step's matrix-core work.  Wavefront
+// w computes rows 64*(w/2) .. +63 and outputs 64*(w%2) .. +63 as 2 x 2 blocks of 32 x 32.  LDS
+// rows are padded to 80 bytes, so the 16 lanes of each fragment-read phase hit distinct banks.
+// Requires K (and so every chunk) to be a multiple of 64.
+constexpr int kLdsTile = 128;  // tokens and outputs per workgroup
+constexpr int kLdsRow = 40;    // bf16 per LDS row: 32 plus 8 of padding
+
+__global__ __launch_bounds__(kProjThreads, 2) void frontend_proj_lds_kernel(ProjParams P) {
+  __shared__ __attribute__((aligned(16))) uint16_t as[2][kLdsTile * kLdsRow];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[2][kLdsTile * kLdsRow];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, g = lane >> 5;
+  const int t0 = blockIdx.y * kLdsTile, n0 = blockIdx.x * kLdsTile;
+  const int s = blockIdx.z;
+  const int k0 = s * P.kchunk, k1 = min(P.K, k0 + P.kchunk);
+  // global -> LDS: 16-byte piece u = tid + 256 j (j < 2) of a 128 x 32 tile is row u / 4, part u % 4
+  const uint16_t* asrc[2];
+  const uint16_t* wsrc[2];
+  int loff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int u = tid + kProjThreads * j, row = u >> 2, part = u & 3;
+    asrc[j] = P.A + static_cast<size_t>(min(t0 + row, P.T - 1)) * P.K + 8 * part;
+    const int nc = min(n0 + row, P.N - 1);
+    wsrc[j] = (nc < P.n_split ? P.W0 + static_cast<size_t>(nc) * P.K
+                              : P.W1 + static_cast<size_t>(nc - P.n_split) * P.K) + 8 * part;
+    loff[j] = row * kLdsRow + 8 * part;
+  }
+  // two register sets of global loads: the step two ahead is requested while this one computes
+  struct Set {
+    u32x4 a[2], w[2];
+  };
+  auto gload = [&](Set& x, int k) {  // k past the chunk re-reads its last step (no branch)
+    k = min(k, k1 - 32);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      x.a[j] = *reinterpret_cast<const u32x4*>(asrc[j] + k);
+      x.w[j] = *reinterpret_cast<const u32x4*>(wsrc[j] + k);
+    }
+  };
+  auto lstore = [&](int buf, const Set& x) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      *reinterpret_cast<u32x4*>(&as[buf][loff[j]]) = x.a[j];
+      *reinterpret_cast<u32x4*>(&ws[buf][loff[j]]) = x.w[j];
+    }
+  };
+  const int wr = 64 * (wave >> 1), wc = 64 * (wave & 1);
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  auto compute = [&](int buf) {
+    bf16x8 fa[2][2], fw[2][2];  // [block][k half]
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        fa[i][h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                  &as[buf][(wr + 32 * i + col) * kLdsRow + 16 * h + 8 * g]));
+        fw[i][h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                  &ws[buf][(wc + 32 * i + col) * kLdsRow + 16 * h + 8 * g]));
+      }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[i][h], fw[j][h], acc[i][j]);
+  };
+  Set x0, x1;
+  gload(x0, k0);
+  gload(x1, k0 + 32);
+  lstore(0, x0);  // waits for x0 only: x1 was requested after it
+  __syncthreads();
+  // steps k (LDS buffer 0) and k + 32 (buffer 1) per iteration, so every register set and buffer
+  // has a fixed role and the loop has no exit in the middle (every chunk is a multiple of 64);
+  // each buffer was last read before the barrier that precedes its store, and the last
+  // iteration's stores (clamped re-reads) are never computed
+  for (int k = k0; k < k1; k += 64) {
+    gload(x0, k + 64);
+    __builtin_amdgcn_sched_barrier(0);  // keep the request ahead of this step's work
+    compute(0);
+    lstore(1, x1);
+    __syncthreads();
+    gload(x1, k + 96);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1);
+    lstore(0, x0);
+    __syncthreads();
+  }
+  float* o = P.out + static_cast<size_t>(s) * P.T * P.N;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wc + 32 * j + col;
+    if (n >= P.N) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = t0 + wr + 32 * i + acc_row(r, g);
+        if (t < P.T) o[static_cast<size_t>(t) * P.N + n] = acc[i][j][r];
+      }
+  }
+}
+
 struct FinParams {
   const float* qp;  // [sq, T, Hi*Di] partials of the index query
   const float* kp;  // [skw, T, Di + Hi] partials of the raw key and the head weights
@@ -215,10 +325,12 @@ __global__ __launch_bounds__(kFinThreads) void frontend_finalize_kernel(FinParam
   }
 }
 
-// Workgroup tile: 32 tokens x 128 outputs for few tokens (decode), 64 x 256 from 64 tokens on.
+// Workgroup tile: 32 tokens x 128 outputs for few tokens (decode), 64 x 256 from 64 tokens on,
+// 128 x 128 through LDS from 128 tokens on when K is a multiple of 64.
+bool lds_tiles(long T, int K) { return T >= 128 && K % 64 == 0; }
 bool big_tiles(long T) { return T >= 64; }
-long tile_t(long T) { return big_tiles(T) ? 64 : 32; }
-long tile_n(long T) { return big_tiles(T) ? 256 : 128; }
+long tile_t(long T, int K) { return lds_tiles(T, K) ? kLdsTile : big_tiles(T) ? 64 : 32; }
+long tile_n(long T, int K) { return lds_tiles(T, K) ? kLdsTile : big_tiles(T) ? 256 : 128; }
 
 struct Split {
   int splits = 1, kchunk = 64;
@@ -228,7 +340,7 @@ struct Split {
 // chunk is a multiple of 64 (so the kernel's unrolled steps cover every chunk but the last).
 Split plan_split(long T, long N, int K) {
   Split sp;
-  const long tiles = ((T + tile_t(T) - 1) / tile_t(T)) * ((N + tile_n(T) - 1) / tile_n(T));
+  const long tiles = ((T + tile_t(T, K) - 1) / tile_t(T, K)) * ((N + tile_n(T, K) - 1) / tile_n(T, K));
   long s = tiles > 0 ? (kTargetGroups + tiles - 1) / tiles : 1;
   s = std::max<long>(1, std::min<long>(s, K / kMinChunk));
   long chunk = (K + s - 1) / s;
@@ -266,12 +378,15 @@ hipError_t launch_frontend(const uint16_t* cq, const uint16_t* hid, const uint16
   char* ws = align_workspace(workspace);
   float* qp = reinterpret_cast<float*>(ws);
   float* kp = reinterpret_cast<float*>(ws + align_up(static_cast<size_t>(sq.splits) * T * Nq * sizeof(float)));
-  const long ty = (T + tile_t(T) - 1) / tile_t(T);
-  if (ty > 65535 || T > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  if ((T + 31) / 32 > 65535 || T > 0x7fffffffL) return hipErrorInvalidConfiguration;
   auto proj = [&](const ProjParams& pp, long N, int splits) {
-    const dim3 grid(static_cast<unsigned>((N + tile_n(T) - 1) / tile_n(T)), static_cast<unsigned>(ty),
+    const int K = pp.K;
+    const dim3 grid(static_cast<unsigned>((N + tile_n(T, K) - 1) / tile_n(T, K)),
+                    static_cast<unsigned>((T + tile_t(T, K) - 1) / tile_t(T, K)),
                     static_cast<unsigned>(splits));
-    if (big_tiles(T))
+    if (lds_tiles(T, K))
+      hipLaunchKernelGGL(frontend_proj_lds_kernel, grid, dim3(kProjThreads), 0, stream, pp);
+    else if (big_tiles(T))
       hipLaunchKernelGGL((frontend_proj_kernel<2, 2>), grid, dim3(kProjThreads), 0, stream, pp);
     else
       hipLaunchKernelGGL((frontend_proj_kernel<1, 1>), grid, dim3(kProjThreads), 0, stream, pp);
