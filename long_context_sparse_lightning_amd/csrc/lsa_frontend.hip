@@ -16,11 +16,15 @@
 //    weights are stored [outputs, inputs] (as a linear layer's), so a lane's 16-byte operand
 //    pieces of both A (a token row) and B (a weight row) are contiguous.  The reduction is split
 //    over enough workgroups to fill the CUs when there are few tokens; fp32 partial sums go to
-//    the workspace.
-//  * frontend_finalize_kernel: one workgroup per token adds the partials in a fixed order and
-//    applies the rotation (angles in fp64, once per token), the key's RMS normalisation (one
-//    wavefront) and the roundings; the key is written to its cache row.
+//    the workspace.  frontend_proj_lds_kernel stages 128 x 128 tiles through LDS for many tokens.
+//  * frontend_finalize_kernel: per token, adds the partials in a fixed order and applies the
+//    rotation (angles in fp64), the key's RMS normalisation (one wavefront) and the roundings;
+//    the key is written to its cache row.
+//  * With many tokens the index query needs no reduction split: its projection then runs last,
+//    rotating and rounding in its epilogue from an angle table the finalize kernel writes, so
+//    the query never makes an fp32 round trip through HBM.
 #include <algorithm>
+#include <cmath>
 
 #include "lsa_internal.h"
 
@@ -32,14 +36,23 @@ constexpr int kTargetGroups = 512; // two workgroups per CU
 constexpr int kMinChunk = 256;     // reduction entries per split (16 matrix-core steps)
 constexpr int kFinThreads = 256;
 constexpr int kMaxRot = 128;       // rotated dims the finalize kernel holds angles for
+constexpr int kFinBatch = 8;       // partial sums a finalize thread has in flight
 
 struct ProjParams {
   const uint16_t* A;   // [T, K]
   const uint16_t* W0;  // rows [0, n_split) of the weights, [n_split, K]
   const uint16_t* W1;  // rows [n_split, N), [N - n_split, K]
   int n_split, T, N, K, kchunk;
-  float* out;          // [splits, T, N]
+  float* out;          // [splits, T, N] fp32 partial sums (unrotated kernels)
+  // rotated bf16 output (frontend_proj_lds_kernel<true>): the index query of one split
+  const float2* table; // [T, R/2] (cos, sin) of each token's rotation angles
+  int Di, R;
+  uint16_t* q_out;     // [T, N]
 };
+
+__device__ __forceinline__ uint16_t bf16_of(float x) {  // round to nearest even
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
 
 // A wavefront computes TM x TN blocks of 32 tokens x 32 outputs (each loaded fragment feeds TN
 // or TM matrix-core steps); the four wavefronts of a workgroup sit side by side along the
@@ -116,15 +129,61 @@ __global__ __launch_bounds__(kProjThreads) void frontend_proj_kernel(ProjParams 
   }
 }
 
+// Epilogue of the unsplit index query: a wavefront's 2 x 2 blocks of 32 tokens x 32 outputs
+// (tokens from t0, outputs from n0) are rotated and written as bf16.  Output n = n0 + 32j + col
+// has the parity of col (n0 is a multiple of 32), so lanes col and col ^ 1 hold the two halves
+// of a pair; the even lane stores both.
+__device__ __forceinline__ void rotate_store(const ProjParams& P, const f32x16 (&acc)[2][2], int t0,
+                                             int n0, int col, int g) {
+  const int half = P.R / 2, rot0 = P.Di - P.R;
+  const bool even = (col & 1) == 0;
+  auto partner = [](float x) {  // value of lane ^ 1 (quad_perm [1,0,3,2])
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));
+  };
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + 32 * j + col;
+    const int d = min(n, P.N - 1) % P.Di;
+    const bool rot = d >= rot0;
+    const bool any_rot = __ballot(rot) != 0;  // wavefront-uniform (false when R = 0)
+    const float2* tab = P.table + (rot ? (d - rot0) >> 1 : 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      // the 16 tokens' angles of this block, requested together
+      float2 cs[16];
+      if (any_rot) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          cs[r] = tab[static_cast<size_t>(min(t0 + 32 * i + acc_row(r, g), P.T - 1)) * half];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = t0 + 32 * i + acc_row(r, g);
+        const float own = acc[i][j][r], other = partner(own);
+        float out = own;
+        if (any_rot && rot)  // pair (x, y) -> (x c - y s, x s + y c)
+          out = even ? own * cs[r].x - other * cs[r].y : other * cs[r].y + own * cs[r].x;
+        const float hi = partner(out);
+        if (even && n < P.N && t < P.T)
+          *reinterpret_cast<uint32_t*>(P.q_out + static_cast<size_t>(t) * P.N + n) =
+              static_cast<uint32_t>(bf16_of(out)) | (static_cast<uint32_t>(bf16_of(hi)) << 16);
+      }
+    }
+  }
+}
+
 // Many tokens (prefill): a workgroup computes 128 tokens x 128 outputs, staging 32-wide steps of
 // both operands in LDS (double-buffered) so each fragment read feeds two matrix-core steps; the
 // next step's global loads are in flight during the current step's matrix-core work.  Wavefront
 // w computes rows 64*(w/2) .. +63 and outputs 64*(w%2) .. +63 as 2 x 2 blocks of 32 x 32.  LDS
 // rows are padded to 80 bytes, so the 16 lanes of each fragment-read phase hit distinct banks.
-// Requires K (and so every chunk) to be a multiple of 64.
+// Requires K (and so every chunk) to be a multiple of 64.  With ROT (the index query without a
+// reduction split) the epilogue applies the rotation and writes bf16 directly: the two outputs
+// of a pair sit in adjacent lanes, exchanged with one DPP swap.
 constexpr int kLdsTile = 128;  // tokens and outputs per workgroup
 constexpr int kLdsRow = 40;    // bf16 per LDS row: 32 plus 8 of padding
 
+template <bool ROT>
 __global__ __launch_bounds__(kProjThreads, 2) void frontend_proj_lds_kernel(ProjParams P) {
   __shared__ __attribute__((aligned(16))) uint16_t as[2][kLdsTile * kLdsRow];
   __shared__ __attribute__((aligned(16))) uint16_t ws[2][kLdsTile * kLdsRow];
@@ -211,6 +270,10 @@ __global__ __launch_bounds__(kProjThreads, 2) void frontend_proj_lds_kernel(Proj
     lstore(0, x0);
     __syncthreads();
   }
+  if constexpr (ROT) {
+    rotate_store(P, acc, t0 + wr, n0 + wc, col, g);
+    return;
+  }
   float* o = P.out + static_cast<size_t>(s) * P.T * P.N;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -227,22 +290,19 @@ __global__ __launch_bounds__(kProjThreads, 2) void frontend_proj_lds_kernel(Proj
 }
 
 struct FinParams {
-  const float* qp;  // [sq, T, Hi*Di] partials of the index query
+  const float* qp;  // [sq, T, Hi*Di] partials of the index query (null: written by the projection)
   const float* kp;  // [skw, T, Di + Hi] partials of the raw key and the head weights
   int sq, skw;
   const float* gain;
   const int32_t* seqlens;
   int Lq, Hi, Di, R, S_max;
-  double theta;
   float eps;
   uint16_t* q_idx;  // [T, Hi, Di]
   float* w;         // [T, Hi]
   uint16_t* k_cache;  // [B, S_max, Di]
+  float2* table;    // [T, R/2] (cos, sin) for the rotated projection epilogue, or null
+  double inv_freq[kMaxRot / 2];  // theta^(-2m/R)
 };
-
-__device__ __forceinline__ uint16_t bf16_of(float x) {
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
-}
 
 // Two adjacent bf16 values (round to nearest even) at dst: one 4-byte store when dst allows it.
 __device__ __forceinline__ void store_pair(uint16_t* dst, float u, float v) {
@@ -255,72 +315,99 @@ __device__ __forceinline__ void store_pair(uint16_t* dst, float u, float v) {
   }
 }
 
+// Sum of the pairs src[0], src[stride], ... (n of them) in split order, kFinBatch loads in flight
+// (indexes past n re-read the last pair and are not added).
+__device__ __forceinline__ float2 sum_splits(const float* src, size_t stride, int n) {
+  float u = 0.0f, v = 0.0f;
+  for (int s0 = 0; s0 < n; s0 += kFinBatch) {
+    float2 x[kFinBatch];
+#pragma unroll
+    for (int j = 0; j < kFinBatch; ++j)
+      x[j] = *reinterpret_cast<const float2*>(src + static_cast<size_t>(min(s0 + j, n - 1)) * stride);
+#pragma unroll
+    for (int j = 0; j < kFinBatch; ++j)
+      if (s0 + j < n) {
+        u += x[j].x;
+        v += x[j].y;
+      }
+  }
+  return float2{u, v};
+}
+
+// The same for single values.
+__device__ __forceinline__ float sum_splits1(const float* src, size_t stride, int n) {
+  float u = 0.0f;
+  for (int s0 = 0; s0 < n; s0 += kFinBatch) {
+    float x[kFinBatch];
+#pragma unroll
+    for (int j = 0; j < kFinBatch; ++j) x[j] = src[static_cast<size_t>(min(s0 + j, n - 1)) * stride];
+#pragma unroll
+    for (int j = 0; j < kFinBatch; ++j)
+      if (s0 + j < n) u += x[j];
+  }
+  return u;
+}
+
+// Grid (T, 1 + q blocks).  Block (t, 0): the key (one wavefront), the head weights and, for the
+// rotated projection epilogue, token t's row of the angle table.  Block (t, y > 0): q pairs
+// 256 (y - 1) .. + 255 of token t, one per thread.  Each block forms the angles it uses once
+// (fp64: p up to 2^20 times a frequency up to 1 would lose most of an fp32 angle's bits).
 __global__ __launch_bounds__(kFinThreads) void frontend_finalize_kernel(FinParams P) {
   __shared__ float cs[kMaxRot / 2], sn[kMaxRot / 2];
   const int t = blockIdx.x, tid = threadIdx.x;
   const int T = gridDim.x;
   const int b = t / P.Lq;
   const int p = P.seqlens[b] - P.Lq + (t - b * P.Lq);
-  const int half = P.R / 2;
-  // rotation of pair m at position p; the angle is formed and reduced in fp64 (p up to 2^20 times
-  // a frequency up to 1 would lose most of an fp32 angle's bits)
-  for (int m = tid; m < half; m += kFinThreads) {
-    const double a = static_cast<double>(p) * pow(P.theta, -2.0 * m / P.R);
-    cs[m] = static_cast<float>(cos(a));
-    sn[m] = static_cast<float>(sin(a));
+  const int half = P.R / 2, Di = P.Di, rot0 = Di - P.R;
+  const int Nq = P.Hi * Di, Nkw = Di + P.Hi;
+  const bool key_block = blockIdx.y == 0;
+  // this thread's pair: q elements (e, e + 1) or key dims (e, e + 1); its partials are requested
+  // before the angles are formed
+  const int e = key_block ? 2 * tid : 2 * ((blockIdx.y - 1) * kFinThreads + tid);
+  const bool mine = key_block ? (tid < kWave && e < Di) : e < Nq;
+  float2 x = float2{0.0f, 0.0f};
+  if (mine)
+    x = key_block ? sum_splits(P.kp + static_cast<size_t>(t) * Nkw + e, static_cast<size_t>(T) * Nkw, P.skw)
+                  : sum_splits(P.qp + static_cast<size_t>(t) * Nq + e, static_cast<size_t>(T) * Nq, P.sq);
+  if (tid < half) {
+    const double a = static_cast<double>(p) * P.inv_freq[tid];
+    const float c = static_cast<float>(cos(a)), sv = static_cast<float>(sin(a));
+    cs[tid] = c;
+    sn[tid] = sv;
+    if (key_block && P.table) P.table[static_cast<size_t>(t) * half + tid] = float2{c, sv};
   }
   __syncthreads();
-  const int Di = P.Di, rot0 = Di - P.R;
   auto rotate = [&](int d, float& u, float& v) {  // pair (d, d + 1), d even
     if (d >= rot0) {
       const int m = (d - rot0) >> 1;
       const float c = cs[m], s = sn[m];
-      const float x = u, y = v;
-      u = x * c - y * s;
-      v = x * s + y * c;
+      const float x0 = u, y0 = v;
+      u = x0 * c - y0 * s;
+      v = x0 * s + y0 * c;
     }
   };
-  // index query: pairs of outputs, partials added in split order
-  const int Nq = P.Hi * Di;
-  for (int e = 2 * tid; e < Nq; e += 2 * kFinThreads) {
-    float u = 0.0f, v = 0.0f;
-#pragma unroll 4
-    for (int s = 0; s < P.sq; ++s) {
-      const float2 x = *reinterpret_cast<const float2*>(P.qp + (static_cast<size_t>(s) * T + t) * Nq + e);
-      u += x.x;
-      v += x.y;
+  float u = x.x, v = x.y;
+  if (!key_block) {
+    if (mine) {
+      rotate(e % Di, u, v);
+      store_pair(P.q_idx + static_cast<size_t>(t) * Nq + e, u, v);
     }
-    rotate(e % Di, u, v);
-    store_pair(P.q_idx + static_cast<size_t>(t) * Nq + e, u, v);
+    return;
   }
-  const int Nkw = Di + P.Hi;
   // head weights
-  for (int h = tid; h < P.Hi; h += kFinThreads) {
-    float x = 0.0f;
-    for (int s = 0; s < P.skw; ++s) x += P.kp[(static_cast<size_t>(s) * T + t) * Nkw + Di + h];
-    P.w[static_cast<size_t>(t) * P.Hi + h] = x;
-  }
+  for (int h = tid; h < P.Hi; h += kFinThreads)
+    P.w[static_cast<size_t>(t) * P.Hi + h] =
+        sum_splits1(P.kp + static_cast<size_t>(t) * Nkw + Di + h, static_cast<size_t>(T) * Nkw, P.skw);
   // key: one wavefront, lane l holds dims 2l and 2l + 1 (Di <= 128)
   if (tid < kWave) {
-    const int d = 2 * tid;
-    const bool mine = d < Di;
-    float u = 0.0f, v = 0.0f;
-    if (mine) {
-#pragma unroll 4
-      for (int s = 0; s < P.skw; ++s) {
-        const float* src = P.kp + (static_cast<size_t>(s) * T + t) * Nkw + d;
-        u += src[0];
-        v += src[1];
-      }
-    }
     const float ss = wave_sum_f(u * u + v * v);
     const float inv = 1.0f / sqrtf(ss / static_cast<float>(Di) + P.eps);
     if (mine) {
-      u = P.gain[d] * (u * inv);
-      v = P.gain[d + 1] * (v * inv);
-      rotate(d, u, v);
+      u = P.gain[e] * (u * inv);
+      v = P.gain[e + 1] * (v * inv);
+      rotate(e, u, v);
       if (p >= 0 && p < P.S_max)  // the caller guarantees it; a bad position writes nothing
-        store_pair(P.k_cache + (static_cast<size_t>(b) * P.S_max + p) * Di + d, u, v);
+        store_pair(P.k_cache + (static_cast<size_t>(b) * P.S_max + p) * Di + e, u, v);
     }
   }
 }
@@ -352,6 +439,26 @@ Split plan_split(long T, long N, int K) {
 
 size_t align_up(size_t x) { return (x + kWorkspaceAlign - 1) & ~(kWorkspaceAlign - 1); }
 
+// Workspace plan.  When the index query needs no reduction split and takes the LDS tiles, its
+// projection rotates and writes bf16 itself (after the finalize kernel has written the angle
+// table); otherwise its fp32 partials go through the finalize kernel.
+struct Plan {
+  Split sq, skw;
+  bool rot_q;
+  size_t q_bytes, k_bytes, table_bytes;
+};
+
+Plan make_plan(long T, int q_lora, int hidden, int Hi, int Di) {
+  Plan pl;
+  pl.sq = plan_split(T, static_cast<long>(Hi) * Di, q_lora);
+  pl.skw = plan_split(T, Di + Hi, hidden);
+  pl.rot_q = lds_tiles(T, q_lora) && pl.sq.splits == 1;
+  pl.q_bytes = pl.rot_q ? 0 : align_up(static_cast<size_t>(pl.sq.splits) * T * Hi * Di * sizeof(float));
+  pl.k_bytes = align_up(static_cast<size_t>(pl.skw.splits) * T * (Di + Hi) * sizeof(float));
+  pl.table_bytes = pl.rot_q ? align_up(static_cast<size_t>(T) * (Di / 2) * sizeof(float2)) : 0;  // R <= Di
+  return pl;
+}
+
 }  // namespace
 
 int frontend_max_rot() { return kMaxRot; }
@@ -359,10 +466,8 @@ int frontend_max_rot() { return kMaxRot; }
 size_t frontend_workspace_bytes(int B, int Lq, int q_lora, int hidden, int Hi, int Di) {
   const long T = static_cast<long>(B) * Lq;
   if (T <= 0) return 0;
-  const Split sq = plan_split(T, static_cast<long>(Hi) * Di, q_lora);
-  const Split skw = plan_split(T, Di + Hi, hidden);
-  return align_up(static_cast<size_t>(sq.splits) * T * Hi * Di * sizeof(float)) +
-         align_up(static_cast<size_t>(skw.splits) * T * (Di + Hi) * sizeof(float)) + kWorkspaceAlign;
+  const Plan pl = make_plan(T, q_lora, hidden, Hi, Di);
+  return pl.q_bytes + pl.k_bytes + pl.table_bytes + kWorkspaceAlign;
 }
 
 hipError_t launch_frontend(const uint16_t* cq, const uint16_t* hid, const uint16_t* wq_b,
@@ -373,19 +478,21 @@ hipError_t launch_frontend(const uint16_t* cq, const uint16_t* hid, const uint16
                            hipStream_t stream) {
   const long T = static_cast<long>(B) * Lq;
   const long Nq = static_cast<long>(Hi) * Di, Nkw = Di + Hi;
-  const Split sq = plan_split(T, Nq, q_lora);
-  const Split skw = plan_split(T, Nkw, hidden);
+  const Plan pl = make_plan(T, q_lora, hidden, Hi, Di);
   char* ws = align_workspace(workspace);
   float* qp = reinterpret_cast<float*>(ws);
-  float* kp = reinterpret_cast<float*>(ws + align_up(static_cast<size_t>(sq.splits) * T * Nq * sizeof(float)));
+  float* kp = reinterpret_cast<float*>(ws + pl.q_bytes);
+  float2* table = reinterpret_cast<float2*>(ws + pl.q_bytes + pl.k_bytes);
   if ((T + 31) / 32 > 65535 || T > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  auto proj = [&](const ProjParams& pp, long N, int splits) {
+  auto proj = [&](const ProjParams& pp, long N, int splits, bool rot) {
     const int K = pp.K;
     const dim3 grid(static_cast<unsigned>((N + tile_n(T, K) - 1) / tile_n(T, K)),
                     static_cast<unsigned>((T + tile_t(T, K) - 1) / tile_t(T, K)),
                     static_cast<unsigned>(splits));
-    if (lds_tiles(T, K))
-      hipLaunchKernelGGL(frontend_proj_lds_kernel, grid, dim3(kProjThreads), 0, stream, pp);
+    if (rot)
+      hipLaunchKernelGGL(frontend_proj_lds_kernel<true>, grid, dim3(kProjThreads), 0, stream, pp);
+    else if (lds_tiles(T, K))
+      hipLaunchKernelGGL(frontend_proj_lds_kernel<false>, grid, dim3(kProjThreads), 0, stream, pp);
     else if (big_tiles(T))
       hipLaunchKernelGGL((frontend_proj_kernel<2, 2>), grid, dim3(kProjThreads), 0, stream, pp);
     else
@@ -393,16 +500,21 @@ hipError_t launch_frontend(const uint16_t* cq, const uint16_t* hid, const uint16
     return hipGetLastError();
   };
   ProjParams pq{cq, wq_b, wq_b, static_cast<int>(Nq), static_cast<int>(T), static_cast<int>(Nq),
-                q_lora, sq.kchunk, qp};
-  hipError_t err = proj(pq, Nq, sq.splits);
-  if (err != hipSuccess) return err;
-  ProjParams pk{hid, wk, w_proj, Di, static_cast<int>(T), static_cast<int>(Nkw), hidden, skw.kchunk, kp};
-  if ((err = proj(pk, Nkw, skw.splits)) != hipSuccess) return err;
-  FinParams pf{qp, kp, sq.splits, skw.splits, gain, seqlens, Lq, Hi, Di, rope_dim, S_max, theta, eps,
-               q_idx, w, k_cache};
-  hipLaunchKernelGGL(frontend_finalize_kernel, dim3(static_cast<unsigned>(T)), dim3(kFinThreads), 0,
-                     stream, pf);
-  return hipGetLastError();
+                q_lora, pl.sq.kchunk, qp, table, Di, rope_dim, q_idx};
+  ProjParams pk{hid, wk, w_proj, Di, static_cast<int>(T), static_cast<int>(Nkw), hidden, pl.skw.kchunk, kp,
+                nullptr, Di, rope_dim, nullptr};
+  FinParams pf{pl.rot_q ? nullptr : qp, kp, pl.sq.splits, pl.skw.splits, gain, seqlens, Lq, Hi, Di,
+               rope_dim, S_max, eps, q_idx, w, k_cache, pl.rot_q ? table : nullptr, {}};
+  for (int m = 0; m < rope_dim / 2; ++m) pf.inv_freq[m] = std::pow(theta, -2.0 * m / rope_dim);
+  const unsigned q_blocks = pl.rot_q ? 0u : static_cast<unsigned>((Nq / 2 + kFinThreads - 1) / kFinThreads);
+  hipError_t err;
+  if (!pl.rot_q && (err = proj(pq, Nq, pl.sq.splits, false)) != hipSuccess) return err;
+  if ((err = proj(pk, Nkw, pl.skw.splits, false)) != hipSuccess) return err;
+  hipLaunchKernelGGL(frontend_finalize_kernel, dim3(static_cast<unsigned>(T), 1 + q_blocks),
+                     dim3(kFinThreads), 0, stream, pf);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (pl.rot_q) return proj(pq, Nq, 1, true);  // reads the angle table the finalize kernel wrote
+  return hipSuccess;
 }
 
 }  // namespace lsa

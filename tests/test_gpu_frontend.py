@@ -2,7 +2,8 @@
 (bf16) within the tolerance used for attention, head weights (fp32) within the worst-case fp32
 summation bound, only the current tokens' cache rows written, deterministic.  Shapes: ragged
 token counts and output tiles, reduction splits, the decode_128k shape at positions near 2^17,
-and a 256-token prefill chunk."""
+a 256-token prefill chunk, and the query projection's rotated epilogue (ragged, and a full
+4096-token chunk on sampled tokens)."""
 import dataclasses
 
 import numpy as np
@@ -42,6 +43,9 @@ CASES = [
     Case("decode_128k", 32, 1, tuple(131072 - 37 * j for j in range(32)), 131072, 1536, 3072, 32,
          128, 64, seed=504),
     Case("prefill_chunk", 1, 256, (131072,), 131072, 1536, 3072, 32, 128, 64, seed=505),
+    # no reduction split with LDS tiles: the query projection rotates in its epilogue; ragged
+    # token tiles, heads that straddle 32-output blocks
+    Case("rotated_epilogue", 2, 150, (150, 4000), 4096, 192, 128, 5, 48, 16, seed=507),
 ]
 
 
@@ -96,6 +100,35 @@ def test_frontend_matches_oracle(c):
                                     rope_theta=c.theta, norm_eps=c.eps)
     torch.cuda.synchronize()
     assert torch.equal(q, q2) and torch.equal(w, w2)
+
+
+def test_frontend_prefill_4096_sampled():
+    """A 4096-token prefill chunk at 128K (the query projection's rotated epilogue, full-size
+    weights): sampled tokens against the oracle, each evaluated as a one-token sequence at the
+    same position; tile edges and the first and last tokens included."""
+    c = Case("prefill_4096", 1, 4096, (131072,), 131072, 1536, 3072, 32, 128, 64, seed=508)
+    X = make(c)
+    cache = torch.zeros(c.B, c.S_max, c.Di, dtype=torch.bfloat16, device="cuda")
+    q, w = lsa.lsa_index_frontend(X["cq"], X["hid"], X["wq_b"], X["wk"], X["k_gain"], X["w_proj"],
+                                  X["seqlens"], cache, rope_dim=c.R, rope_theta=c.theta,
+                                  norm_eps=c.eps)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(c.seed)
+    toks = sorted(set([0, 1, 127, 128, 129, 2047, 2048, 4094, 4095]) |
+                  set(rng.integers(0, c.Lq, 23).tolist()))
+    pos = [c.seqlens[0] - c.Lq + i for i in toks]
+    sel = lambda x: x[0, toks].unsqueeze(1)  # [n, 1, ...]: one-token sequences
+    rq, rw, rk = oracle.index_frontend(bits(sel(X["cq"])), bits(sel(X["hid"])), bits(X["wq_b"]),
+                                       bits(X["wk"]), X["k_gain"].cpu().numpy(), bits(X["w_proj"]),
+                                       np.array([p + 1 for p in pos], np.int32), c.Hi, c.Di, c.R,
+                                       c.theta, c.eps)
+    assert_attention_close(sel(q).float().cpu().numpy(), rq, "prefill_4096 q_idx")
+    hid = gen.as_bf16_f64(bits(sel(X["hid"])))
+    mag = np.einsum("blj,hj->blh", np.abs(hid), np.abs(gen.as_bf16_f64(bits(X["w_proj"]))))
+    gam = c.hidden * 2.0 ** -24 / (1 - c.hidden * 2.0 ** -24)
+    assert np.all(np.abs(sel(w).cpu().numpy().astype(np.float64) - rw) <= gam * mag + 1e-30)
+    got_k = cache[0, pos].float().cpu().numpy().reshape(len(toks), 1, c.Di)
+    assert_attention_close(got_k, rk, "prefill_4096 k")
 
 
 def test_frontend_feeds_the_indexer():
