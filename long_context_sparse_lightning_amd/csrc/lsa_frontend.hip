@@ -42,13 +42,28 @@ struct ProjParams {
   const uint16_t* A;   // [T, K]
   const uint16_t* W0;  // rows [0, n_split) of the weights, [n_split, K]
   const uint16_t* W1;  // rows [n_split, N), [N - n_split, K]
-  int n_split, T, N, K, kchunk;
+  int n_split, T, N, K, kchunk, splits;
   float* out;          // [splits, T, N] fp32 partial sums (unrotated kernels)
   // rotated bf16 output (frontend_proj_lds_kernel<true>): the index query of one split
   const float2* table; // [T, R/2] (cos, sin) of each token's rotation angles
   int Di, R;
   uint16_t* q_out;     // [T, N]
 };
+
+// One launch for two projections of the same tiling (the index query, and the key with the head
+// weights): x blocks [0, nx0) belong to p[0], the rest to p[1]; z is the reduction split.
+struct ProjGroup {
+  ProjParams p[2];
+  int nx0;
+};
+
+// This workgroup's problem and x block; false when the problem has fewer splits than the grid.
+__device__ __forceinline__ bool pick(const ProjGroup& G, ProjParams& P, int& bx) {
+  const bool second = static_cast<int>(blockIdx.x) >= G.nx0;
+  P = second ? G.p[1] : G.p[0];
+  bx = second ? static_cast<int>(blockIdx.x) - G.nx0 : static_cast<int>(blockIdx.x);
+  return static_cast<int>(blockIdx.z) < P.splits;
+}
 
 __device__ __forceinline__ uint16_t bf16_of(float x) {  // round to nearest even
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
@@ -59,12 +74,15 @@ __device__ __forceinline__ uint16_t bf16_of(float x) {  // round to nearest even
 // outputs, so they share the token rows through the cache.  Workgroup tile: 32*TM tokens x
 // 128*TN outputs.
 template <int TM, int TN>
-__global__ __launch_bounds__(kProjThreads) void frontend_proj_kernel(ProjParams P) {
+__global__ __launch_bounds__(kProjThreads) void frontend_proj_kernel(ProjGroup G) {
+  ProjParams P;
+  int bx;
+  if (!pick(G, P, bx)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, g = lane >> 5;
   const int t0 = blockIdx.y * 32 * TM;
-  const int n0 = (blockIdx.x * 4 + wave) * 32 * TN;
+  const int n0 = (bx * 4 + wave) * 32 * TN;
   const int s = blockIdx.z;
   const int k0 = s * P.kchunk, k1 = min(P.K, k0 + P.kchunk);
   // rows past the end re-read the last row (their results are not stored)
@@ -184,13 +202,16 @@ constexpr int kLdsTile = 128;  // tokens and outputs per workgroup
 constexpr int kLdsRow = 40;    // bf16 per LDS row: 32 plus 8 of padding
 
 template <bool ROT>
-__global__ __launch_bounds__(kProjThreads, 2) void frontend_proj_lds_kernel(ProjParams P) {
+__global__ __launch_bounds__(kProjThreads, 2) void frontend_proj_lds_kernel(ProjGroup G) {
+  ProjParams P;
+  int bx;
+  if (!pick(G, P, bx)) return;
   __shared__ __attribute__((aligned(16))) uint16_t as[2][kLdsTile * kLdsRow];
   __shared__ __attribute__((aligned(16))) uint16_t ws[2][kLdsTile * kLdsRow];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, g = lane >> 5;
-  const int t0 = blockIdx.y * kLdsTile, n0 = blockIdx.x * kLdsTile;
+  const int t0 = blockIdx.y * kLdsTile, n0 = bx * kLdsTile;
   const int s = blockIdx.z;
   const int k0 = s * P.kchunk, k1 = min(P.K, k0 + P.kchunk);
   // global -> LDS: 16-byte piece u = tid + 256 j (j < 2) of a 128 x 32 tile is row u / 4, part u % 4
@@ -484,36 +505,49 @@ hipError_t launch_frontend(const uint16_t* cq, const uint16_t* hid, const uint16
   float* kp = reinterpret_cast<float*>(ws + pl.q_bytes);
   float2* table = reinterpret_cast<float2*>(ws + pl.q_bytes + pl.k_bytes);
   if ((T + 31) / 32 > 65535 || T > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  auto proj = [&](const ProjParams& pp, long N, int splits, bool rot) {
-    const int K = pp.K;
-    const dim3 grid(static_cast<unsigned>((N + tile_n(T, K) - 1) / tile_n(T, K)),
+  // tiles along the outputs of a problem with N outputs and reduction length K
+  auto nx = [&](long N, int K) { return static_cast<int>((N + tile_n(T, K) - 1) / tile_n(T, K)); };
+  auto same_tiling = [&](int K0, int K1) {
+    return lds_tiles(T, K0) == lds_tiles(T, K1);  // tile sizes depend on T and on this alone
+  };
+  // launches one or two projections of the same tiling
+  auto proj = [&](const ProjParams& a, long Na, const ProjParams* b, long Nb, bool rot) {
+    ProjGroup G{{a, b ? *b : a}, nx(Na, a.K)};
+    const int K = a.K;
+    const dim3 grid(static_cast<unsigned>(G.nx0 + (b ? nx(Nb, b->K) : 0)),
                     static_cast<unsigned>((T + tile_t(T, K) - 1) / tile_t(T, K)),
-                    static_cast<unsigned>(splits));
+                    static_cast<unsigned>(std::max(a.splits, b ? b->splits : 0)));
     if (rot)
-      hipLaunchKernelGGL(frontend_proj_lds_kernel<true>, grid, dim3(kProjThreads), 0, stream, pp);
+      hipLaunchKernelGGL(frontend_proj_lds_kernel<true>, grid, dim3(kProjThreads), 0, stream, G);
     else if (lds_tiles(T, K))
-      hipLaunchKernelGGL(frontend_proj_lds_kernel<false>, grid, dim3(kProjThreads), 0, stream, pp);
+      hipLaunchKernelGGL(frontend_proj_lds_kernel<false>, grid, dim3(kProjThreads), 0, stream, G);
     else if (big_tiles(T))
-      hipLaunchKernelGGL((frontend_proj_kernel<2, 2>), grid, dim3(kProjThreads), 0, stream, pp);
+      hipLaunchKernelGGL((frontend_proj_kernel<2, 2>), grid, dim3(kProjThreads), 0, stream, G);
     else
-      hipLaunchKernelGGL((frontend_proj_kernel<1, 1>), grid, dim3(kProjThreads), 0, stream, pp);
+      hipLaunchKernelGGL((frontend_proj_kernel<1, 1>), grid, dim3(kProjThreads), 0, stream, G);
     return hipGetLastError();
   };
   ProjParams pq{cq, wq_b, wq_b, static_cast<int>(Nq), static_cast<int>(T), static_cast<int>(Nq),
-                q_lora, pl.sq.kchunk, qp, table, Di, rope_dim, q_idx};
-  ProjParams pk{hid, wk, w_proj, Di, static_cast<int>(T), static_cast<int>(Nkw), hidden, pl.skw.kchunk, kp,
-                nullptr, Di, rope_dim, nullptr};
+                q_lora, pl.sq.kchunk, pl.sq.splits, qp, table, Di, rope_dim, q_idx};
+  ProjParams pk{hid, wk, w_proj, Di, static_cast<int>(T), static_cast<int>(Nkw), hidden, pl.skw.kchunk,
+                pl.skw.splits, kp, nullptr, Di, rope_dim, nullptr};
   FinParams pf{pl.rot_q ? nullptr : qp, kp, pl.sq.splits, pl.skw.splits, gain, seqlens, Lq, Hi, Di,
                rope_dim, S_max, eps, q_idx, w, k_cache, pl.rot_q ? table : nullptr, {}};
   for (int m = 0; m < rope_dim / 2; ++m) pf.inv_freq[m] = std::pow(theta, -2.0 * m / rope_dim);
   const unsigned q_blocks = pl.rot_q ? 0u : static_cast<unsigned>((Nq / 2 + kFinThreads - 1) / kFinThreads);
   hipError_t err;
-  if (!pl.rot_q && (err = proj(pq, Nq, pl.sq.splits, false)) != hipSuccess) return err;
-  if ((err = proj(pk, Nkw, pl.skw.splits, false)) != hipSuccess) return err;
+  if (pl.rot_q) {
+    err = proj(pk, Nkw, nullptr, 0, false);
+  } else if (same_tiling(q_lora, hidden)) {
+    err = proj(pq, Nq, &pk, Nkw, false);
+  } else if ((err = proj(pq, Nq, nullptr, 0, false)) == hipSuccess) {
+    err = proj(pk, Nkw, nullptr, 0, false);
+  }
+  if (err != hipSuccess) return err;
   hipLaunchKernelGGL(frontend_finalize_kernel, dim3(static_cast<unsigned>(T), 1 + q_blocks),
                      dim3(kFinThreads), 0, stream, pf);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (pl.rot_q) return proj(pq, Nq, 1, true);  // reads the angle table the finalize kernel wrote
+  if (pl.rot_q) return proj(pq, Nq, nullptr, 0, true);  // reads the angle table the finalize kernel wrote
   return hipSuccess;
 }
 

@@ -46,6 +46,8 @@ CASES = [
     # no reduction split with LDS tiles: the query projection rotates in its epilogue; ragged
     # token tiles, heads that straddle 32-output blocks
     Case("rotated_epilogue", 2, 150, (150, 4000), 4096, 192, 128, 5, 48, 16, seed=507),
+    # the two projections take different tilings (q_lora not a multiple of 64): two launches
+    Case("mixed_tiling", 1, 130, (500,), 512, 80, 128, 4, 64, 32, seed=509),
 ]
 
 
