@@ -17,12 +17,13 @@ from __future__ import annotations
 import argparse
 import csv
 import os
-import re
 import statistics
+
+from long_context_sparse_lightning_amd.prof_trace import short
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-KERNELS = ("index_scores_qb_kernel", "sparse_mla_kernel")
+KERNELS = ("index_scores_qb_kernel", "sparse_mla_kernel", "frontend_proj_lds_kernel")
 
 
 def per_dispatch(path: str):
@@ -43,16 +44,15 @@ def summarize(csv_path: str, workload: str, command: str) -> str:
              "Command (repository root, one MI355X):", "", f"    {command}", "",
              "| kernel | dispatches | MfmaUtil % (mean) | bf16 matrix flops per dispatch | "
              "profiled duration (us, mean) |", "|---|---|---|---|---|"]
-    for k in KERNELS:
-        ds = [d for d in disp.values() if k in d["kernel"] and "MfmaUtil" in d]
-        if not ds:
-            continue
+    by_name = {}
+    for d in disp.values():
+        if "MfmaUtil" in d and any(k in d["kernel"] for k in KERNELS):
+            by_name.setdefault(short(d["kernel"]), []).append(d)
+    for name in sorted(by_name, key=lambda n: [k in n for k in KERNELS].index(True)):
+        ds = by_name[name]
         util = statistics.mean(d["MfmaUtil"] for d in ds)
         flops = statistics.mean(d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512 for d in ds)
         dur = statistics.mean(d["ns"] for d in ds) / 1e3
-        full = next(d["kernel"] for d in ds)
-        m = re.search(k + r"(<[^>]*>)?", full)
-        name = m.group(0) if m else k
         lines.append(f"| {name} | {len(ds)} | {util:.1f} | {flops:.4g} | {dur:.1f} |")
     lines += ["", "MfmaUtil = MFMA-busy cycles summed over SIMDs / (GPU-active cycles x SIMDs); "
               "bf16 matrix flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (includes the padded "

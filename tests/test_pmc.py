@@ -5,7 +5,7 @@ import json
 
 import pytest
 
-from long_context_sparse_lightning_amd import pmc, pmc_mfma
+from long_context_sparse_lightning_amd import pmc, pmc_mfma, prof_trace
 
 FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp",
           "End_Timestamp"]
@@ -86,3 +86,21 @@ def test_mfma_table(tmp_path, monkeypatch):
     assert "    the command" in text
     assert "| index_scores_qb_kernel<8, 2> | 2 | 62.0 | 5.12e+05 | 3.5 |" in text
     assert "| sparse_mla_kernel<576, 512, true> | 2 | 21.0 | 1.024e+04 | 1.5 |" in text
+
+
+def test_trace_summary(tmp_path):
+    stats = tmp_path / "run_kernel_stats.csv"
+    with open(stats, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "AverageNs", "MinNs", "MaxNs"])
+        w.writeheader()
+        w.writerow({"Name": K1, "Calls": 45, "AverageNs": 183800.0, "MinNs": 178800, "MaxNs": 239900})
+        w.writerow({"Name": "(anonymous namespace)::gen_fill_kernel(void*, int, unsigned int)",
+                    "Calls": 7, "AverageNs": 2000.0, "MinNs": 1000, "MaxNs": 3000})
+    bench = {"steps": 20, "ms_per_step": 0.25, "value": 128000.0, "unit": "queries/s",
+             "roofline": {"kernel": "lsa_index_topk", "avg_launch_ms": 0.2041, "achieved": 5262.9,
+                          "unit": "GB/s", "frac": 0.6579, "peak": 8000.0}}
+    text = prof_trace.summarize(str(stats), "t", "rocprofv3 cmd", bench)
+    assert "    rocprofv3 cmd" in text
+    assert "| index_scores_kernel<128, true> | 45 | 183.8 | 178.8 | 239.9 |" in text
+    assert "| gen_fill_kernel (input setup, not a step) | 7 | 2.0 | 1.0 | 3.0 |" in text
+    assert "average launch 204.1 us -> 5262.9 GB/s algorithmic (65.8% of 8000.0 GB/s)" in text
