@@ -126,6 +126,37 @@ def sparse_mla(q, kv, indices, n_sel, seqlens, Dv: int, scale: float):
     return out, lse
 
 
+def mtp_draft_indices(indices, n_sel, index_seqlens, seqlens, max_appended: int):
+    """Selection of a multi-token-prediction draft step on a shared index pass (page "LongCat
+    Sparse Attention技术深度解析", "技术实现细节": the three draft steps share one index pass).
+    indices int32 [B,topk] and n_sel int32 [B] of the pass made at index_seqlens [B]; the query
+    sits at p = seqlens[b] - 1.  Per sequence: the pass's first min(n_sel, topk) entries, then
+    the positions appended since, index_seqlens[b] .. p (at most max_appended of them).
+    Returns (indices int32 [B,1,topk+max_appended], -1 padded; n_sel int32 [B,1])."""
+    indices = np.asarray(indices, np.int32)
+    B, topk = indices.shape
+    out = np.full((B, 1, topk + max_appended), -1, np.int32)
+    cnt = np.zeros((B, 1), np.int32)
+    for b in range(B):
+        base = indices[b, :max(0, min(int(n_sel[b]), topk))]
+        first = max(int(index_seqlens[b]), 0)
+        app = np.arange(first, min(int(seqlens[b]), first + max_appended), dtype=np.int32)
+        sel = np.concatenate([base, app])
+        out[b, 0, :len(sel)] = sel
+        cnt[b, 0] = len(sel)
+    return out, cnt
+
+
+def mtp_draft_attention(q, kv, indices, n_sel, index_seqlens, seqlens, max_appended: int, Dv: int,
+                        scale: float):
+    """Attention of a draft step (q bf16 bits [B,H,Dqk]) over mtp_draft_indices' selection:
+    the attention of sparse_mla.  Returns (out f64 [B,H,Dv], lse f64 [B,H])."""
+    idx, cnt = mtp_draft_indices(indices, n_sel, index_seqlens, seqlens, max_appended)
+    q = np.asarray(q)
+    out, lse = sparse_mla(q[:, None], kv, idx, cnt, seqlens, Dv, scale)
+    return out[:, 0], lse[:, 0]
+
+
 def index_frontend(cq, hid, wq_b, wk, gain, w_proj, seqlens, Hi: int, Di: int, rope_dim: int,
                    theta: float, eps: float):
     """cq bf16 bits [B,Lq,q_lora]; hid bf16 bits [B,Lq,hidden]; wq_b bf16 bits [Hi*Di,q_lora];
