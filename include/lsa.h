@@ -133,6 +133,9 @@ lsa_status lsa_index_topk(const void* q_idx, const float* w, const void* k_idx,
                           int init_tokens, int local_tokens, int32_t* indices, int32_t* n_sel,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Largest selection the attention takes: 64 partial splits of at most 2048 rows each. */
+#define LSA_MLA_MAX_TOPK 131072
+
 /* Workspace (bytes) lsa_sparse_mla_decode / _prefill need for these sizes (0 is possible).
  * `dense` is 1 when the call will pass indices == NULL. */
 size_t lsa_mla_workspace_bytes(int B, int Lq, int H, int Dv, int S_max, int topk, int dense);
@@ -159,7 +162,7 @@ size_t lsa_mla_workspace_bytes(int B, int Lq, int H, int Dv, int S_max, int topk
  * one index pass); the inputs are never written.
  * Rows that select nothing get out = 0 and lse = -inf.
  * Supported: (Dqk, Dv) in {(576, 512), (80, 64)}; H >= 1 (heads are processed in groups of
- * 32); topk >= 1 when indices != NULL.
+ * 32); 1 <= topk <= LSA_MLA_MAX_TOPK when indices != NULL.
  */
 lsa_status lsa_sparse_mla_decode(const void* q, const void* kv, const int32_t* indices,
                                  const int32_t* n_sel, const int32_t* seqlens, int B, int H,
@@ -172,6 +175,43 @@ lsa_status lsa_sparse_mla_prefill(const void* q, const void* kv, const int32_t* 
                                   int H, int Dqk, int Dv, int S_max, int topk,
                                   float softmax_scale, void* out, float* lse, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/* Most positions appended after an index pass that lsa_mtp_draft_attention takes. */
+#define LSA_MTP_MAX_APPENDED 64
+/* Largest selection lsa_mtp_draft_attention takes (its last split also holds the appended
+ * positions). */
+#define LSA_MTP_MAX_TOPK 65536
+
+/* Workspace (bytes) lsa_mtp_draft_attention needs for these sizes (0 is possible). */
+size_t lsa_mtp_draft_workspace_bytes(int B, int H, int Dv, int S_max, int topk, int max_appended);
+
+/*
+ * Attention of a multi-token-prediction draft step on a shared index pass (page "LongCat Sparse
+ * Attention技术深度解析…", section "技术实现细节", multi-token prediction: the three draft steps
+ * of speculative decoding share a single index pass; config key dsa_mtp_cli).  The index pass
+ * ran when sequence b had index_seqlens[b] tokens; the draft steps have appended the tokens
+ * since.  For the query at p = seqlens[b] - 1:
+ *   sel = indices[b, 0:n_sel[b]]  followed by  index_seqlens[b], ..., p
+ * (the appended positions, at most max_appended of them; later ones are not attended), then the
+ * attention of lsa_sparse_mla_decode over sel.  The appended tokens are the most recent ones,
+ * which the forced local window keeps at every position, so each draft step attends to them
+ * without a new index pass.
+ *   indices        int32 [B, topk] of the index pass (lsa_index_topk or lsa_topk_select, Lq = 1)
+ *   n_sel          int32 [B]
+ *   index_seqlens  int32 [B] sequence lengths at the index pass
+ *   seqlens        int32 [B] current lengths
+ *   q, kv, out, lse, softmax_scale, workspace, stream: as for lsa_sparse_mla_decode.
+ * The inputs are never written; one index pass serves any number of calls.
+ * Errors: those of lsa_sparse_mla_decode; NULL indices, n_sel or index_seqlens ->
+ * LSA_ERR_NULL_ARG; max_appended outside [0, LSA_MTP_MAX_APPENDED] -> LSA_ERR_BAD_SHAPE;
+ * topk > LSA_MTP_MAX_TOPK -> LSA_ERR_UNSUPPORTED.
+ */
+lsa_status lsa_mtp_draft_attention(const void* q, const void* kv, const int32_t* indices,
+                                   const int32_t* n_sel, const int32_t* index_seqlens,
+                                   const int32_t* seqlens, int B, int H, int Dqk, int Dv,
+                                   int S_max, int topk, int max_appended, float softmax_scale,
+                                   void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /* Workspace (bytes) lsa_index_frontend needs for these sizes (0 for invalid sizes). */
 size_t lsa_index_frontend_workspace_bytes(int B, int Lq, int q_lora, int hidden, int Hi, int Di);

@@ -149,6 +149,8 @@ static lsa_status check_mla(const char* fn, int B, int Lq, int H, int Dqk, int D
     return fail(LSA_ERR_BAD_SHAPE, "%s: H=%d Dqk=%d Dv=%d S_max=%d must be > 0", fn, H, Dqk, Dv, S_max);
   if (Dv > Dqk) return fail(LSA_ERR_BAD_SHAPE, "%s: Dv=%d > Dqk=%d", fn, Dv, Dqk);
   if (!dense && topk <= 0) return fail(LSA_ERR_BAD_SHAPE, "%s: topk=%d must be > 0", fn, topk);
+  if (!dense && topk > LSA_MLA_MAX_TOPK)
+    return fail(LSA_ERR_UNSUPPORTED, "%s: topk=%d > %d", fn, topk, LSA_MLA_MAX_TOPK);
   if (!(softmax_scale == softmax_scale) || softmax_scale == INFINITY || softmax_scale == -INFINITY)
     return fail(LSA_ERR_BAD_SHAPE, "%s: softmax_scale must be finite", fn);
   if (!((Dqk == 576 && Dv == 512) || (Dqk == 80 && Dv == 64)))
@@ -158,7 +160,9 @@ static lsa_status check_mla(const char* fn, int B, int Lq, int H, int Dqk, int D
 }
 
 size_t lsa_mla_workspace_bytes(int B, int Lq, int H, int Dv, int S_max, int topk, int dense) {
-  if (B <= 0 || Lq <= 0 || H <= 0 || Dv <= 0 || S_max <= 0 || (!dense && topk <= 0)) return 0;
+  if (B <= 0 || Lq <= 0 || H <= 0 || Dv <= 0 || S_max <= 0 ||
+      (!dense && (topk <= 0 || topk > LSA_MLA_MAX_TOPK)))
+    return 0;
   return lsa::mla_workspace_bytes(B, Lq, H, Dv, S_max, topk, dense);
 }
 
@@ -199,6 +203,42 @@ lsa_status lsa_sparse_mla_prefill(const void* q, const void* kv, const int32_t* 
                                   size_t workspace_bytes, void* stream) {
   return run_mla("lsa_sparse_mla_prefill", q, kv, indices, n_sel, seqlens, B, Lq, H, Dqk, Dv,
                  S_max, topk, softmax_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+size_t lsa_mtp_draft_workspace_bytes(int B, int H, int Dv, int S_max, int topk, int max_appended) {
+  if (B <= 0 || H <= 0 || Dv <= 0 || S_max <= 0 || topk <= 0 || topk > LSA_MTP_MAX_TOPK ||
+      max_appended < 0 || max_appended > LSA_MTP_MAX_APPENDED)
+    return 0;
+  return lsa::mla_workspace_bytes(B, 1, H, Dv, S_max, topk, 0, max_appended);
+}
+
+lsa_status lsa_mtp_draft_attention(const void* q, const void* kv, const int32_t* indices,
+                                   const int32_t* n_sel, const int32_t* index_seqlens,
+                                   const int32_t* seqlens, int B, int H, int Dqk, int Dv,
+                                   int S_max, int topk, int max_appended, float softmax_scale,
+                                   void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  const char* fn = "lsa_mtp_draft_attention";
+  lsa_status st = check_mla(fn, B, 1, H, Dqk, Dv, S_max, topk, false, softmax_scale);
+  if (st != LSA_OK) return st;
+  if (max_appended < 0 || max_appended > LSA_MTP_MAX_APPENDED)
+    return fail(LSA_ERR_BAD_SHAPE, "%s: max_appended=%d outside [0, %d]", fn, max_appended,
+                LSA_MTP_MAX_APPENDED);
+  if (topk > LSA_MTP_MAX_TOPK)
+    return fail(LSA_ERR_UNSUPPORTED, "%s: topk=%d > %d", fn, topk, LSA_MTP_MAX_TOPK);
+  if (B == 0) return ok();
+  if (!q || !kv || !seqlens || !out) return fail(LSA_ERR_NULL_ARG, "%s: NULL q/kv/seqlens/out", fn);
+  if (!indices || !n_sel || !index_seqlens)
+    return fail(LSA_ERR_NULL_ARG, "%s: NULL indices/n_sel/index_seqlens", fn);
+  const size_t need = lsa::mla_workspace_bytes(B, 1, H, Dv, S_max, topk, 0, max_appended);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(LSA_ERR_WORKSPACE, "%s: workspace %zu bytes at %p, need %zu", fn, workspace_bytes,
+                workspace, need);
+  return launched(lsa::launch_mla(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv),
+                                  indices, n_sel, seqlens, B, 1, H, Dqk, Dv, S_max, topk, softmax_scale,
+                                  static_cast<uint16_t*>(out), lse, workspace,
+                                  static_cast<hipStream_t>(stream), index_seqlens, max_appended),
+                  fn);
 }
 
 static lsa_status check_frontend(int B, int Lq, int q_lora, int hidden, int Hi, int Di,

@@ -155,11 +155,14 @@ hipError_t launch_index_topk(const uint16_t* q_idx, const float* w, const uint16
                              int topk, int init_tokens, int local_tokens, int32_t* indices,
                              int32_t* n_sel, void* workspace, hipStream_t stream);
 
-size_t mla_workspace_bytes(int B, int Lq, int H, int Dv, int S_max, int topk, int dense);
+// With index_seqlens, each row also attends to the positions appended after the index pass
+// ([index_seqlens[b], p], at most max_app); `app` sizes the plan for them.
+size_t mla_workspace_bytes(int B, int Lq, int H, int Dv, int S_max, int topk, int dense, int app = 0);
 hipError_t launch_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indices,
                       const int32_t* n_sel, const int32_t* seqlens, int B, int Lq, int H, int Dqk,
                       int Dv, int S_max, int topk, float softmax_scale, uint16_t* out, float* lse,
-                      void* workspace, hipStream_t stream);
+                      void* workspace, hipStream_t stream, const int32_t* index_seqlens = nullptr,
+                      int max_app = 0);
 
 // Indexer front end: index queries, head weights and the new keys of the current tokens.
 int frontend_max_rot();

@@ -90,6 +90,10 @@ struct MlaParams {
   const int32_t* indices;
   const int32_t* n_sel;
   const int32_t* seqlens;
+  // positions appended after the index pass (multi-token-prediction draft steps): with
+  // index_seqlens, row (b, i) also attends to [index_seqlens[b], p], at most max_app of them
+  const int32_t* index_seqlens;
+  int max_app;
   int Lq, H, S_max, topk;
   int hgroups, splits, kps;  // head groups, workgroups per (row, head group), rows per split
   int pairs;                 // query rows x heads
@@ -152,9 +156,15 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
   const int b = row / P.Lq;
   const int n = min(P.seqlens[b] - P.Lq + (row - b * P.Lq) + 1, P.S_max);
   constexpr bool sparse = SPARSE;
-  const int cnt = sparse ? min(P.n_sel[row], P.topk) : max(n, 0);
+  const int cnt_sel = sparse ? min(P.n_sel[row], P.topk) : max(n, 0);
+  int cnt = cnt_sel, app0 = 0;
+  if (sparse && P.index_seqlens) {
+    app0 = max(P.index_seqlens[b], 0);
+    cnt += min(max(n - app0, 0), P.max_app);
+  }
   const int j0 = split * P.kps;
-  const int j1 = min(cnt, j0 + P.kps);
+  // the last split also takes the appended positions (without them cnt <= splits * kps)
+  const int j1 = split == P.splits - 1 ? cnt : min(cnt, j0 + P.kps);
   const int ntiles = j1 > j0 ? (j1 - j0 + kTile - 1) / kTile : 0;
   const uint16_t* kv_b = P.kv + static_cast<size_t>(b) * P.S_max * DQK;
 
@@ -176,7 +186,10 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
   // this split's row positions (clamped into the cache) staged in LDS
   if constexpr (sparse) {
     const int32_t* ilist = P.indices + static_cast<size_t>(row) * P.topk;
-    for (int j = tid; j < j1 - j0; j += kThreads) slice[j] = min(max(ilist[j0 + j], 0), P.S_max - 1);
+    for (int j = tid; j < j1 - j0; j += kThreads) {
+      const int jj = j0 + j;
+      slice[j] = jj < cnt_sel ? min(max(ilist[jj], 0), P.S_max - 1) : app0 + (jj - cnt_sel);
+    }
   }
   // retire the query and index loads here: a wait left to the compiler would sit inside the
   // loop and drain the ring on every step
@@ -507,7 +520,7 @@ struct MlaPlan {
   size_t ws_o_bytes = 0, ws_ml_bytes = 0, ws_slack = 0;
 };
 
-MlaPlan make_plan(long rows, int H, int Dv, int S_max, int topk, int dense) {
+MlaPlan make_plan(long rows, int H, int Dv, int S_max, int topk, int dense, int app = 0) {
   MlaPlan pl;
   pl.hgroups = (H + kHeadGroup - 1) / kHeadGroup;
   const long keys = dense ? S_max : topk;
@@ -518,9 +531,13 @@ MlaPlan make_plan(long rows, int H, int Dv, int S_max, int topk, int dense) {
   splits = std::min<long>(splits, kMaxSplits);
   if (!dense) splits = std::max<long>(splits, (keys + kMaxRowsPerSplit - 1) / kMaxRowsPerSplit);
   splits = std::max<long>(splits, 1);
-  long kps = (keys + splits - 1) / splits;
-  kps = ((kps + kTile - 1) / kTile) * kTile;
-  if (kps < kTile) kps = kTile;
+  auto per_split = [&](long sp) {
+    const long k = ((keys + sp - 1) / sp + kTile - 1) / kTile * kTile;
+    return k < kTile ? static_cast<long>(kTile) : k;
+  };
+  long kps = per_split(splits);
+  // the last split also stages the appended positions: keep them within its LDS slice
+  while (!dense && app > 0 && kps + app > kMaxRowsPerSplit && splits < kMaxSplits) kps = per_split(++splits);
   splits = (keys + kps - 1) / kps;
   if (splits < 1) splits = 1;
   pl.splits = static_cast<int>(splits);
@@ -555,23 +572,27 @@ hipError_t launch_dims(const MlaParams& P, long rows, hipStream_t stream) {
 
 }  // namespace
 
-size_t mla_workspace_bytes(int B, int Lq, int H, int Dv, int S_max, int topk, int dense) {
-  const MlaPlan pl = make_plan(static_cast<long>(B) * Lq, H, Dv, S_max, topk, dense);
+size_t mla_workspace_bytes(int B, int Lq, int H, int Dv, int S_max, int topk, int dense, int app) {
+  const MlaPlan pl = make_plan(static_cast<long>(B) * Lq, H, Dv, S_max, topk, dense, app);
   return pl.ws_o_bytes + pl.ws_ml_bytes + pl.ws_slack;
 }
 
 hipError_t launch_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indices,
                       const int32_t* n_sel, const int32_t* seqlens, int B, int Lq, int H, int Dqk,
                       int Dv, int S_max, int topk, float softmax_scale, uint16_t* out, float* lse,
-                      void* workspace, hipStream_t stream) {
+                      void* workspace, hipStream_t stream, const int32_t* index_seqlens,
+                      int max_app) {
   const long rows = static_cast<long>(B) * Lq;
-  const MlaPlan pl = make_plan(rows, H, Dv, S_max, topk, indices == nullptr);
+  const int app = index_seqlens ? max_app : 0;
+  const MlaPlan pl = make_plan(rows, H, Dv, S_max, topk, indices == nullptr, app);
   MlaParams P{};
   P.q = q;
   P.kv = kv;
   P.indices = indices;
   P.n_sel = n_sel;
   P.seqlens = seqlens;
+  P.index_seqlens = index_seqlens;
+  P.max_app = app;
   P.Lq = Lq;
   P.H = H;
   P.S_max = S_max;

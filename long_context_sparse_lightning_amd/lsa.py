@@ -22,7 +22,8 @@ STATUS = {0: "LSA_OK", 1: "LSA_ERR_NULL_ARG", 2: "LSA_ERR_BAD_SHAPE", 3: "LSA_ER
 EXPORTED = ["lsa_status_str", "lsa_last_error", "lsa_index_scores", "lsa_topk_workspace_bytes",
             "lsa_topk_select", "lsa_index_topk_workspace_bytes", "lsa_index_topk",
             "lsa_mla_workspace_bytes", "lsa_sparse_mla_decode", "lsa_sparse_mla_prefill",
-            "lsa_index_frontend_workspace_bytes", "lsa_index_frontend"]
+            "lsa_index_frontend_workspace_bytes", "lsa_index_frontend",
+            "lsa_mtp_draft_workspace_bytes", "lsa_mtp_draft_attention"]
 
 
 class LsaError(RuntimeError):
@@ -68,6 +69,10 @@ def lib():
         L.lsa_index_frontend.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, F, I, P, P, P,
                                          P, Z, P]
         L.lsa_index_frontend.restype = I
+        L.lsa_mtp_draft_workspace_bytes.argtypes = [I, I, I, I, I, I]
+        L.lsa_mtp_draft_workspace_bytes.restype = Z
+        L.lsa_mtp_draft_attention.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, P, Z, P]
+        L.lsa_mtp_draft_attention.restype = I
         _lib = L
     return _lib
 
@@ -223,6 +228,37 @@ def lsa_sparse_mla_prefill(q, kv, indices, n_sel, seqlens, Dv, softmax_scale, ou
     """q bf16 [B,Lq,H,Dqk], kv bf16 [B,S_max,Dqk], indices i32 [B,Lq,topk] (or None: dense
     causal), n_sel i32 [B,Lq] -> out bf16 [B,Lq,H,Dv] (lse f32 [B,Lq,H] written if given)."""
     return _mla(False, q, kv, indices, n_sel, seqlens, Dv, softmax_scale, out, lse, workspace)
+
+
+def lsa_mtp_draft_workspace_bytes(B, H, Dv, S_max, topk, max_appended) -> int:
+    return int(lib().lsa_mtp_draft_workspace_bytes(B, H, Dv, S_max, topk, max_appended))
+
+
+def lsa_mtp_draft_attention(q, kv, indices, n_sel, index_seqlens, seqlens, Dv, softmax_scale,
+                            max_appended=3, out=None, lse=None, workspace=None):
+    """A draft step on a shared index pass: q bf16 [B,H,Dqk], kv bf16 [B,S_max,Dqk], indices i32
+    [B,topk] and n_sel i32 [B] of the pass made at index_seqlens i32 [B]; the query sits at
+    seqlens[b] - 1 and also attends to the positions appended since (at most max_appended)
+    -> out bf16 [B,H,Dv] (lse f32 [B,H] written if given)."""
+    _want(q, "q", torch.bfloat16, 3)
+    _want(kv, "kv", torch.bfloat16, 3)
+    _want(indices, "indices", torch.int32, 2)
+    _want(n_sel, "n_sel", torch.int32, 1)
+    _want(index_seqlens, "index_seqlens", torch.int32, 1)
+    _want(seqlens, "seqlens", torch.int32, 1)
+    B, H, Dqk = q.shape
+    S_max, topk = kv.shape[1], indices.shape[1]
+    if out is None:
+        out = torch.empty(B, H, Dv, dtype=torch.bfloat16, device=q.device)
+    need = lsa_mtp_draft_workspace_bytes(B, H, Dv, S_max, topk, max_appended)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().lsa_mtp_draft_attention(_ptr(q), _ptr(kv), _ptr(indices), _ptr(n_sel),
+                                         _ptr(index_seqlens), _ptr(seqlens), B, H, Dqk, Dv, S_max,
+                                         topk, int(max_appended), float(softmax_scale), _ptr(out),
+                                         _ptr(lse), _ptr(workspace), wbytes, _stream(q)))
+    return out
 
 
 def lsa_index_frontend_workspace_bytes(B, Lq, q_lora, hidden, Hi, Di) -> int:

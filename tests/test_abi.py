@@ -102,6 +102,8 @@ def test_mla_argument_errors_and_workspace():
     assert dec(p, p, p, p, p, 4, 32, 576, 512, 1000, 0, 0.1, p, None, p, 1 << 30, None) == 2
     assert dec(p, p, p, p, p, 4, 32, 576, 512, 1000, 64, float("nan"), p, None, p, 1 << 30,
                None) == 2
+    assert dec(p, p, p, p, p, 4, 32, 576, 512, 1 << 20, 131073, 0.1, p, None, p, 1 << 30, None) == 3
+    assert L.lsa_mla_workspace_bytes(4, 1, 32, 512, 1 << 20, 131073, 0) == 0
     need = L.lsa_mla_workspace_bytes(32, 1, 32, 512, 131072, 2048, 0)
     assert need > 0
     assert dec(p, p, p, p, p, 32, 32, 576, 512, 131072, 2048, 0.07, p, None, None, 0, None) == 4
@@ -133,8 +135,33 @@ def test_index_frontend_argument_errors_and_workspace():
     assert fe(None, None, None, None, None, None, None, 0, 1, 1536, 3072, 32, 128, 64, 1e6, 1e-6,
               100, None, None, None, None, 0, None) == 0
     assert L.lsa_index_frontend_workspace_bytes(32, 1, 1530, 3072, 32, 128) == 0
-    # prefill-sized calls stay modest: one reduction split at 4096 tokens
-    assert L.lsa_index_frontend_workspace_bytes(1, 4096, 1536, 3072, 32, 128) <= 96 << 20
+    # prefill-sized calls stay modest: the query is rotated in its projection's epilogue, so only
+    # the key/weight partials and the angle table remain
+    assert L.lsa_index_frontend_workspace_bytes(1, 4096, 1536, 3072, 32, 128) <= 32 << 20
+
+
+def test_mtp_draft_argument_errors_and_workspace():
+    L = lsa.lib()
+    p = ctypes.c_void_p(16)
+    f = L.lsa_mtp_draft_attention
+
+    def call(B=4, Dqk=576, Dv=512, topk=2048, app=3, idx=p, nsel=p, iseq=p, ws=p, wbytes=1 << 30):
+        return f(p, p, idx, nsel, iseq, p, B, 32, Dqk, Dv, 131072, topk, app, 0.07, p, None, ws,
+                 wbytes, None)
+
+    assert call(app=-1) == 2 and call(app=65) == 2 and call(topk=0) == 2
+    assert call(topk=65537) == 3 and L.lsa_mtp_draft_workspace_bytes(4, 32, 512, 1 << 20, 65537, 3) == 0
+    assert call(Dqk=512, Dv=448) == 3
+    assert call(idx=None) == 1 and call(nsel=None) == 1 and call(iseq=None) == 1
+    need = L.lsa_mtp_draft_workspace_bytes(32, 32, 512, 131072, 2048, 3)
+    assert need > 0 and need == L.lsa_mla_workspace_bytes(32, 1, 32, 512, 131072, 2048, 0)
+    assert call(B=32, wbytes=need - 1) == 4 and call(B=32, ws=None, wbytes=0) == 4
+    assert f(None, None, None, None, None, None, 0, 32, 576, 512, 100, 64, 3, 0.1, None, None,
+             None, 0, None) == 0
+    assert L.lsa_mtp_draft_workspace_bytes(32, 32, 512, 131072, 2048, 65) == 0
+    # one split per row of 2048 at 512 rows: the appended positions push it to two
+    assert L.lsa_mtp_draft_workspace_bytes(512, 32, 512, 131072, 2048, 3) > 0
+    assert L.lsa_mla_workspace_bytes(512, 1, 32, 512, 131072, 2048, 0) == 0
 
 
 @pytest.mark.parametrize("name", ["tiny_decode", "decode_32k", "decode_128k", "prefill_128k",
