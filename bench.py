@@ -59,11 +59,18 @@ def algorithmic_bytes(wl):
     for b in range(wl.B):
         for i in range(wl.Lq):
             n = wl.seqlens[b] - wl.Lq + i + 1
-            k = min(n, wl.topk)
             tot += n * wl.Di * 2 + wl.Hi * wl.Di * 2 + wl.Hi * 4 + wl.topk * 4
-            tot += wl.mla_calls * (k * wl.Dqk * 2 + wl.H * wl.Dqk * 2 + wl.H * wl.Dv * 2 + wl.topk * 4)
+            tot += sum(attn_row_bytes(wl, n, c) for c in range(wl.attn_calls))
             score_rt += 2 * n * 4
     return tot, score_rt
+
+
+def attn_row_bytes(wl, n, c):
+    """Attention call c of one query row whose index pass saw n positions: the selected latent
+    rows (plus the draft positions appended since the pass), the query, the output and the
+    index list."""
+    rows = min(n, wl.topk) + wl.attn_inputs(c)[2]
+    return rows * wl.Dqk * 2 + wl.H * wl.Dqk * 2 + wl.H * wl.Dv * 2 + wl.topk * 4
 
 
 def indexer_bytes(wl):
@@ -174,7 +181,8 @@ def cpu_baseline(wl, sample_rows, gpu=None):
         prepared.append((b, i, p, host_slice(wl, "qidx", b)[i:i + 1][None],
                          host_slice(wl, "w", b)[i:i + 1][None],
                          host_slice(wl, "kidx", b)[None, : p + 1],
-                         [host_slice(wl, f"q{c}", b)[i][None, None] for c in range(wl.mla_calls)]))
+                         [host_slice(wl, wl.attn_inputs(c)[0], b)[i][None, None]
+                          for c in range(wl.attn_calls)]))
     cores = oracle.max_threads()
     t_total = 0.0
     checked, idx_equal, worst_max, worst_l2 = set(), True, 0.0, 0.0
@@ -185,27 +193,31 @@ def cpu_baseline(wl, sample_rows, gpu=None):
         sc = oracle.index_scores(qi, w, k, sl, 1)
         idx, nsel = oracle.topk_select(sc, sl, wl.topk, wl.init, wl.local)
         t_total += time.perf_counter() - t0
-        sel = idx[0, 0, : nsel[0, 0]]
-        m = sel.size
-        kvs = [host_kv_rows(wl, f"kv{c}", b, sel)[None] for c in range(wl.mla_calls)]
+        # each call's selection: the pass's, plus the positions drafted since (draft steps)
+        sels = [oracle.mtp_draft_indices(idx[:, 0], nsel[:, 0], sl, sl + wl.attn_inputs(c)[2],
+                                         wl.draft_steps)[0][0, 0] if wl.draft_steps
+                else idx[0, 0] for c in range(wl.attn_calls)]
+        sels = [s_[s_ >= 0] if wl.draft_steps else s_[: nsel[0, 0]] for s_ in sels]
+        kvs = [host_kv_rows(wl, wl.attn_inputs(c)[1], b, sels[c])[None] for c in range(wl.attn_calls)]
         t0 = time.perf_counter()
-        refs = [oracle.sparse_mla(qs[c], kvs[c], np.arange(m, dtype=np.int32)[None, None],
-                                  np.array([[m]], np.int32), np.array([m], np.int32), wl.Dv,
-                                  wl.scale)[0] for c in range(wl.mla_calls)]
+        refs = [oracle.sparse_mla(qs[c], kvs[c], np.arange(sels[c].size, dtype=np.int32)[None, None],
+                                  np.array([[sels[c].size]], np.int32),
+                                  np.array([sels[c].size], np.int32), wl.Dv, wl.scale)[0]
+                for c in range(wl.attn_calls)]
         t_total += time.perf_counter() - t0
         if gpu is not None and (b, i) not in checked:  # not timed
             checked.add((b, i))
             g_idx, g_nsel, g_outs = gpu
             idx_equal &= bool(int(g_nsel[b, i]) == int(nsel[0, 0])
                               and np.array_equal(g_idx[b, i].cpu().numpy(), idx[0, 0]))
-            for c in range(wl.mla_calls):
+            for c in range(wl.attn_calls):
                 ref = refs[c][0, 0]
                 err = g_outs[c][b, i].float().cpu().numpy().astype(np.float64) - ref
                 worst_max = max(worst_max, float(np.abs(err).max() / max(np.abs(ref).max(), 1e-300)))
                 worst_l2 = max(worst_l2, float(np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-300)))
     res = {"value": len(rows) / t_total, "unit": "queries/s", "cores": cores, "kind": "oracle",
            "sample": f"{len(rows)} query-row evaluations over the {len(every)} query rows of "
-                     f"{wl.name} (each: full indexer scan, top-k and {wl.mla_calls} MLA call(s)); "
+                     f"{wl.name} (each: full indexer scan, top-k and {wl.attn_calls} MLA call(s)); "
                      f"{t_total:.2f} s wall on {cores} threads"}
     if gpu is not None:
         res["parity_on_timed_buffers"] = {
@@ -247,11 +259,15 @@ def main():
     else:
         tws = torch.empty(max(1, lsa.lsa_topk_workspace_bytes(B, Lq, wl.S_max, wl.topk, wl.init,
                                                               wl.local)), dtype=torch.uint8, device=dev)
-    mws = torch.empty(max(1, lsa.lsa_mla_workspace_bytes(B, Lq, wl.H, wl.Dv, wl.S_max, wl.topk,
-                                                         False)), dtype=torch.uint8, device=dev)
+    if wl.draft_steps:
+        mws_bytes = lsa.lsa_mtp_draft_workspace_bytes(B, wl.H, wl.Dv, wl.S_max, wl.topk, wl.draft_steps)
+        draft_seqlens = [X["seqlens"] + c for c in range(wl.draft_steps)]
+    else:
+        mws_bytes = lsa.lsa_mla_workspace_bytes(B, Lq, wl.H, wl.Dv, wl.S_max, wl.topk, False)
+    mws = torch.empty(max(1, mws_bytes), dtype=torch.uint8, device=dev)
     outs = [torch.empty(B, Lq, wl.H, wl.Dv, dtype=torch.bfloat16, device=dev)
-            for _ in range(wl.mla_calls)]
-    lses = [torch.empty(B, Lq, wl.H, dtype=torch.float32, device=dev) for _ in range(wl.mla_calls)]
+            for _ in range(wl.attn_calls)]
+    lses = [torch.empty(B, Lq, wl.H, dtype=torch.float32, device=dev) for _ in range(wl.attn_calls)]
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
@@ -271,8 +287,13 @@ def main():
                                 n_sel=nsel, workspace=tws)
         if ev is not None:
             ev[2].record(stream)
-        for c in range(wl.mla_calls):
-            if wl.decode:
+        for c in range(wl.attn_calls):
+            if wl.draft_steps:  # draft step c on the shared index pass
+                lsa.lsa_mtp_draft_attention(X[f"q{c}"][:, 0], X["kv0"], idx[:, 0], nsel[:, 0],
+                                            X["seqlens"], draft_seqlens[c], wl.Dv, wl.scale,
+                                            max_appended=wl.draft_steps, out=outs[c][:, 0],
+                                            lse=lses[c][:, 0], workspace=mws)
+            elif wl.decode:
                 lsa.lsa_sparse_mla_decode(X[f"q{c}"][:, 0], X[f"kv{c}"], idx[:, 0], nsel[:, 0],
                                           X["seqlens"], wl.Dv, wl.scale, out=outs[c][:, 0],
                                           lse=lses[c][:, 0], workspace=mws)
@@ -307,7 +328,7 @@ def main():
     # Pass 2: the same K steps with an event at every call boundary, for the per-call durations
     # (roofline, stages) and the spread of step times.  The last stage of step s ends where step
     # s+1's first event is recorded (the same stream position).
-    n_ev = 3 + wl.mla_calls
+    n_ev = 3 + wl.attn_calls
     step_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for s in range(args.steps):
@@ -318,7 +339,7 @@ def main():
     step_list = sorted(step_ev[s][0].elapsed_time(step_ev[s + 1][0]) for s in range(args.steps - 1))
 
     ms_per_step = elapsed_ms / args.steps
-    queries = B * Lq
+    queries = B * Lq * (wl.draft_steps or 1)  # draft steps: one query per step and sequence
     value = queries * args.steps / (elapsed_ms / 1e3)
     alg, score_rt = algorithmic_bytes(wl)
     k1_bytes = fused_call_bytes(wl) if fused else indexer_bytes(wl)
@@ -387,8 +408,8 @@ def main():
     # per-stage algorithmic bytes: the indexer call as in the roofline; top-k (split path) reads
     # the visible scores and writes the indices; an attention call gathers the selected rows and
     # moves q, out and the index list
-    mla_bytes = sum(min(wl.seqlens[b] - wl.Lq + i + 1, wl.topk) * wl.Dqk * 2 + wl.H * wl.Dqk * 2
-                    + wl.H * wl.Dv * 2 + wl.topk * 4 for b in range(wl.B) for i in range(wl.Lq))
+    mla_bytes = [sum(attn_row_bytes(wl, wl.seqlens[b] - wl.Lq + i + 1, c)
+                     for b in range(wl.B) for i in range(wl.Lq)) for c in range(wl.attn_calls)]
     topk_bytes = sum((wl.seqlens[b] - wl.Lq + i + 1) * 4 + wl.topk * 4 + 4
                      for b in range(wl.B) for i in range(wl.Lq))
     # (rates only for decode: prefill rows share keys and selected rows, so per-row byte counts
@@ -399,10 +420,10 @@ def main():
     if not fused:
         stages["topk_call_ms"] = round(mean(1), 5)
         stages["topk_call_gbs"] = round(topk_bytes / (mean(1) / 1e3) / 1e9, 1)
-    for c in range(wl.mla_calls):
+    for c in range(wl.attn_calls):
         stages[f"mla{c}_call_ms"] = round(mean(2 + c), 5)
         if wl.decode:
-            stages[f"mla{c}_call_gbs"] = round(mla_bytes / (mean(2 + c) / 1e3) / 1e9, 1)
+            stages[f"mla{c}_call_gbs"] = round(mla_bytes[c] / (mean(2 + c) / 1e3) / 1e9, 1)
     # the same step with one attention call (the shape of configurations with one sub-block)
     stages["one_mla_step_ms"] = round(mean(0) + mean(1) + mean(2), 5)
     # spread of step times in pass 2 (which carries the boundary events)
@@ -434,7 +455,8 @@ def main():
         "config": {"workload": wl.name, "path": args.path, "batch": B, "context": wl.S_max, "query_tokens": Lq,
                    "index_heads": wl.Hi, "index_dim": wl.Di, "topk": wl.topk,
                    "init_tokens": wl.init, "local_tokens": wl.local, "mla_heads": wl.H,
-                   "qk_dim": wl.Dqk, "v_dim": wl.Dv, "mla_calls_per_step": wl.mla_calls},
+                   "qk_dim": wl.Dqk, "v_dim": wl.Dv, "mla_calls_per_step": wl.attn_calls,
+                   "draft_steps": wl.draft_steps},
         "roofline": roofline,
         "stages": stages,
     }

@@ -44,7 +44,9 @@ KIND_NAMES = {"dyadic": DYADIC, "weight": WEIGHT, "normal": NORMAL}
 # tensor tags
 TAGS = {"qidx": 1, "w": 2, "kidx": 3, "q": 4, "kv0": 5, "kv1": 6, "q1": 7, "scores": 8,
         # indexer front end: q-LoRA representation, hidden state, projections, key-norm gain
-        "cq": 9, "hid": 10, "wq_b": 11, "wk": 12, "w_proj": 13, "k_gain": 14}
+        "cq": 9, "hid": 10, "wq_b": 11, "wk": 12, "w_proj": 13, "k_gain": 14,
+        # third multi-token-prediction draft query
+        "q2": 15}
 
 NORMAL_SCALE = 1.0 / math.sqrt(4.0 * (65536.0 * 65536.0 - 1.0) / 12.0)
 

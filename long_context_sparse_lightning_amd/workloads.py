@@ -35,6 +35,9 @@ class Workload:
     Dv: int = 512
     scale: float = 1.0 / math.sqrt(192.0)
     mla_calls: int = 1
+    # multi-token-prediction draft steps on one index pass (0: none).  Draft step c runs at
+    # length seqlens[b] + c on cache kv0 with its own query q{c}.
+    draft_steps: int = 0
     seed: int = 1000
     notes: str = field(default="", compare=False)
 
@@ -45,6 +48,15 @@ class Workload:
     @property
     def decode(self) -> bool:
         return self.Lq == 1
+
+    @property
+    def attn_calls(self) -> int:
+        """Attention calls per step (draft steps share one cache; sub-blocks have their own)."""
+        return self.draft_steps or self.mla_calls
+
+    def attn_inputs(self, c: int):
+        """(query, cache, positions appended since the index pass) of attention call c."""
+        return f"q{c}", ("kv0" if self.draft_steps else f"kv{c}"), (c if self.draft_steps else 0)
 
 
 def _wl(name, B, S, Lq=1, seqlens=None, **kw):
@@ -64,6 +76,10 @@ WORKLOADS = {
     "decode_128k": _wl("decode_128k", 32, 131072, mla_calls=2, seed=1002),
     "prefill_128k": _wl("prefill_128k", 1, 131072, Lq=4096, seed=1003),
     "decode_1m": _wl("decode_1m", 4, 983040, seed=1004),
+    # multi-token prediction: one index pass at 131070 tokens serves three draft steps (lengths
+    # 131070, 131071, 131072), each attending to the selection plus the tokens drafted since
+    "mtp_decode_128k": _wl("mtp_decode_128k", 32, 131072, seqlens=[131070] * 32, draft_steps=3,
+                           seed=1005),
 }
 
 
@@ -79,6 +95,8 @@ def tensor_specs(wl: Workload):
     if wl.mla_calls > 1:
         specs["q1"] = (gen.TAGS["q1"], (wl.B, wl.Lq, wl.H, wl.Dqk), gen.NORMAL)
         specs["kv1"] = (gen.TAGS["kv1"], (wl.B, wl.S_max, wl.Dqk), gen.NORMAL)
+    for c in range(1, wl.draft_steps):
+        specs[f"q{c}"] = (gen.TAGS[f"q{c}"], (wl.B, wl.Lq, wl.H, wl.Dqk), gen.NORMAL)
     return specs
 
 

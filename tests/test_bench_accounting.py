@@ -24,6 +24,17 @@ def test_decode_128k_bytes():
     assert score_rt == 32 * 2 * 131072 * 4
 
 
+def test_mtp_decode_128k_bytes():
+    wl = WORKLOADS["mtp_decode_128k"]
+    assert wl.attn_calls == 3 and [wl.attn_inputs(c) for c in range(3)] == [
+        ("q0", "kv0", 0), ("q1", "kv0", 1), ("q2", "kv0", 2)]
+    # one index pass over 131070 keys, then draft step c gathers 2048 + c latent rows
+    n = 131070
+    per_draft = lambda c: (2048 + c) * 1152 + 32 * 1152 + 32 * 1024 + 2048 * 4
+    alg, _ = bench.algorithmic_bytes(wl)
+    assert alg == 32 * (n * 256 + 8192 + 128 + 2048 * 4 + sum(per_draft(c) for c in range(3)))
+
+
 def test_prefill_128k_flops():
     wl = WORKLOADS["prefill_128k"]
     # query i of 4096 sees 126976 + i + 1 keys
