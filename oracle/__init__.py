@@ -49,6 +49,8 @@ def lib():
         L.lsa_oracle_index_frontend.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I,
                                                 ctypes.c_double, ctypes.c_double, P, P, P]
         L.lsa_oracle_index_frontend.restype = I
+        L.lsa_oracle_hier_topk.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, I, P, P]
+        L.lsa_oracle_hier_topk.restype = I
         L.lsa_oracle_set_threads.argtypes = [I]
         L.lsa_oracle_max_threads.restype = I
         _lib = L
@@ -124,6 +126,28 @@ def sparse_mla(q, kv, indices, n_sel, seqlens, Dv: int, scale: float):
     if rc != 0:
         raise ValueError(f"lsa_oracle_sparse_mla: bad input ({rc})")
     return out, lse
+
+
+def hier_topk(q_idx, w, k_idx, seqlens, topk: int, init_tokens: int, local_tokens: int, Bk: int,
+              M: int):
+    """Hierarchical indexing of decode rows (see lsa_oracle_hier_topk): q_idx bf16 bits
+    [B,Hi,Di], w f32 [B,Hi], k_idx bf16 bits [B,S_max,Di] -> (indices int32 [B,topk] ascending,
+    -1 padded; n_sel int32 [B])."""
+    q_idx = _c(q_idx, np.uint16)
+    w = _c(w, np.float32)
+    k_idx = _c(k_idx, np.uint16)
+    seqlens = _c(seqlens, np.int32)
+    B, Hi, Di = q_idx.shape
+    S_max = k_idx.shape[1]
+    assert w.shape == (B, Hi) and k_idx.shape == (B, S_max, Di)
+    idx = np.empty((B, topk), dtype=np.int32)
+    nsel = np.empty(B, dtype=np.int32)
+    rc = lib().lsa_oracle_hier_topk(q_idx.ctypes.data, w.ctypes.data, k_idx.ctypes.data,
+                                    seqlens.ctypes.data, B, Hi, Di, S_max, topk, init_tokens,
+                                    local_tokens, Bk, M, idx.ctypes.data, nsel.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"lsa_oracle_hier_topk: bad input ({rc})")
+    return idx, nsel
 
 
 def mtp_draft_indices(indices, n_sel, index_seqlens, seqlens, max_appended: int):

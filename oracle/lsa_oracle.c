@@ -27,6 +27,10 @@
  *  - scores are rounded once to fp32, and the selection ranks the fp32 values;
  *  - a latent row is [latent (Dv values) | rope]; the value vector is its first Dv entries.
  *
+ * Hierarchical indexing (lsa_oracle_hier_topk, at the end of this file) follows the LSA page's
+ * "分层索引"; its block size and block score are readings listed with the function, and its
+ * parity against the pages is unpinned.
+ *
  * The indexer front end (lsa_oracle_index_frontend, at the end of this file) follows page 1's
  * "LSA" description of wq_b, wk with RMS normalisation and weights_proj, with the attention's
  * rotary settings; its readings are listed with the function.
@@ -333,4 +337,111 @@ int lsa_oracle_index_frontend(const uint16_t* cq, const uint16_t* hid, const uin
     }
   }
   return (bad & 1) ? -1 : 0;
+}
+
+/*
+ * Hierarchical indexing (page "LongCat Sparse Attention技术深度解析", section on LSA's three
+ * strategies, "分层索引": a coarse block-level score first, then the token selection inside the
+ * chosen blocks, which shrinks the candidates the indexer scores).  The page gives no block size
+ * and no block score; the readings taken here:
+ *  - block j of sequence b is tokens [j*Bk, (j+1)*Bk); its key is the mean of their index keys,
+ *    rounded once to bf16 (round to nearest even);
+ *  - a block is scored like a token, I_j = sum_h w[h] * max(0, q[h] . key_j) (fp64, rounded
+ *    once to fp32);
+ *  - the blocks scored are the nb = w0 / Bk complete blocks before the sliding window, which
+ *    starts at w0 = max(p - local + 1, 0); the M best are kept (larger score first, then the
+ *    lower block), all of them when nb <= M;
+ *  - candidates: the sink (s < init), every position from nb*Bk on (the partial block before the
+ *    window and the window), and the tokens of the kept blocks; the other tokens get the score
+ *    -inf; then the selection of lsa_oracle_topk (dense fallback when n <= topk, sink and window
+ *    forced, larger key first, then the lower position).
+ * Decode rows only (one query per sequence, at p = seqlens[b] - 1).
+ * q_idx: bf16 [B, Hi, Di]; w: fp32 [B, Hi]; k_idx: bf16 [B, S_max, Di]; indices: int32
+ * [B, topk] ascending, padded with -1; n_sel: int32 [B].
+ * Returns 0, -1 on a bad position, -2 on bad sizes.
+ */
+static uint16_t bf16_round(double x) {
+  /* round x to 8 significant bits, nearest even (the default rounding mode), then take the
+     top half of the fp32 pattern (exact: the value has at most 8 significant bits) */
+  if (x == 0.0) return 0;
+  int e;
+  double m = frexp(x, &e); /* x = m * 2^e, 0.5 <= |m| < 1 */
+  float f = (float)ldexp(nearbyint(ldexp(m, 8)), e - 8);
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(u >> 16);
+}
+
+static double weighted_relu_score(const uint16_t* q, const float* w, const uint16_t* k, int Hi, int Di) {
+  double total = 0.0;
+  for (int h = 0; h < Hi; ++h) {
+    double g = 0.0;
+    for (int d = 0; d < Di; ++d) g += bf16_value(q[(long)h * Di + d]) * bf16_value(k[d]);
+    total += (double)w[h] * (g > 0.0 ? g : 0.0);
+  }
+  return (double)(float)total;
+}
+
+int lsa_oracle_hier_topk(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+                         const int32_t* seqlens, int B, int Hi, int Di, int S_max, int topk,
+                         int init_tokens, int local_tokens, int Bk, int M, int32_t* indices,
+                         int32_t* n_sel) {
+  if (Bk <= 0 || M < 0 || init_tokens < 0 || local_tokens < 0 || init_tokens + local_tokens > topk)
+    return -2;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int b = 0; b < B; ++b) {
+    long p = (long)seqlens[b] - 1, n = p + 1;
+    int32_t* out = indices + (long)b * topk;
+    if (p < 0 || p >= S_max) {
+      bad |= 1;
+      continue;
+    }
+    for (int j = 0; j < topk; ++j) out[j] = -1;
+    if (n <= topk) {
+      for (long s = 0; s < n; ++s) out[s] = (int32_t)s;
+      n_sel[b] = (int32_t)n;
+      continue;
+    }
+    const uint16_t* qr = q_idx + (long)b * Hi * Di;
+    const float* wr = w + (long)b * Hi;
+    const uint16_t* kb = k_idx + (long)b * S_max * Di;
+    long w0 = p - local_tokens + 1;
+    if (w0 < 0) w0 = 0;
+    long nb = w0 / Bk;
+    /* stage 1: block keys and block scores, the M best blocks kept */
+    ranked_t* blocks = (ranked_t*)malloc(sizeof(ranked_t) * (size_t)(nb > 0 ? nb : 1));
+    uint16_t* key = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)Di);
+    for (long j = 0; j < nb; ++j) {
+      for (int d = 0; d < Di; ++d) {
+        double s = 0.0;
+        for (int t = 0; t < Bk; ++t) s += bf16_value(kb[(j * Bk + t) * (long)Di + d]);
+        key[d] = bf16_round(s / Bk);
+      }
+      blocks[j].key = weighted_relu_score(qr, wr, key, Hi, Di);
+      blocks[j].pos = (int32_t)j;
+    }
+    qsort(blocks, (size_t)nb, sizeof(ranked_t), cmp_rank);
+    char* kept = (char*)calloc((size_t)(nb > 0 ? nb : 1), 1);
+    for (long j = 0; j < nb && j < M; ++j) kept[blocks[j].pos] = 1;
+    /* stage 2: token keys over the candidates, -inf elsewhere; sink and window forced */
+    ranked_t* all = (ranked_t*)malloc(sizeof(ranked_t) * (size_t)n);
+    for (long s = 0; s < n; ++s) {
+      int forced = (s < init_tokens) || (s > p - local_tokens);
+      int cand = s < init_tokens || s >= nb * Bk || kept[s / Bk];
+      all[s].key = forced ? INFINITY
+                   : cand ? weighted_relu_score(qr, wr, kb + s * (long)Di, Hi, Di)
+                          : -INFINITY;
+      all[s].pos = (int32_t)s;
+    }
+    qsort(all, (size_t)n, sizeof(ranked_t), cmp_rank);
+    for (int j = 0; j < topk; ++j) out[j] = all[j].pos;
+    qsort(out, (size_t)topk, sizeof(int32_t), cmp_int);
+    n_sel[b] = topk;
+    free(all);
+    free(kept);
+    free(key);
+    free(blocks);
+  }
+  return bad ? -1 : 0;
 }
