@@ -213,6 +213,51 @@ lsa_status lsa_mtp_draft_attention(const void* q, const void* kv, const int32_t*
                                    void* out, float* lse, void* workspace, size_t workspace_bytes,
                                    void* stream);
 
+/*
+ * Block keys for hierarchical indexing (page "LongCat Sparse Attention技术深度解析", section on
+ * LSA's three strategies, "分层索引": block-level approximate scores come first, then the token
+ * selection inside the chosen blocks).  The page gives no block size or block key; here block j
+ * of sequence b is tokens [j*Bk, (j+1)*Bk) and its key is the mean of their index keys, rounded
+ * once to bf16 (round to nearest even; the sum is taken in fp32, exact for keys on a coarse
+ * dyadic grid).  Writes block_keys[b, j, :] for first_block <= j < seqlens[b] / Bk (complete
+ * blocks only), so a cache that grows can be summarised block by block.
+ *   k_idx       bf16 [B, S_max, Di] index-key cache
+ *   block_keys  bf16 [B, S_max / Bk, Di] (caller-owned; other rows are not touched)
+ * Supported: Bk a power of two in [8, 1024], Bk <= S_max; Di a multiple of 16, <= 128.
+ * Errors: NULL pointers (B > 0) -> LSA_ERR_NULL_ARG; bad sizes -> LSA_ERR_BAD_SHAPE /
+ * LSA_ERR_UNSUPPORTED.
+ */
+lsa_status lsa_block_keys(const void* k_idx, const int32_t* seqlens, int B, int S_max, int Di,
+                          int Bk, int first_block, void* block_keys, void* stream);
+
+/* Workspace (bytes) lsa_hier_index_topk needs for these sizes (0 for invalid sizes). */
+size_t lsa_hier_workspace_bytes(int B, int S_max, int Bk, int topk, int init_tokens,
+                                int local_tokens, int M);
+
+/*
+ * Hierarchical indexer + top-k for decode rows ("分层索引", same page): for the query at
+ * p = seqlens[b] - 1 (n = p + 1 visible keys):
+ *  - n <= topk: every position (the dense fallback of lsa_topk_select);
+ *  - else the nb = w0 / Bk complete blocks before the sliding window (w0 = max(p - local + 1, 0))
+ *    are scored like keys, I_j = sum_h w[b,h] * max(0, q_idx[b,h,:] . block_keys[b,j,:]), and
+ *    the M best kept (larger score, then lower block; all when nb <= M);
+ *  - tokens outside the sink [0, init), the positions from nb*Bk on (the partial block and the
+ *    window) and the kept blocks get the score -inf; the others their indexer score; then the
+ *    selection of lsa_topk_select (sink and window forced, ties to the lower position).
+ * This is an approximation of lsa_index_topk (exact when M >= nb); with M*Bk well above
+ * topk - init - local it reads about (nb + M*Bk) keys instead of n.
+ *   q_idx bf16 [B, Hi, Di]; w fp32 [B, Hi]; k_idx bf16 [B, S_max, Di]; block_keys from
+ *   lsa_block_keys (complete for every block below seqlens[b] / Bk); indices int32 [B, topk]
+ *   ascending, -1 padded; n_sel int32 [B].
+ * Supported: Hi <= 32, Di a multiple of 16 and <= 128, Bk a power of two in [8, 1024],
+ * 1 <= M <= S_max / Bk, and the sizes lsa_topk_select takes.  Errors as lsa_index_topk.
+ */
+lsa_status lsa_hier_index_topk(const void* q_idx, const float* w, const void* k_idx,
+                               const void* block_keys, const int32_t* seqlens, int B, int Hi,
+                               int Di, int S_max, int topk, int init_tokens, int local_tokens,
+                               int Bk, int M, int32_t* indices, int32_t* n_sel, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* Workspace (bytes) lsa_index_frontend needs for these sizes (0 for invalid sizes). */
 size_t lsa_index_frontend_workspace_bytes(int B, int Lq, int q_lora, int hidden, int Hi, int Di);
 

@@ -31,7 +31,8 @@ COMMON_FLAGS = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
-LSA_SOURCES = ["lsa_api.hip", "lsa_indexer.hip", "lsa_topk.hip", "lsa_mla.hip", "lsa_frontend.hip"]
+LSA_SOURCES = ["lsa_api.hip", "lsa_indexer.hip", "lsa_topk.hip", "lsa_mla.hip", "lsa_frontend.hip",
+               "lsa_hier.hip"]
 GEN_SOURCES = ["lsa_gen.hip"]
 
 

@@ -142,6 +142,77 @@ lsa_status lsa_index_topk(const void* q_idx, const float* w, const void* k_idx,
                   "lsa_index_topk");
 }
 
+static bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
+
+static lsa_status check_blocks(const char* fn, int B, int S_max, int Di, int Bk) {
+  if (B < 0 || S_max <= 0 || Di <= 0)
+    return fail(LSA_ERR_BAD_SHAPE, "%s: B=%d S_max=%d Di=%d", fn, B, S_max, Di);
+  if (!pow2_in(Bk, 8, 1024) || Bk > S_max)
+    return fail(LSA_ERR_UNSUPPORTED, "%s: Bk=%d must be a power of two in [8, 1024], <= S_max=%d", fn,
+                Bk, S_max);
+  if (Di % 16 || Di > 128) return fail(LSA_ERR_UNSUPPORTED, "%s: Di=%d not a multiple of 16 <= 128", fn, Di);
+  return LSA_OK;
+}
+
+lsa_status lsa_block_keys(const void* k_idx, const int32_t* seqlens, int B, int S_max, int Di,
+                          int Bk, int first_block, void* block_keys, void* stream) {
+  const char* fn = "lsa_block_keys";
+  lsa_status st = check_blocks(fn, B, S_max, Di, Bk);
+  if (st != LSA_OK) return st;
+  if (first_block < 0) return fail(LSA_ERR_BAD_SHAPE, "%s: first_block=%d < 0", fn, first_block);
+  if (B == 0) return ok();
+  if (!k_idx || !seqlens || !block_keys) return fail(LSA_ERR_NULL_ARG, "%s: NULL k_idx/seqlens/block_keys", fn);
+  return launched(lsa::launch_block_keys(static_cast<const uint16_t*>(k_idx), seqlens, B, S_max, Di, Bk,
+                                         first_block, static_cast<uint16_t*>(block_keys),
+                                         static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+static lsa_status check_hier(int B, int S_max, int topk, int init_tokens, int local_tokens, int Bk,
+                             int M) {
+  const char* fn = "lsa_hier_index_topk";
+  lsa_status st = check_topk(B, 1, S_max, topk, init_tokens, local_tokens);
+  if (st != LSA_OK) return st;
+  if (!pow2_in(Bk, 8, 1024) || Bk > S_max)
+    return fail(LSA_ERR_UNSUPPORTED, "%s: Bk=%d must be a power of two in [8, 1024], <= S_max=%d", fn,
+                Bk, S_max);
+  if (M < 1 || M > S_max / Bk)
+    return fail(LSA_ERR_BAD_SHAPE, "%s: M=%d outside [1, S_max / Bk = %d]", fn, M, S_max / Bk);
+  return LSA_OK;
+}
+
+size_t lsa_hier_workspace_bytes(int B, int S_max, int Bk, int topk, int init_tokens,
+                                int local_tokens, int M) {
+  if (B <= 0 || check_hier(B, S_max, topk, init_tokens, local_tokens, Bk, M) != LSA_OK) return 0;
+  return lsa::hier_workspace_bytes(B, S_max, Bk, topk, init_tokens, local_tokens, M);
+}
+
+lsa_status lsa_hier_index_topk(const void* q_idx, const float* w, const void* k_idx,
+                               const void* block_keys, const int32_t* seqlens, int B, int Hi,
+                               int Di, int S_max, int topk, int init_tokens, int local_tokens,
+                               int Bk, int M, int32_t* indices, int32_t* n_sel, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  const char* fn = "lsa_hier_index_topk";
+  lsa_status st = check_hier(B, S_max, topk, init_tokens, local_tokens, Bk, M);
+  if (st != LSA_OK) return st;
+  if (Hi <= 0 || Hi > lsa::hier_max_heads() || Di <= 0 || Di % 16 || Di > 128)
+    return fail(LSA_ERR_UNSUPPORTED, "%s: Hi=%d (<= %d) Di=%d (multiple of 16, <= 128)", fn, Hi,
+                lsa::hier_max_heads(), Di);
+  if (B == 0) return ok();
+  if (!q_idx || !w || !k_idx || !block_keys || !seqlens || !indices || !n_sel)
+    return fail(LSA_ERR_NULL_ARG, "%s: NULL input or output", fn);
+  const size_t need = lsa::hier_workspace_bytes(B, S_max, Bk, topk, init_tokens, local_tokens, M);
+  if (!workspace || workspace_bytes < need)
+    return fail(LSA_ERR_WORKSPACE, "%s: workspace %zu bytes at %p, need %zu", fn, workspace_bytes,
+                workspace, need);
+  return launched(lsa::launch_hier_index_topk(static_cast<const uint16_t*>(q_idx), w,
+                                              static_cast<const uint16_t*>(k_idx),
+                                              static_cast<const uint16_t*>(block_keys), seqlens, B,
+                                              Hi, Di, S_max, topk, init_tokens, local_tokens, Bk, M,
+                                              indices, n_sel, workspace, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
 static lsa_status check_mla(const char* fn, int B, int Lq, int H, int Dqk, int Dv, int S_max, int topk,
                             bool dense, float softmax_scale) {
   if (B < 0 || Lq < 0) return fail(LSA_ERR_BAD_SHAPE, "%s: B=%d Lq=%d must be >= 0", fn, B, Lq);

@@ -164,6 +164,17 @@ hipError_t launch_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indi
                       void* workspace, hipStream_t stream, const int32_t* index_seqlens = nullptr,
                       int max_app = 0);
 
+// Hierarchical indexing: block-mean keys, block scores, the kept blocks' token selection.
+int hier_max_heads();
+size_t hier_workspace_bytes(int B, int S_max, int Bk, int topk, int init, int local, int M);
+hipError_t launch_block_keys(const uint16_t* k_idx, const int32_t* seqlens, int B, int S_max, int Di,
+                             int Bk, int first_block, uint16_t* block_keys, hipStream_t stream);
+hipError_t launch_hier_index_topk(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+                                  const uint16_t* block_keys, const int32_t* seqlens, int B, int Hi,
+                                  int Di, int S_max, int topk, int init, int local, int Bk, int M,
+                                  int32_t* indices, int32_t* n_sel, void* workspace,
+                                  hipStream_t stream);
+
 // Indexer front end: index queries, head weights and the new keys of the current tokens.
 int frontend_max_rot();
 size_t frontend_workspace_bytes(int B, int Lq, int q_lora, int hidden, int Hi, int Di);

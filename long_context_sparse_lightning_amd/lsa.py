@@ -23,7 +23,8 @@ EXPORTED = ["lsa_status_str", "lsa_last_error", "lsa_index_scores", "lsa_topk_wo
             "lsa_topk_select", "lsa_index_topk_workspace_bytes", "lsa_index_topk",
             "lsa_mla_workspace_bytes", "lsa_sparse_mla_decode", "lsa_sparse_mla_prefill",
             "lsa_index_frontend_workspace_bytes", "lsa_index_frontend",
-            "lsa_mtp_draft_workspace_bytes", "lsa_mtp_draft_attention"]
+            "lsa_mtp_draft_workspace_bytes", "lsa_mtp_draft_attention", "lsa_block_keys",
+            "lsa_hier_workspace_bytes", "lsa_hier_index_topk"]
 
 
 class LsaError(RuntimeError):
@@ -73,6 +74,12 @@ def lib():
         L.lsa_mtp_draft_workspace_bytes.restype = Z
         L.lsa_mtp_draft_attention.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, F, P, P, P, Z, P]
         L.lsa_mtp_draft_attention.restype = I
+        L.lsa_block_keys.argtypes = [P, P, I, I, I, I, I, P, P]
+        L.lsa_block_keys.restype = I
+        L.lsa_hier_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+        L.lsa_hier_workspace_bytes.restype = Z
+        L.lsa_hier_index_topk.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, P, P, Z, P]
+        L.lsa_hier_index_topk.restype = I
         _lib = L
     return _lib
 
@@ -259,6 +266,57 @@ def lsa_mtp_draft_attention(q, kv, indices, n_sel, index_seqlens, seqlens, Dv, s
                                          topk, int(max_appended), float(softmax_scale), _ptr(out),
                                          _ptr(lse), _ptr(workspace), wbytes, _stream(q)))
     return out
+
+
+def lsa_block_keys(k_idx, seqlens, Bk, block_keys=None, first_block=0):
+    """k_idx bf16 [B,S_max,Di], seqlens i32 [B] -> block_keys bf16 [B,S_max//Bk,Di] (rows
+    first_block .. seqlens[b]//Bk - 1 written: the bf16 means of complete blocks of Bk keys)."""
+    _want(k_idx, "k_idx", torch.bfloat16, 3)
+    _want(seqlens, "seqlens", torch.int32, 1)
+    B, S_max, Di = k_idx.shape
+    if block_keys is None:
+        block_keys = torch.zeros(B, S_max // Bk, Di, dtype=torch.bfloat16, device=k_idx.device)
+    _want(block_keys, "block_keys", torch.bfloat16, 3)
+    if block_keys.shape != (B, S_max // Bk, Di) or seqlens.shape[0] != B:
+        raise ValueError("lsa_block_keys: inconsistent shapes")
+    _check(lib().lsa_block_keys(_ptr(k_idx), _ptr(seqlens), B, S_max, Di, int(Bk), int(first_block),
+                                _ptr(block_keys), _stream(k_idx)))
+    return block_keys
+
+
+def lsa_hier_workspace_bytes(B, S_max, Bk, topk, init_tokens, local_tokens, M) -> int:
+    return int(lib().lsa_hier_workspace_bytes(B, S_max, Bk, topk, init_tokens, local_tokens, M))
+
+
+def lsa_hier_index_topk(q_idx, w, k_idx, block_keys, seqlens, topk, init_tokens, local_tokens, Bk,
+                        M, indices=None, n_sel=None, workspace=None):
+    """Hierarchical indexer + top-k of decode rows: q_idx bf16 [B,Hi,Di], w f32 [B,Hi], k_idx
+    bf16 [B,S_max,Di], block_keys bf16 [B,S_max//Bk,Di] (lsa_block_keys) -> (indices i32
+    [B,topk], n_sel i32 [B])."""
+    _want(q_idx, "q_idx", torch.bfloat16, 3)
+    _want(w, "w", torch.float32, 2)
+    _want(k_idx, "k_idx", torch.bfloat16, 3)
+    _want(block_keys, "block_keys", torch.bfloat16, 3)
+    _want(seqlens, "seqlens", torch.int32, 1)
+    B, Hi, Di = q_idx.shape
+    S_max = k_idx.shape[1]
+    if w.shape != (B, Hi) or k_idx.shape != (B, S_max, Di) or seqlens.shape[0] != B \
+            or block_keys.shape != (B, S_max // Bk, Di):
+        raise ValueError("lsa_hier_index_topk: inconsistent shapes")
+    dev = q_idx.device
+    if indices is None:
+        indices = torch.empty(B, topk, dtype=torch.int32, device=dev)
+    if n_sel is None:
+        n_sel = torch.empty(B, dtype=torch.int32, device=dev)
+    need = lsa_hier_workspace_bytes(B, S_max, Bk, topk, init_tokens, local_tokens, M)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().lsa_hier_index_topk(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(block_keys),
+                                     _ptr(seqlens), B, Hi, Di, S_max, topk, init_tokens, local_tokens,
+                                     int(Bk), int(M), _ptr(indices), _ptr(n_sel), _ptr(workspace),
+                                     wbytes, _stream(q_idx)))
+    return indices, n_sel
 
 
 def lsa_index_frontend_workspace_bytes(B, Lq, q_lora, hidden, Hi, Di) -> int:

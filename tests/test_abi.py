@@ -114,6 +114,28 @@ def test_mla_argument_errors_and_workspace():
     assert L.lsa_mla_workspace_bytes(1, 4096, 32, 512, 131072, 2048, 0) == 0
 
 
+def test_hierarchical_argument_errors_and_workspace():
+    L = lsa.lib()
+    p = ctypes.c_void_p(16)
+    bk = L.lsa_block_keys
+    assert bk(p, p, 2, 4096, 128, 48, 0, p, None) == 3  # not a power of two
+    assert bk(p, p, 2, 4096, 128, 4, 0, p, None) == 3 and bk(p, p, 2, 4096, 128, 2048, 0, p, None) == 3
+    assert bk(p, p, 2, 4096, 120, 64, 0, p, None) == 3 and bk(p, p, 2, 32, 128, 64, 0, p, None) == 3
+    assert bk(p, p, 2, 4096, 128, 64, -1, p, None) == 2 and bk(p, None, 2, 4096, 128, 64, 0, p, None) == 1
+    h = L.lsa_hier_index_topk
+
+    def call(Hi=32, Di=128, topk=2048, init=16, local=1024, Bk=64, M=32, bk_=p, ws=p, wbytes=1 << 30):
+        return h(p, p, p, bk_, p, 4, Hi, Di, 131072, topk, init, local, Bk, M, p, p, ws, wbytes, None)
+
+    assert call(Hi=33) == 3 and call(Di=120) == 3 and call(Bk=96) == 3
+    assert call(M=0) == 2 and call(M=2049) == 2 and call(init=1500) == 2
+    assert call(bk_=None) == 1
+    need = L.lsa_hier_workspace_bytes(4, 131072, 64, 2048, 16, 1024, 32)
+    assert 0 < need < 16 << 20
+    assert call(wbytes=need - 1) == 4 and call(ws=None, wbytes=0) == 4
+    assert L.lsa_hier_workspace_bytes(4, 131072, 64, 2048, 16, 1024, 0) == 0
+
+
 def test_index_frontend_argument_errors_and_workspace():
     L = lsa.lib()
     p = ctypes.c_void_p(16)
