@@ -59,10 +59,21 @@ def algorithmic_bytes(wl):
     for b in range(wl.B):
         for i in range(wl.Lq):
             n = wl.seqlens[b] - wl.Lq + i + 1
-            tot += n * wl.Di * 2 + wl.Hi * wl.Di * 2 + wl.Hi * 4 + wl.topk * 4
+            tot += index_keys_read(wl, n) * wl.Di * 2 + wl.Hi * wl.Di * 2 + wl.Hi * 4 + wl.topk * 4
             tot += sum(attn_row_bytes(wl, n, c) for c in range(wl.attn_calls))
             score_rt += 2 * n * 4
     return tot, score_rt
+
+
+def index_keys_read(wl, n):
+    """Key rows the index pass of a row with n visible positions must read: all n, or with
+    hierarchical indexing the block keys before the window plus the tokens scored (the kept
+    blocks and the partial block before the window; the sink and window are forced)."""
+    if not wl.hier_block or n <= wl.topk:
+        return n if not wl.hier_block else 0
+    w0 = max(n - wl.local, 0)
+    nb = w0 // wl.hier_block
+    return nb + min(wl.hier_keep, nb) * wl.hier_block + (w0 - nb * wl.hier_block)
 
 
 def attn_row_bytes(wl, n, c):
@@ -95,6 +106,13 @@ def query_blocked(wl):
     """True when lsa_index_scores runs the query-blocked scan for this shape (16 query rows per
     workgroup share each key tile; a dense contraction, bound by the matrix cores)."""
     return wl.Di == 128 and wl.Lq >= 16
+
+
+def hier_call_bytes(wl):
+    """Algorithmic bytes of one lsa_hier_index_topk call: the block keys and token keys it must
+    score, the index query and weights, the indices and n_sel."""
+    return sum(index_keys_read(wl, wl.seqlens[b]) * wl.Di * 2 + wl.Hi * wl.Di * 2 + wl.Hi * 4
+               + wl.topk * 4 + 4 for b in range(wl.B))
 
 
 def fused_call_bytes(wl):
@@ -190,8 +208,13 @@ def cpu_baseline(wl, sample_rows, gpu=None):
         n = p + 1
         sl = np.array([n], np.int32)
         t0 = time.perf_counter()
-        sc = oracle.index_scores(qi, w, k, sl, 1)
-        idx, nsel = oracle.topk_select(sc, sl, wl.topk, wl.init, wl.local)
+        if wl.hier_block:
+            hi, hn = oracle.hier_topk(qi[:, 0], w[:, 0], k, sl, wl.topk, wl.init, wl.local,
+                                      wl.hier_block, wl.hier_keep)
+            idx, nsel = hi[:, None], hn[:, None]
+        else:
+            sc = oracle.index_scores(qi, w, k, sl, 1)
+            idx, nsel = oracle.topk_select(sc, sl, wl.topk, wl.init, wl.local)
         t_total += time.perf_counter() - t0
         # each call's selection: the pass's, plus the positions drafted since (draft steps)
         sels = [oracle.mtp_draft_indices(idx[:, 0], nsel[:, 0], sl, sl + wl.attn_inputs(c)[2],
@@ -242,18 +265,36 @@ def main():
     from long_context_sparse_lightning_amd.workloads import WORKLOADS, device_inputs
 
     wl = WORKLOADS[args.workload]
-    if args.path is None:
+    if wl.hier_block:
+        args.path = "hier"
+    elif args.path is None:
         args.path = "fused" if wl.decode else "split"
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     X = device_inputs(wl, device=dev)
     B, Lq = wl.B, wl.Lq
-    scores = None if args.path == "fused" else torch.empty(B, Lq, wl.S_max, dtype=torch.float32,
+    scores = None if args.path in ("fused", "hier") else torch.empty(B, Lq, wl.S_max, dtype=torch.float32,
                                                              device=dev)
     idx = torch.empty(B, Lq, wl.topk, dtype=torch.int32, device=dev)
     nsel = torch.empty(B, Lq, dtype=torch.int32, device=dev)
     fused = args.path == "fused"
-    if fused:
+    hier = args.path == "hier"
+    if hier:
+        # the block summary of the cache: built once here, maintained block by block as a cache
+        # grows (one block completes every hier_block decode steps)
+        bkeys = torch.zeros(B, wl.S_max // wl.hier_block, wl.Di, dtype=torch.bfloat16, device=dev)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        lsa.lsa_block_keys(X["kidx"], X["seqlens"], wl.hier_block, block_keys=bkeys)
+        torch.cuda.synchronize()
+        ev0.record()
+        lsa.lsa_block_keys(X["kidx"], X["seqlens"], wl.hier_block, block_keys=bkeys)
+        ev1.record()
+        torch.cuda.synchronize()
+        block_keys_ms = ev0.elapsed_time(ev1)
+        tws = torch.empty(lsa.lsa_hier_workspace_bytes(B, wl.S_max, wl.hier_block, wl.topk, wl.init,
+                                                       wl.local, wl.hier_keep), dtype=torch.uint8,
+                          device=dev)
+    elif fused:
         tws = torch.empty(max(1, lsa.lsa_index_topk_workspace_bytes(B, Lq, wl.S_max, wl.topk, wl.init,
                                                                     wl.local)), dtype=torch.uint8, device=dev)
     else:
@@ -275,14 +316,18 @@ def main():
         # [start, after the indexer call, after top-k, after each attention call]
         if ev is not None:
             ev[0].record(stream)
-        if fused:
+        if hier:
+            lsa.lsa_hier_index_topk(X["qidx"][:, 0], X["w"][:, 0], X["kidx"], bkeys, X["seqlens"],
+                                    wl.topk, wl.init, wl.local, wl.hier_block, wl.hier_keep,
+                                    indices=idx[:, 0], n_sel=nsel[:, 0], workspace=tws)
+        elif fused:
             lsa.lsa_index_topk(X["qidx"], X["w"], X["kidx"], X["seqlens"], wl.topk, wl.init,
                                wl.local, indices=idx, n_sel=nsel, workspace=tws)
         else:
             lsa.lsa_index_scores(X["qidx"], X["w"], X["kidx"], X["seqlens"], scores=scores)
         if ev is not None:
             ev[1].record(stream)
-        if not fused:
+        if not fused and not hier:
             lsa.lsa_topk_select(scores, X["seqlens"], wl.topk, wl.init, wl.local, indices=idx,
                                 n_sel=nsel, workspace=tws)
         if ev is not None:
@@ -338,14 +383,37 @@ def main():
     k1_ms = sum(st[0] for st in stage_ms) / args.steps
     step_list = sorted(step_ev[s][0].elapsed_time(step_ev[s + 1][0]) for s in range(args.steps - 1))
 
+    recall = None
+    if hier:
+        # share of the exact selection (lsa_index_topk on the same inputs) the hierarchical one
+        # keeps; synthetic keys have no block structure, so this is a floor
+        e_idx, _ = lsa.lsa_index_topk(X["qidx"], X["w"], X["kidx"], X["seqlens"], wl.topk, wl.init,
+                                      wl.local)
+        torch.cuda.synchronize()
+        hits = sum(len(set(idx[b, 0].tolist()) & set(e_idx[b, 0].tolist())) for b in range(B))
+        recall = round(hits / (B * wl.topk), 4)
+
     ms_per_step = elapsed_ms / args.steps
     queries = B * Lq * (wl.draft_steps or 1)  # draft steps: one query per step and sequence
     value = queries * args.steps / (elapsed_ms / 1e3)
     alg, score_rt = algorithmic_bytes(wl)
-    k1_bytes = fused_call_bytes(wl) if fused else indexer_bytes(wl)
+    k1_bytes = (hier_call_bytes(wl) if hier else fused_call_bytes(wl) if fused
+                else indexer_bytes(wl))
     k1_gbs = k1_bytes / (k1_ms / 1e3) / 1e9
     step_gbs = alg / (ms_per_step / 1e3) / 1e9
-    if fused:
+    mla_bytes = [sum(attn_row_bytes(wl, wl.seqlens[b] - wl.Lq + i + 1, c)
+                     for b in range(wl.B) for i in range(wl.Lq)) for c in range(wl.attn_calls)]
+    if hier:
+        # the index pass reads a small fraction of the keys; the attention call dominates
+        att_ms = sum(st[2 + c] for st in stage_ms for c in range(wl.attn_calls)) / (
+            args.steps * wl.attn_calls)
+        att_gbs = mla_bytes[0] / (att_ms / 1e3) / 1e9
+        roofline = {"kernel": "lsa_sparse_mla_decode (sparse_mla_kernel<576,512,true> + "
+                              "mla_combine_kernel)",
+                    "bound": "hbm", "achieved": round(att_gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(att_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "avg_launch_ms": round(att_ms, 5), "alg_bytes_per_launch": mla_bytes[0]}
+    elif fused:
         roofline = {"kernel": "lsa_index_topk (index_scores_kernel<128,true> + topk_merge_kernel)",
                     "bound": "hbm", "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
@@ -408,8 +476,6 @@ def main():
     # per-stage algorithmic bytes: the indexer call as in the roofline; top-k (split path) reads
     # the visible scores and writes the indices; an attention call gathers the selected rows and
     # moves q, out and the index list
-    mla_bytes = [sum(attn_row_bytes(wl, wl.seqlens[b] - wl.Lq + i + 1, c)
-                     for b in range(wl.B) for i in range(wl.Lq)) for c in range(wl.attn_calls)]
     topk_bytes = sum((wl.seqlens[b] - wl.Lq + i + 1) * 4 + wl.topk * 4 + 4
                      for b in range(wl.B) for i in range(wl.Lq))
     # (rates only for decode: prefill rows share keys and selected rows, so per-row byte counts
@@ -417,7 +483,10 @@ def main():
     stages = {"index_call_ms": round(mean(0), 5)}
     if wl.decode:
         stages["index_call_gbs"] = round(k1_bytes / (mean(0) / 1e3) / 1e9, 1)
-    if not fused:
+    if hier:
+        stages["block_keys_build_ms"] = round(block_keys_ms, 5)
+        stages["selection_recall_vs_exact"] = recall
+    elif not fused:
         stages["topk_call_ms"] = round(mean(1), 5)
         stages["topk_call_gbs"] = round(topk_bytes / (mean(1) / 1e3) / 1e9, 1)
     for c in range(wl.attn_calls):
@@ -456,7 +525,8 @@ def main():
                    "index_heads": wl.Hi, "index_dim": wl.Di, "topk": wl.topk,
                    "init_tokens": wl.init, "local_tokens": wl.local, "mla_heads": wl.H,
                    "qk_dim": wl.Dqk, "v_dim": wl.Dv, "mla_calls_per_step": wl.attn_calls,
-                   "draft_steps": wl.draft_steps},
+                   "draft_steps": wl.draft_steps, "hier_block": wl.hier_block,
+                   "hier_keep": wl.hier_keep},
         "roofline": roofline,
         "stages": stages,
     }

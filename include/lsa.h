@@ -250,7 +250,9 @@ size_t lsa_hier_workspace_bytes(int B, int S_max, int Bk, int topk, int init_tok
  *   lsa_block_keys (complete for every block below seqlens[b] / Bk); indices int32 [B, topk]
  *   ascending, -1 padded; n_sel int32 [B].
  * Supported: Hi <= 32, Di a multiple of 16 and <= 128, Bk a power of two in [8, 1024],
- * 1 <= M <= S_max / Bk, and the sizes lsa_topk_select takes.  Errors as lsa_index_topk.
+ * 1 <= M <= S_max / Bk with M*Bk >= topk - local_tokens (so the kept blocks always hold enough
+ * candidates and no -inf token is ever selected), and the sizes lsa_topk_select takes.  Errors
+ * as lsa_index_topk.
  */
 lsa_status lsa_hier_index_topk(const void* q_idx, const float* w, const void* k_idx,
                                const void* block_keys, const int32_t* seqlens, int B, int Hi,

@@ -178,6 +178,9 @@ static lsa_status check_hier(int B, int S_max, int topk, int init_tokens, int lo
                 Bk, S_max);
   if (M < 1 || M > S_max / Bk)
     return fail(LSA_ERR_BAD_SHAPE, "%s: M=%d outside [1, S_max / Bk = %d]", fn, M, S_max / Bk);
+  if (static_cast<long>(M) * Bk < static_cast<long>(topk) - local_tokens)
+    return fail(LSA_ERR_BAD_SHAPE, "%s: M*Bk=%ld below topk - local_tokens=%d (too few candidates)", fn,
+                static_cast<long>(M) * Bk, topk - local_tokens);
   return LSA_OK;
 }
 

@@ -6,21 +6,27 @@
 //   index keys); a block is scored like a token, sum_h w[h] * max(0, q[h] . key); the blocks
 //   scored are the nb = w0 / Bk complete ones before the sliding window (w0 = max(p - local + 1,
 //   0)); the M best are kept; tokens outside the sink, the window, the partial block before it
-//   and the kept blocks get the score -inf; then the usual selection.
+//   and the kept blocks are excluded (they would score -inf); then the usual selection, which
+//   never reaches an excluded token when M*Bk >= topk - local (required).
 //
 // Design for gfx950.  Block keys are a summary of the key cache, built once per completed block
 // (lsa_block_keys), so a decode pass reads nb block keys (1/Bk of the cache) plus the kept
 // blocks' tokens instead of every key.
-//  * hier_score_kernel<TOKENS>: one wavefront scores 32 key rows against the row's (up to) 32
-//    index heads with the 32x32x16 bf16 MFMA, heads as the A rows and keys as the B columns, so
-//    a lane ends with 16 head dot products of one key: the ReLU-weighted head sum is 16 FMAs and
-//    one lane swap (xor 32).  Stage 1 (blocks) writes the block scores and each row's block
-//    count; stage 2 (tokens) writes a dense score row: the score for candidates, -inf for
-//    tokens outside the kept blocks (a wavefront whose 32 tokens are all excluded loads no key).
-//  * The two selections (M blocks, then topk tokens) are the top-k kernels of lsa_topk.hip.
+//  * One wavefront scores 32 key rows against the row's (up to) 32 index heads with the
+//    32x32x16 bf16 MFMA, heads as the A rows and keys as the B columns, so a lane ends with 16
+//    head dot products of one key: the ReLU-weighted head sum is 16 FMAs and one lane swap.
+//  * hier_block_scores_kernel: the block scores and each row's block count; the M best blocks
+//    come from the top-k kernels of lsa_topk.hip.
+//  * hier_candidates_kernel: one workgroup per (row, chunk of positions) scores the middle
+//    tokens of its chunk that lie in kept blocks or in the partial block before the window, and
+//    writes them as a (key, position) list in the format of the exact merge of lsa_topk.hip,
+//    which makes the final selection.  Excluded tokens are never written (a wavefront whose 32
+//    tokens are all excluded loads nothing), so the merge sees about M*Bk candidates per row.
+//    This needs at least R = topk - init - local middle candidates per row: M*Bk >= topk - local.
 #include <algorithm>
 
 #include "lsa_internal.h"
+#include "lsa_select.h"
 
 namespace lsa {
 namespace {
@@ -64,11 +70,15 @@ struct HierParams {
   const int32_t* seqlens;
   int Hi, Di, S_max, Bk, init, local;
   int nblk;               // S_max / Bk
-  float* scores;          // stage 1: [B, nblk]; stage 2: [B, S_max]
+  float* scores;          // stage 1: [B, nblk] block scores
   int32_t* nb_out;        // stage 1: blocks scored per row
   const int32_t* kept;    // stage 2: [B, M] kept blocks (ascending), kept_n[B] of them
   const int32_t* kept_n;
-  int M;
+  int M, topk;
+  int chunk_keys, chunks;  // stage 2: candidate lists, one per chunk of positions
+  uint32_t* count;         // [B, chunks]
+  uint32_t* range;         // [B, chunks, 2] smallest and largest key of each list
+  uint2* cand;             // [B, chunks, chunk_keys] (order key, position)
 };
 
 // Scores of key rows r0 .. r0 + 31 (row = lane & 31) against the row's heads; valid in every
@@ -97,55 +107,91 @@ __device__ __forceinline__ float score32(const HierParams& P, int b, const uint1
   return s + xor32(s);
 }
 
-// grid (ceil(rows / 128), B).  TOKENS = false: block scores of blocks [0, nb); true: the dense
-// token score row [0, p] of stage 2.
-template <bool TOKENS>
-__global__ __launch_bounds__(kHierThreads) void hier_score_kernel(HierParams P) {
-  __shared__ int keep[kRowsPerGroup / 8 + 2];  // kept flags of the blocks this group touches
+// grid (ceil(nblk / 128), B): scores of blocks [0, nb) and the row's nb.
+__global__ __launch_bounds__(kHierThreads) void hier_block_scores_kernel(HierParams P) {
   const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = min(P.seqlens[b], P.S_max), p = n - 1;
-  const int w0 = max(p - P.local + 1, 0);
-  const int nb = w0 / P.Bk;
+  const int nb = max(p - P.local + 1, 0) / P.Bk;
   const int r0 = blockIdx.x * kRowsPerGroup + wave * 32;
-  if constexpr (!TOKENS) {
-    if (blockIdx.x == 0 && tid == 0) P.nb_out[b] = nb;
-    if (r0 >= nb) return;
-    const float s = score32(P, b, P.keys, static_cast<size_t>(P.nblk) * P.Di, r0, nb - 1);
-    const int j = r0 + lane;
-    if (lane < 32 && j < nb) P.scores[static_cast<size_t>(b) * P.nblk + j] = s;
-  } else {
-    // kept flags of blocks [first_blk, first_blk + span)
-    const int g0 = blockIdx.x * kRowsPerGroup;
-    const int first_blk = g0 / P.Bk;
-    const int span = (kRowsPerGroup - 1) / P.Bk + 2;
-    for (int i = tid; i < span; i += kHierThreads) keep[i] = 0;
-    __syncthreads();
-    const int cnt = P.kept_n[b];
-    for (int i = tid; i < cnt; i += kHierThreads) {
-      const int j = P.kept[static_cast<size_t>(b) * P.M + i] - first_blk;
-      if (j >= 0 && j < span) keep[j] = 1;
+  if (blockIdx.x == 0 && tid == 0) P.nb_out[b] = nb;
+  if (r0 >= nb) return;
+  const float s = score32(P, b, P.keys, static_cast<size_t>(P.nblk) * P.Di, r0, nb - 1);
+  const int j = r0 + lane;
+  if (lane < 32 && j < nb) P.scores[static_cast<size_t>(b) * P.nblk + j] = s;
+}
+
+constexpr int kMaxSpan = 8192 / 8;  // blocks per chunk: chunk_keys <= 8192, Bk >= 8
+
+// grid (chunks, B): the candidate list of positions [c * chunk_keys, (c + 1) * chunk_keys) of
+// row b: its middle positions (init <= s <= p - local) inside kept blocks or at or after nb*Bk.
+// Every list is written (count 0 when empty, and for dense rows, which the merge fills itself).
+__global__ __launch_bounds__(kHierThreads) void hier_candidates_kernel(HierParams P) {
+  __shared__ int keep[kMaxSpan];
+  __shared__ uint32_t n_out, k_lo, k_hi;
+  const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = min(P.seqlens[b], P.S_max), p = n - 1;
+  const int nb = max(p - P.local + 1, 0) / P.Bk;
+  const int base = c * P.chunk_keys;
+  const int a = max(P.init, base), z = min(p - P.local, base + P.chunk_keys - 1);
+  const size_t lc = static_cast<size_t>(b) * P.chunks + c;
+  if (n <= P.topk || a > z) {
+    if (tid == 0) {
+      P.count[lc] = 0u;
+      P.range[2 * lc] = 0xffffffffu;
+      P.range[2 * lc + 1] = 0u;
     }
-    __syncthreads();
-    if (r0 > p) return;
+    return;
+  }
+  const int span = P.chunk_keys / P.Bk;  // blocks of this chunk (chunk_keys is a multiple of Bk)
+  const int first_blk = base / P.Bk;
+  for (int i = tid; i < span; i += kHierThreads) keep[i] = 0;
+  if (tid == 0) {
+    n_out = 0u;
+    k_lo = 0xffffffffu;
+    k_hi = 0u;
+  }
+  __syncthreads();
+  const int cnt = P.kept_n[b];
+  for (int i = tid; i < cnt; i += kHierThreads) {
+    const int j = P.kept[static_cast<size_t>(b) * P.M + i] - first_blk;
+    if (j >= 0 && j < span) keep[j] = 1;
+  }
+  __syncthreads();
+  uint2* list = P.cand + lc * static_cast<size_t>(P.chunk_keys);
+  for (int r0 = base + wave * 32; r0 <= z; r0 += kRowsPerGroup) {
+    if (r0 + 31 < a) continue;
     const int s = r0 + (lane & 31);
-    const bool forced = s < P.init || s > p - P.local;
-    const bool cand = s < P.init || s >= nb * P.Bk || keep[s / P.Bk - first_blk] != 0;
-    float v = -INFINITY;
-    if (__ballot(cand && !forced) != 0)  // wavefront-uniform
-      v = score32(P, b, P.keys, static_cast<size_t>(P.S_max) * P.Di, r0, p);
-    if (forced) v = 0.0f;  // the selection forces these; the value is not used
-    else if (!cand) v = -INFINITY;
-    if (lane < 32 && s <= p) P.scores[static_cast<size_t>(b) * P.S_max + s] = v;
+    const int blk = min(max((s - base) / P.Bk, 0), span - 1);
+    const bool cand = lane < 32 && s >= a && s <= z && (s >= nb * P.Bk || keep[blk] != 0);
+    const uint64_t mask = __ballot(cand);
+    if (mask == 0) continue;  // wavefront-uniform
+    const float v = score32(P, b, P.keys, static_cast<size_t>(P.S_max) * P.Di, r0, p);
+    uint32_t at = 0;
+    if (lane == 0) at = atomicAdd(&n_out, static_cast<uint32_t>(__popcll(mask)));
+    at = __shfl(at, 0) + lanes_below(mask);
+    if (cand) {
+      const uint32_t key = sel::order_key(v);
+      list[at] = make_uint2(key, static_cast<uint32_t>(s));
+      atomicMin(&k_lo, key);
+      atomicMax(&k_hi, key);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    P.count[lc] = n_out;
+    P.range[2 * lc] = k_lo;
+    P.range[2 * lc + 1] = k_hi;
   }
 }
 
 size_t align_up(size_t x) { return (x + kWorkspaceAlign - 1) & ~(kWorkspaceAlign - 1); }
 
 struct HierLayout {
-  size_t blk_scores, nb, kept, kept_n, tok_scores, topk_ws, total;
+  size_t blk_scores, nb, kept, kept_n, count, range, cand, topk_ws, total;
+  int chunk_keys, chunks;
 };
 
-HierLayout hier_layout(int B, int S_max, int Bk, int topk, int init, int local, int M) {
+HierLayout hier_layout(int B, int S_max, int Bk, int M) {
   HierLayout L{};
   const size_t nblk = static_cast<size_t>(S_max / Bk);
   size_t off = 0;
@@ -157,11 +203,20 @@ HierLayout hier_layout(int B, int S_max, int Bk, int topk, int init, int local, 
   off += align_up(static_cast<size_t>(B) * M * sizeof(int32_t));
   L.kept_n = off;
   off += align_up(static_cast<size_t>(B) * sizeof(int32_t));
-  L.tok_scores = off;
-  off += align_up(static_cast<size_t>(B) * S_max * sizeof(float));
+  // candidate lists: a power-of-two chunk length (a multiple of every block size), at most
+  // topk_merge_max_chunks() lists per row
+  L.chunk_keys = 2048;
+  while (static_cast<long>(L.chunk_keys) * topk_merge_max_chunks() < S_max) L.chunk_keys *= 2;
+  L.chunks = (S_max + L.chunk_keys - 1) / L.chunk_keys;
+  const size_t lists = static_cast<size_t>(B) * L.chunks;
+  L.count = off;
+  off += align_up(lists * sizeof(uint32_t));
+  L.range = off;
+  off += align_up(lists * 2 * sizeof(uint32_t));
+  L.cand = off;
+  off += align_up(lists * L.chunk_keys * sizeof(uint2));
   L.topk_ws = off;
-  off += align_up(std::max(topk_workspace_bytes(B, 1, static_cast<int>(nblk), M, 0, 0),
-                           topk_workspace_bytes(B, 1, S_max, topk, init, local)));
+  off += align_up(topk_workspace_bytes(B, 1, static_cast<int>(nblk), M, 0, 0));
   L.total = off + kWorkspaceAlign;
   return L;
 }
@@ -171,7 +226,8 @@ HierLayout hier_layout(int B, int S_max, int Bk, int topk, int init, int local, 
 int hier_max_heads() { return kMaxHeads; }
 
 size_t hier_workspace_bytes(int B, int S_max, int Bk, int topk, int init, int local, int M) {
-  return hier_layout(B, S_max, Bk, topk, init, local, M).total;
+  (void)topk, (void)init, (void)local;  // the final selection runs on the candidate lists
+  return hier_layout(B, S_max, Bk, M).total;
 }
 
 hipError_t launch_block_keys(const uint16_t* k_idx, const int32_t* seqlens, int B, int S_max, int Di,
@@ -189,7 +245,8 @@ hipError_t launch_hier_index_topk(const uint16_t* q_idx, const float* w, const u
                                   int Di, int S_max, int topk, int init, int local, int Bk, int M,
                                   int32_t* indices, int32_t* n_sel, void* workspace,
                                   hipStream_t stream) {
-  const HierLayout L = hier_layout(B, S_max, Bk, topk, init, local, M);
+  const HierLayout L = hier_layout(B, S_max, Bk, M);
+  if (L.chunk_keys / Bk > kMaxSpan) return hipErrorInvalidConfiguration;
   char* ws = align_workspace(workspace);
   const int nblk = S_max / Bk;
   HierParams P{};
@@ -208,30 +265,34 @@ hipError_t launch_hier_index_topk(const uint16_t* q_idx, const float* w, const u
   int32_t* nb = reinterpret_cast<int32_t*>(ws + L.nb);
   int32_t* kept = reinterpret_cast<int32_t*>(ws + L.kept);
   int32_t* kept_n = reinterpret_cast<int32_t*>(ws + L.kept_n);
-  float* tok = reinterpret_cast<float*>(ws + L.tok_scores);
   void* tws = ws + L.topk_ws;
+  P.topk = topk;
   // stage 1: block scores and the row's block count
   P.keys = block_keys;
   P.scores = blk_scores;
   P.nb_out = nb;
   const unsigned gb = static_cast<unsigned>(std::max(1, (nblk + kRowsPerGroup - 1) / kRowsPerGroup));
-  hipLaunchKernelGGL((hier_score_kernel<false>), dim3(gb, static_cast<unsigned>(B)), dim3(kHierThreads),
+  hipLaunchKernelGGL(hier_block_scores_kernel, dim3(gb, static_cast<unsigned>(B)), dim3(kHierThreads),
                      0, stream, P);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // the M best blocks of each row (every block when nb <= M)
   if ((err = launch_topk(blk_scores, nb, B, 1, nblk, M, 0, 0, kept, kept_n, tws, stream)) != hipSuccess)
     return err;
-  // stage 2: the dense token score row, then the selection
+  // stage 2: candidate lists of the kept blocks' tokens, then the exact merge
   P.keys = k_idx;
-  P.scores = tok;
   P.kept = kept;
   P.kept_n = kept_n;
-  const unsigned gt = static_cast<unsigned>((S_max + kRowsPerGroup - 1) / kRowsPerGroup);
-  hipLaunchKernelGGL((hier_score_kernel<true>), dim3(gt, static_cast<unsigned>(B)), dim3(kHierThreads),
-                     0, stream, P);
+  P.chunk_keys = L.chunk_keys;
+  P.chunks = L.chunks;
+  P.count = reinterpret_cast<uint32_t*>(ws + L.count);
+  P.range = reinterpret_cast<uint32_t*>(ws + L.range);
+  P.cand = reinterpret_cast<uint2*>(ws + L.cand);
+  hipLaunchKernelGGL(hier_candidates_kernel, dim3(static_cast<unsigned>(L.chunks), static_cast<unsigned>(B)),
+                     dim3(kHierThreads), 0, stream, P);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  return launch_topk(tok, seqlens, B, 1, S_max, topk, init, local, indices, n_sel, tws, stream);
+  return launch_topk_merge(seqlens, 1, S_max, topk, init, local, 0, B, L.chunks, L.chunk_keys, P.count,
+                           P.range, P.cand, indices, n_sel, stream);
 }
 
 }  // namespace lsa

@@ -38,6 +38,9 @@ class Workload:
     # multi-token-prediction draft steps on one index pass (0: none).  Draft step c runs at
     # length seqlens[b] + c on cache kv0 with its own query q{c}.
     draft_steps: int = 0
+    # hierarchical indexing: block size and blocks kept (0: the exact indexer)
+    hier_block: int = 0
+    hier_keep: int = 0
     seed: int = 1000
     notes: str = field(default="", compare=False)
 
@@ -80,6 +83,10 @@ WORKLOADS = {
     # 131070, 131071, 131072), each attending to the selection plus the tokens drafted since
     "mtp_decode_128k": _wl("mtp_decode_128k", 32, 131072, seqlens=[131070] * 32, draft_steps=3,
                            seed=1005),
+    # hierarchical indexing on the decode_128k shapes: blocks of 64 keys, the 32 best kept (twice
+    # the middle budget of 2048 - 16 - 1024 tokens); same inputs as decode_128k
+    "hier_decode_128k": _wl("hier_decode_128k", 32, 131072, mla_calls=2, hier_block=64,
+                            hier_keep=32, seed=1002),
 }
 
 

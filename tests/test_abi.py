@@ -129,6 +129,7 @@ def test_hierarchical_argument_errors_and_workspace():
 
     assert call(Hi=33) == 3 and call(Di=120) == 3 and call(Bk=96) == 3
     assert call(M=0) == 2 and call(M=2049) == 2 and call(init=1500) == 2
+    assert call(M=15) == 2  # 15 * 64 < topk - local: too few candidates
     assert call(bk_=None) == 1
     need = L.lsa_hier_workspace_bytes(4, 131072, 64, 2048, 16, 1024, 32)
     assert 0 < need < 16 << 20

@@ -35,6 +35,18 @@ def test_mtp_decode_128k_bytes():
     assert alg == 32 * (n * 256 + 8192 + 128 + 2048 * 4 + sum(per_draft(c) for c in range(3)))
 
 
+def test_hier_decode_128k_bytes():
+    wl = WORKLOADS["hier_decode_128k"]
+    # window from 131072 - 1024 = 130048: 2032 complete blocks of 64 scored, 32 kept (2048
+    # tokens scored), no partial block; the sink and window are forced
+    assert bench.index_keys_read(wl, 131072) == 2032 + 32 * 64
+    assert bench.index_keys_read(wl, 2000) == 0  # dense fallback: nothing scored
+    per_row = 4080 * 256 + 8192 + 128 + 2048 * 4
+    assert bench.hier_call_bytes(wl) == 32 * (per_row + 4)
+    per_mla = 2048 * 1152 + 32 * 1152 + 32 * 1024 + 2048 * 4
+    assert bench.algorithmic_bytes(wl)[0] == 32 * (per_row + 2 * per_mla)
+
+
 def test_prefill_128k_flops():
     wl = WORKLOADS["prefill_128k"]
     # query i of 4096 sees 126976 + i + 1 keys

@@ -1,8 +1,9 @@
 """GPU hierarchical indexing (lsa_block_keys, lsa_hier_index_topk) against the oracle on dyadic
 index queries and keys (every score and block mean is exact in fp32 and bf16, so selections
 compare bit for bit): block keys equal the bf16 block means; selections equal the oracle's for
-dense rows, rows whose blocks are all kept, budgets above the kept tokens (-inf ties decided by
-position), block sizes 8 to 1024; with every block kept the result is lsa_index_topk's."""
+dense rows, rows whose blocks are all kept, kept blocks holding exactly the middle budget, block
+sizes 8 to 1024, a 1M-token context (chunk lists of 8192); with every block kept the result is
+lsa_index_topk's; too few kept tokens for the budget is refused."""
 import dataclasses
 
 import numpy as np
@@ -36,12 +37,13 @@ class Case:
 CASES = [
     # rows: long, all blocks kept (nb <= M), dense (n <= topk)
     Case("small", 3, 4096, (4096, 700, 200), 4, 32, 256, 4, 64, 16, 24, 701),
-    # M * Bk = 128 below the middle budget of 188: -inf tokens fill the rest
-    Case("short_budget", 2, 4096, (4096, 3001), 4, 32, 256, 4, 64, 16, 8, 702),
+    # M * Bk = topk - local: with block 0 kept, exactly the middle budget of candidates
+    Case("exact_fill", 2, 4096, (4096, 3001), 4, 32, 256, 4, 64, 16, 12, 702),
     Case("bk8", 2, 2048, (2048, 1999), 8, 64, 128, 2, 16, 8, 20, 703),
     Case("bk1024", 2, 16384, (16384, 9000), 32, 128, 2048, 16, 1024, 1024, 4, 704),
     Case("decode_32k", 8, 32768, tuple(32768 - 97 * j for j in range(8)), 32, 128, 2048, 16, 1024,
          64, 32, 705),
+    Case("context_1m", 2, 1 << 20, (1 << 20, 700001), 32, 128, 2048, 16, 1024, 64, 32, 706),
 ]
 
 
@@ -111,3 +113,11 @@ def test_incremental_block_keys():
                               first_block=(c.seqlens[2] - 100) // c.Bk)
     torch.cuda.synchronize()
     assert torch.equal(full, part)
+
+
+def test_too_few_kept_tokens_is_refused():
+    c = CASES[0]
+    q, w, k, seq = make(c)
+    bk = lsa.lsa_block_keys(k, seq, c.Bk)
+    with pytest.raises(lsa.LsaError):  # 11 * 16 = 176 < topk - local = 192
+        lsa.lsa_hier_index_topk(q, w, k, bk, seq, c.topk, c.init, c.local, c.Bk, 11)
