@@ -15,14 +15,16 @@
 //  * One wavefront scores 32 key rows against the row's (up to) 32 index heads with the
 //    32x32x16 bf16 MFMA, heads as the A rows and keys as the B columns, so a lane ends with 16
 //    head dot products of one key: the ReLU-weighted head sum is 16 FMAs and one lane swap.
-//  * hier_block_scores_kernel: the block scores and each row's block count; the M best blocks
-//    come from the top-k kernels of lsa_topk.hip.
-//  * hier_candidates_kernel: one workgroup per (row, chunk of positions) scores the middle
-//    tokens of its chunk that lie in kept blocks or in the partial block before the window, and
-//    writes them as a (key, position) list in the format of the exact merge of lsa_topk.hip,
-//    which makes the final selection.  Excluded tokens are never written (a wavefront whose 32
-//    tokens are all excluded loads nothing), so the merge sees about M*Bk candidates per row.
-//    This needs at least R = topk - init - local middle candidates per row: M*Bk >= topk - local.
+//  * hier_block_scores_kernel: the block scores and each row's block count; it also empties the
+//    row's candidate lists for stage 2.  The M best blocks come from the top-k kernels of
+//    lsa_topk.hip.
+//  * hier_candidates_kernel: one wavefront per 32-token tile of a kept block (or of the partial
+//    block before the window) scores its middle tokens and appends them, with one atomic per
+//    wavefront, to the (key, position) list of their chunk of positions, in the format of the
+//    exact merge of lsa_topk.hip, which makes the final selection.  Only kept tokens are
+//    scored or written, so the merge sees about M*Bk candidates per row; the order inside a list
+//    varies, the merge's result does not.  This needs at least R = topk - init - local middle
+//    candidates per row: M*Bk >= topk - local.
 #include <algorithm>
 
 #include "lsa_internal.h"
@@ -113,75 +115,62 @@ __global__ __launch_bounds__(kHierThreads) void hier_block_scores_kernel(HierPar
   const int n = min(P.seqlens[b], P.S_max), p = n - 1;
   const int nb = max(p - P.local + 1, 0) / P.Bk;
   const int r0 = blockIdx.x * kRowsPerGroup + wave * 32;
-  if (blockIdx.x == 0 && tid == 0) P.nb_out[b] = nb;
+  if (blockIdx.x == 0) {  // the row's block count and empty candidate lists for stage 2
+    if (tid == 0) P.nb_out[b] = nb;
+    for (int c = tid; c < P.chunks; c += kHierThreads) {
+      const size_t lc = static_cast<size_t>(b) * P.chunks + c;
+      P.count[lc] = 0u;
+      P.range[2 * lc] = 0xffffffffu;
+      P.range[2 * lc + 1] = 0u;
+    }
+  }
   if (r0 >= nb) return;
   const float s = score32(P, b, P.keys, static_cast<size_t>(P.nblk) * P.Di, r0, nb - 1);
   const int j = r0 + lane;
   if (lane < 32 && j < nb) P.scores[static_cast<size_t>(b) * P.nblk + j] = s;
 }
 
-constexpr int kMaxSpan = 8192 / 8;  // blocks per chunk: chunk_keys <= 8192, Bk >= 8
-
-// grid (chunks, B): the candidate list of positions [c * chunk_keys, (c + 1) * chunk_keys) of
-// row b: its middle positions (init <= s <= p - local) inside kept blocks or at or after nb*Bk.
-// Every list is written (count 0 when empty, and for dense rows, which the merge fills itself).
+// grid (ceil(tiles / 4), B), tiles = (M + 1) * ceil(Bk / 32): tile t < M * tpb covers the
+// tokens of kept block t / tpb (32 of them from 32 * (t % tpb)); the last tpb tiles cover the
+// partial block before the window.  A tile's tokens lie in one block, hence in one chunk list.
 __global__ __launch_bounds__(kHierThreads) void hier_candidates_kernel(HierParams P) {
-  __shared__ int keep[kMaxSpan];
-  __shared__ uint32_t n_out, k_lo, k_hi;
-  const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.y, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int n = min(P.seqlens[b], P.S_max), p = n - 1;
+  if (n <= P.topk) return;  // dense: the merge fills the row
+  const int hi = p - P.local;  // middle positions [init, hi]
   const int nb = max(p - P.local + 1, 0) / P.Bk;
-  const int base = c * P.chunk_keys;
-  const int a = max(P.init, base), z = min(p - P.local, base + P.chunk_keys - 1);
-  const size_t lc = static_cast<size_t>(b) * P.chunks + c;
-  if (n <= P.topk || a > z) {
-    if (tid == 0) {
-      P.count[lc] = 0u;
-      P.range[2 * lc] = 0xffffffffu;
-      P.range[2 * lc + 1] = 0u;
-    }
+  const int tpb = (P.Bk + 31) / 32;
+  int first, last;  // the tile's positions [first, last]
+  if (t < P.M * tpb) {
+    const int i = t / tpb;
+    if (i >= P.kept_n[b]) return;
+    const int blk0 = P.kept[static_cast<size_t>(b) * P.M + i] * P.Bk;
+    first = blk0 + 32 * (t % tpb);
+    last = min(first + 31, blk0 + P.Bk - 1);
+  } else if (t < (P.M + 1) * tpb) {
+    first = nb * P.Bk + 32 * (t - P.M * tpb);
+    last = min(first + 31, nb * P.Bk + P.Bk - 1);
+  } else {
     return;
   }
-  const int span = P.chunk_keys / P.Bk;  // blocks of this chunk (chunk_keys is a multiple of Bk)
-  const int first_blk = base / P.Bk;
-  for (int i = tid; i < span; i += kHierThreads) keep[i] = 0;
-  if (tid == 0) {
-    n_out = 0u;
-    k_lo = 0xffffffffu;
-    k_hi = 0u;
+  const int s = first + (lane & 31);
+  const bool cand = lane < 32 && s <= last && s >= P.init && s <= hi;
+  const uint64_t mask = __ballot(cand);
+  if (mask == 0) return;  // wavefront-uniform
+  const float v = score32(P, b, P.keys, static_cast<size_t>(P.S_max) * P.Di, first, p);
+  const uint32_t key = sel::order_key(v);
+  // one list slot range per wavefront, and the list's key bounds
+  const size_t lc = static_cast<size_t>(b) * P.chunks + first / P.chunk_keys;
+  uint32_t at = 0;
+  if (lane == 0) at = atomicAdd(&P.count[lc], static_cast<uint32_t>(__popcll(mask)));
+  at = __shfl(at, 0) + lanes_below(mask);
+  const uint32_t kmin = wave_min(cand ? key : 0xffffffffu), kmax = wave_max(cand ? key : 0u);
+  if (lane == 0) {
+    atomicMin(&P.range[2 * lc], kmin);
+    atomicMax(&P.range[2 * lc + 1], kmax);
   }
-  __syncthreads();
-  const int cnt = P.kept_n[b];
-  for (int i = tid; i < cnt; i += kHierThreads) {
-    const int j = P.kept[static_cast<size_t>(b) * P.M + i] - first_blk;
-    if (j >= 0 && j < span) keep[j] = 1;
-  }
-  __syncthreads();
-  uint2* list = P.cand + lc * static_cast<size_t>(P.chunk_keys);
-  for (int r0 = base + wave * 32; r0 <= z; r0 += kRowsPerGroup) {
-    if (r0 + 31 < a) continue;
-    const int s = r0 + (lane & 31);
-    const int blk = min(max((s - base) / P.Bk, 0), span - 1);
-    const bool cand = lane < 32 && s >= a && s <= z && (s >= nb * P.Bk || keep[blk] != 0);
-    const uint64_t mask = __ballot(cand);
-    if (mask == 0) continue;  // wavefront-uniform
-    const float v = score32(P, b, P.keys, static_cast<size_t>(P.S_max) * P.Di, r0, p);
-    uint32_t at = 0;
-    if (lane == 0) at = atomicAdd(&n_out, static_cast<uint32_t>(__popcll(mask)));
-    at = __shfl(at, 0) + lanes_below(mask);
-    if (cand) {
-      const uint32_t key = sel::order_key(v);
-      list[at] = make_uint2(key, static_cast<uint32_t>(s));
-      atomicMin(&k_lo, key);
-      atomicMax(&k_hi, key);
-    }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    P.count[lc] = n_out;
-    P.range[2 * lc] = k_lo;
-    P.range[2 * lc + 1] = k_hi;
-  }
+  if (cand) P.cand[lc * static_cast<size_t>(P.chunk_keys) + at] = make_uint2(key, static_cast<uint32_t>(s));
 }
 
 size_t align_up(size_t x) { return (x + kWorkspaceAlign - 1) & ~(kWorkspaceAlign - 1); }
@@ -246,7 +235,6 @@ hipError_t launch_hier_index_topk(const uint16_t* q_idx, const float* w, const u
                                   int32_t* indices, int32_t* n_sel, void* workspace,
                                   hipStream_t stream) {
   const HierLayout L = hier_layout(B, S_max, Bk, M);
-  if (L.chunk_keys / Bk > kMaxSpan) return hipErrorInvalidConfiguration;
   char* ws = align_workspace(workspace);
   const int nblk = S_max / Bk;
   HierParams P{};
@@ -267,7 +255,12 @@ hipError_t launch_hier_index_topk(const uint16_t* q_idx, const float* w, const u
   int32_t* kept_n = reinterpret_cast<int32_t*>(ws + L.kept_n);
   void* tws = ws + L.topk_ws;
   P.topk = topk;
-  // stage 1: block scores and the row's block count
+  P.chunk_keys = L.chunk_keys;
+  P.chunks = L.chunks;
+  P.count = reinterpret_cast<uint32_t*>(ws + L.count);
+  P.range = reinterpret_cast<uint32_t*>(ws + L.range);
+  P.cand = reinterpret_cast<uint2*>(ws + L.cand);
+  // stage 1: block scores, the row's block count, empty candidate lists
   P.keys = block_keys;
   P.scores = blk_scores;
   P.nb_out = nb;
@@ -283,12 +276,8 @@ hipError_t launch_hier_index_topk(const uint16_t* q_idx, const float* w, const u
   P.keys = k_idx;
   P.kept = kept;
   P.kept_n = kept_n;
-  P.chunk_keys = L.chunk_keys;
-  P.chunks = L.chunks;
-  P.count = reinterpret_cast<uint32_t*>(ws + L.count);
-  P.range = reinterpret_cast<uint32_t*>(ws + L.range);
-  P.cand = reinterpret_cast<uint2*>(ws + L.cand);
-  hipLaunchKernelGGL(hier_candidates_kernel, dim3(static_cast<unsigned>(L.chunks), static_cast<unsigned>(B)),
+  const int tiles = (M + 1) * ((Bk + 31) / 32);
+  hipLaunchKernelGGL(hier_candidates_kernel, dim3(static_cast<unsigned>((tiles + 3) / 4), static_cast<unsigned>(B)),
                      dim3(kHierThreads), 0, stream, P);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   return launch_topk_merge(seqlens, 1, S_max, topk, init, local, 0, B, L.chunks, L.chunk_keys, P.count,

@@ -24,6 +24,7 @@
 // range still spread over the histogram instead of piling into a few bins.
 // Every step counts exactly, so the result does not depend on scheduling.
 #include <algorithm>
+#include <atomic>
 
 #include "lsa_select.h"
 
@@ -341,9 +342,23 @@ size_t merge_lds_bytes(int S_max) {
   return sizeof(uint32_t) * (static_cast<size_t>(kMsBits) + (S_max + 31) / 32 + 1);
 }
 
+// The attribute is a maximum: it is raised only when a launch needs more than the device's
+// current setting, so calls of different sizes do not reset it back and forth.
 hipError_t set_merge_lds(size_t lds) {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(topk_merge_kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  constexpr int kDevices = 64;
+  static std::atomic<size_t> set_to[kDevices];
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev >= 0 && dev < kDevices && set_to[dev].load(std::memory_order_relaxed) >= lds) return hipSuccess;
+  err = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_merge_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  if (err == hipSuccess && dev >= 0 && dev < kDevices) {
+    size_t cur = set_to[dev].load(std::memory_order_relaxed);
+    while (cur < lds && !set_to[dev].compare_exchange_weak(cur, lds)) {
+    }
+  }
+  return err;
 }
 
 }  // namespace
