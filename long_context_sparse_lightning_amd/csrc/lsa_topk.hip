@@ -43,7 +43,6 @@ using sel::select_bin;
 
 constexpr int kChunk = 16384;        // positions per chunk workgroup
 constexpr int kChunkThreads = 512;
-constexpr int kChunkWaves = kChunkThreads / kWave;
 constexpr int kChunkItems = kChunk / kChunkThreads;  // 32 per thread
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeWaves = kMergeThreads / kWave;
@@ -133,7 +132,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
   uint32_t* sh_lk = lds + kMsHist;                                     // rank list keys
   int32_t* sh_lp = reinterpret_cast<int32_t*>(lds + kMsHist + kTieList);  // rank list positions
   uint32_t* sh_bits = lds + kMsBits;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int grow = blockIdx.x;
   const int row = P.row0 + grow;
   const RowGeom g = row_geom(P.seqlens, row, P.Lq, P.S_max, P.topk, P.init, P.local);

@@ -66,6 +66,27 @@ int main() {
   CHECK(lsa_index_frontend(p, p, p, p, nullptr, p, ip, 2, 1, 1536, 3072, 32, 128, 64, 1e6f, 1e-6f, 100, p, fp, p, p, size_t(1) << 30, nullptr) == LSA_ERR_NULL_ARG);
   CHECK(lsa_index_frontend(p, p, p, p, fp, p, ip, 32, 1, 1536, 3072, 32, 128, 64, 1e6f, 1e-6f, 100, p, fp, p, p, feneed - 1, nullptr) == LSA_ERR_WORKSPACE && has_error());
   CHECK(lsa_index_frontend(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 1, 1536, 3072, 32, 128, 64, 1e6f, 1e-6f, 100, nullptr, nullptr, nullptr, nullptr, 0, nullptr) == LSA_OK && !has_error());
+
+  // multi-token-prediction draft attention
+  const size_t dneed = lsa_mtp_draft_workspace_bytes(32, 32, 512, 131072, 2048, 3);
+  CHECK(dneed > 0 && lsa_mtp_draft_workspace_bytes(32, 32, 512, 131072, 2048, 65) == 0);
+  CHECK(lsa_mtp_draft_attention(p, p, ip, ip, ip, ip, 4, 32, 576, 512, 131072, 2048, -1, 0.07f, p, fp, p, size_t(1) << 30, nullptr) == LSA_ERR_BAD_SHAPE && has_error());
+  CHECK(lsa_mtp_draft_attention(p, p, ip, ip, ip, ip, 4, 32, 576, 512, 131072, 65537, 3, 0.07f, p, fp, p, size_t(1) << 30, nullptr) == LSA_ERR_UNSUPPORTED);
+  CHECK(lsa_mtp_draft_attention(p, p, ip, ip, nullptr, ip, 4, 32, 576, 512, 131072, 2048, 3, 0.07f, p, fp, p, size_t(1) << 30, nullptr) == LSA_ERR_NULL_ARG);
+  CHECK(lsa_mtp_draft_attention(p, p, ip, ip, ip, ip, 32, 32, 576, 512, 131072, 2048, 3, 0.07f, p, fp, p, dneed - 1, nullptr) == LSA_ERR_WORKSPACE);
+  CHECK(lsa_mtp_draft_attention(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 32, 576, 512, 100, 64, 3, 0.1f, nullptr, nullptr, nullptr, 0, nullptr) == LSA_OK && !has_error());
+  // hierarchical indexing
+  CHECK(lsa_block_keys(p, ip, 2, 4096, 128, 48, 0, p, nullptr) == LSA_ERR_UNSUPPORTED && has_error());
+  CHECK(lsa_block_keys(p, ip, 2, 4096, 128, 64, -1, p, nullptr) == LSA_ERR_BAD_SHAPE);
+  CHECK(lsa_block_keys(p, nullptr, 2, 4096, 128, 64, 0, p, nullptr) == LSA_ERR_NULL_ARG);
+  CHECK(lsa_block_keys(nullptr, nullptr, 0, 4096, 128, 64, 0, nullptr, nullptr) == LSA_OK && !has_error());
+  const size_t hneed = lsa_hier_workspace_bytes(4, 131072, 64, 2048, 16, 1024, 32);
+  CHECK(hneed > 0 && lsa_hier_workspace_bytes(4, 131072, 64, 2048, 16, 1024, 15) == 0);
+  CHECK(lsa_hier_index_topk(p, fp, p, p, ip, 4, 32, 128, 131072, 2048, 16, 1024, 64, 15, op, op, p, size_t(1) << 30, nullptr) == LSA_ERR_BAD_SHAPE && has_error());
+  CHECK(lsa_hier_index_topk(p, fp, p, p, ip, 4, 33, 128, 131072, 2048, 16, 1024, 64, 32, op, op, p, size_t(1) << 30, nullptr) == LSA_ERR_UNSUPPORTED);
+  CHECK(lsa_hier_index_topk(p, fp, p, nullptr, ip, 4, 32, 128, 131072, 2048, 16, 1024, 64, 32, op, op, p, size_t(1) << 30, nullptr) == LSA_ERR_NULL_ARG);
+  CHECK(lsa_hier_index_topk(p, fp, p, p, ip, 4, 32, 128, 131072, 2048, 16, 1024, 64, 32, op, op, p, hneed - 1, nullptr) == LSA_ERR_WORKSPACE);
+  CHECK(lsa_hier_index_topk(nullptr, nullptr, nullptr, nullptr, nullptr, 0, 32, 128, 131072, 2048, 16, 1024, 64, 32, nullptr, nullptr, nullptr, 0, nullptr) == LSA_OK && !has_error());
   std::puts("abi driver: ok");
   return 0;
 }
