@@ -102,31 +102,17 @@ __global__ __launch_bounds__(kChunkThreads, 4) void topk_chunk_kernel(TopkParams
 // Dynamic LDS layout of the merge kernel (32-bit words).
 constexpr int kMsScan = 0;                          // [kMergeWaves]
 constexpr int kMsRes = kMsScan + kMergeWaves;       // [16] results of select_bin / counters
-constexpr int kMsCnt = kMsRes + 16;                 // [2][kMergeWaves] block_count / min-max
+constexpr int kMsCnt = kMsRes + 16;                 // [2][kMergeWaves] spare
 constexpr int kMsOff = kMsCnt + 2 * kMergeWaves;    // [kMaxChunks + 1] candidate offsets
 constexpr int kMsHist = kMsOff + kMaxChunks + 16;   // [kBins] radix rounds, then the rank list
 static_assert(kMaxChunks <= kMergeThreads, "one thread per chunk list");
 constexpr int kMsBits = kMsHist + kBins;            // bitmap over the middle range
 static_assert(2 * kTieList <= kBins, "the rank list reuses the histogram");
 
-// Block-wide sum of a per-thread count (one barrier; alternating slots).
-__device__ __forceinline__ uint32_t block_count(uint32_t v, uint32_t* cnt, int& parity) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  v = wave_last(wave_prefix_sum(v));
-  if (lane == 0) cnt[parity * kMergeWaves + wave] = v;
-  __syncthreads();
-  uint32_t t = 0;
-#pragma unroll
-  for (int w = 0; w < kMergeWaves; ++w) t += cnt[parity * kMergeWaves + w];
-  parity ^= 1;
-  return t;
-}
-
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   uint32_t* sh_scan = lds + kMsScan;
   uint32_t* sh_res = lds + kMsRes;
-  uint32_t* sh_cnt = lds + kMsCnt;
   uint32_t* sh_off = lds + kMsOff;
   uint32_t* sh_h = lds + kMsHist;
   uint32_t* sh_lk = lds + kMsHist;                                     // rank list keys
@@ -281,17 +267,33 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
         }
         if (rank < need) set_bit(pt);
       }
-    } else {  // more than kTieList equal keys (s_in == 0): bisect for the cut-off position
-      int parity = 0, cut = -1;
-      for (int bit = 20; bit >= 0; --bit) {
-        const int mid = cut + (1 << bit);
-        if (mid >= P.S_max) continue;
-        uint32_t v = 0;
-        each([&](uint32_t k, int32_t p) { v += (k == pref && p <= mid) ? 1u : 0u; });
-        if (block_count(v, sh_cnt, parity) < need) cut = mid;
+    } else {
+      // more than kTieList equal keys (s_in == 0): the `need` lowest positions among them, by a
+      // radix select on the position (below 2^20): its top 12 bits, then its low 8.  Digits are
+      // mirrored so that select_bin's target-th largest is the target-th lowest position.
+      constexpr int kPer = kBins / kMergeThreads;
+      uint32_t want = need, hi_digit = 0, cut = 0;
+      for (int round = 0; round < 2; ++round) {
+        for (int i = tid; i < kBins; i += kMergeThreads) sh_h[i] = 0u;
+        __syncthreads();
+        each([&](uint32_t k, int32_t p) {
+          const uint32_t u = static_cast<uint32_t>(p);
+          if (k != pref) return;
+          if (round == 0) atomicAdd(&sh_h[bin_slot<kMergeThreads>(kBins - 1 - (u >> 8))], 1u);
+          else if ((u >> 8) == hi_digit) atomicAdd(&sh_h[bin_slot<kMergeThreads>(kBins - 1 - (u & 255u))], 1u);
+        });
+        __syncthreads();
+        uint32_t c[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) c[i] = sh_h[i * kMergeThreads + tid];
+        select_bin<kPer, kMergeWaves>(c, want, sh_scan, sh_res);
+        want -= sh_res[1];
+        const uint32_t d = kBins - 1 - sh_res[0];
+        if (round == 0) hi_digit = d;
+        else cut = (hi_digit << 8) | d;
       }
       each([&](uint32_t k, int32_t p) {
-        if (k == pref && p <= cut + 1) set_bit(p);
+        if (k == pref && static_cast<uint32_t>(p) <= cut) set_bit(p);
       });
     }
   }
