@@ -156,7 +156,8 @@ def mtp_draft_indices(indices, n_sel, index_seqlens, seqlens, max_appended: int)
     indices int32 [B,topk] and n_sel int32 [B] of the pass made at index_seqlens [B]; the query
     sits at p = seqlens[b] - 1.  Per sequence: the pass's first min(n_sel, topk) entries, then
     the positions appended since, index_seqlens[b] .. p (at most max_appended of them).
-    Returns (indices int32 [B,1,topk+max_appended], -1 padded; n_sel int32 [B,1])."""
+    Returns (indices int32 [B,1,topk+max_appended], -1 padded; n_sel int32 [B,1]).  Where the
+    shared pass runs (here: at the first draft step) is parity unpinned against the pages."""
     indices = np.asarray(indices, np.int32)
     B, topk = indices.shape
     out = np.full((B, 1, topk + max_appended), -1, np.int32)

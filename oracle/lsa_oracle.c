@@ -272,7 +272,9 @@ int lsa_oracle_sparse_mla(const uint16_t* q, const uint16_t* kv, const int32_t* 
  * that part turns by the angle p * theta^(-2m/R):
  *   (u, v) -> (u cos a - v sin a, u sin a + v cos a).
  * Readings: the rotated part is the last R dims (the latent rows put rope last), pairs are
- * adjacent, RMSNorm carries a per-dim gain and eps, no extra scale on w.
+ * adjacent, RMSNorm carries a per-dim gain and eps, no extra scale on w.  Which dims rotate and
+ * how they pair is parity unpinned against the pages (they do not say); the pins fix this
+ * function to the readings.
  * cq: bf16 [B, Lq, q_lora]; hid: bf16 [B, Lq, hidden]; wq_b: bf16 [Hi*Di, q_lora];
  * wk: bf16 [Di, hidden]; gain: fp32 [Di]; w_proj: bf16 [Hi, hidden]; outputs fp64:
  * q_out [B, Lq, Hi, Di], w_out [B, Lq, Hi], k_out [B, Lq, Di].
