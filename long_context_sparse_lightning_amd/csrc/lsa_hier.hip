@@ -16,8 +16,10 @@
 //    32x32x16 bf16 MFMA, heads as the A rows and keys as the B columns, so a lane ends with 16
 //    head dot products of one key: the ReLU-weighted head sum is 16 FMAs and one lane swap.
 //  * hier_block_scores_kernel: the block scores and each row's block count; it also empties the
-//    row's candidate lists for stage 2.  The M best blocks come from the top-k kernels of
-//    lsa_topk.hip.
+//    row's candidate lists for stage 2.
+//  * hier_block_select_kernel: one 1024-thread workgroup per row keeps the M best blocks: three
+//    radix rounds over the 32-bit order key in an LDS histogram, the lowest blocks among equal
+//    keys, and an ascending compaction of a block bitmap.
 //  * hier_candidates_kernel: one wavefront per 32-token tile of a kept block (or of the partial
 //    block before the window) scores its middle tokens and appends them, with one atomic per
 //    wavefront, to the (key, position) list of their chunk of positions, in the format of the
@@ -74,8 +76,8 @@ struct HierParams {
   int nblk;               // S_max / Bk
   float* scores;          // stage 1: [B, nblk] block scores
   int32_t* nb_out;        // stage 1: blocks scored per row
-  const int32_t* kept;    // stage 2: [B, M] kept blocks (ascending), kept_n[B] of them
-  const int32_t* kept_n;
+  int32_t* kept;          // [B, M] kept blocks (ascending), kept_n[B] of them
+  int32_t* kept_n;
   int M, topk;
   int chunk_keys, chunks;  // stage 2: candidate lists, one per chunk of positions
   uint32_t* count;         // [B, chunks]
@@ -130,6 +132,87 @@ __global__ __launch_bounds__(kHierThreads) void hier_block_scores_kernel(HierPar
   if (lane < 32 && j < nb) P.scores[static_cast<size_t>(b) * P.nblk + j] = s;
 }
 
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kSelPer = sel::kBins / kSelThreads;
+constexpr int kMaxSelBlocks = 1 << 17;  // S_max / Bk with S_max <= 2^20 and Bk >= 8
+
+// grid (B): the M best of the row's nb block scores (larger score, then the lower block) in
+// ascending order, or every block when nb <= M.
+__global__ __launch_bounds__(kSelThreads) void hier_block_select_kernel(HierParams P) {
+  __shared__ uint32_t hist[sel::kBins];
+  __shared__ uint32_t win[kMaxSelBlocks / 32], tie[kMaxSelBlocks / 32];
+  __shared__ uint32_t sh_scan[kSelWaves], sh_res[4];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int nb = P.nb_out[b];
+  const float* sc = P.scores + static_cast<size_t>(b) * P.nblk;
+  int32_t* out = P.kept + static_cast<size_t>(b) * P.M;
+  if (nb <= P.M) {
+    for (int j = tid; j < P.M; j += kSelThreads) out[j] = j < nb ? j : -1;
+    if (tid == 0) P.kept_n[b] = max(nb, 0);
+    return;
+  }
+  // the M-th largest key: its top 12 bits, the next 12, the last 8
+  uint32_t want = static_cast<uint32_t>(P.M), pref = 0;
+  for (int round = 0; round < 3; ++round) {
+    const int shift = round == 0 ? 20 : round == 1 ? 8 : 0;
+    const int prev = round == 1 ? 20 : 8;  // in play: (k >> prev) == pref (rounds 1, 2)
+    const uint32_t mask = round < 2 ? 0xfffu : 0xffu;
+    for (int i = tid; i < sel::kBins; i += kSelThreads) hist[i] = 0u;
+    __syncthreads();
+    for (int j = tid; j < nb; j += kSelThreads) {
+      const uint32_t k = sel::order_key(sc[j]);
+      if (round == 0 || (k >> prev) == pref)
+        atomicAdd(&hist[sel::bin_slot<kSelThreads>((k >> shift) & mask)], 1u);
+    }
+    __syncthreads();
+    uint32_t c[kSelPer];
+#pragma unroll
+    for (int i = 0; i < kSelPer; ++i) c[i] = hist[i * kSelThreads + tid];
+    sel::select_bin<kSelPer, kSelWaves>(c, want, sh_scan, sh_res);
+    want -= sh_res[1];
+    pref = (pref << (round < 2 ? 12 : 8)) | sh_res[0];
+  }
+  // winners: keys above pref, and the `want` lowest blocks whose key equals it
+  const int words = (nb + 31) / 32;
+  for (int i = tid; i < words; i += kSelThreads) win[i] = tie[i] = 0u;
+  __syncthreads();
+  for (int j = tid; j < nb; j += kSelThreads) {
+    const uint32_t k = sel::order_key(sc[j]);
+    if (k > pref) atomicOr(&win[j >> 5], 1u << (j & 31));
+    else if (k == pref) atomicOr(&tie[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  const int wpt = (words + kSelThreads - 1) / kSelThreads;  // contiguous words per thread
+  const int w0 = tid * wpt, w1 = min(words, w0 + wpt);
+  uint32_t mine = 0, total;
+  for (int w = w0; w < w1; ++w) mine += __popc(tie[w]);
+  uint32_t rank = sel::block_prefix<kSelWaves>(mine, sh_scan, &total);
+  for (int w = w0; w < w1 && rank < want; ++w) {
+    uint32_t bits = tie[w];
+    while (bits && rank < want) {
+      const uint32_t low = bits & (~bits + 1u);
+      win[w] |= low;
+      bits ^= low;
+      ++rank;
+    }
+  }
+  __syncthreads();
+  mine = 0;
+  for (int w = w0; w < w1; ++w) mine += __popc(win[w]);
+  uint32_t at = sel::block_prefix<kSelWaves>(mine, sh_scan, &total);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t bits = win[w];
+    while (bits) {
+      const int i = __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (at < static_cast<uint32_t>(P.M)) out[at] = 32 * w + i;
+      ++at;
+    }
+  }
+  if (tid == 0) P.kept_n[b] = P.M;
+}
+
 // grid (ceil(tiles / 4), B), tiles = (M + 1) * ceil(Bk / 32): tile t < M * tpb covers the
 // tokens of kept block t / tpb (32 of them from 32 * (t % tpb)); the last tpb tiles cover the
 // partial block before the window.  A tile's tokens lie in one block, hence in one chunk list.
@@ -176,7 +259,7 @@ __global__ __launch_bounds__(kHierThreads) void hier_candidates_kernel(HierParam
 size_t align_up(size_t x) { return (x + kWorkspaceAlign - 1) & ~(kWorkspaceAlign - 1); }
 
 struct HierLayout {
-  size_t blk_scores, nb, kept, kept_n, count, range, cand, topk_ws, total;
+  size_t blk_scores, nb, kept, kept_n, count, range, cand, total;
   int chunk_keys, chunks;
 };
 
@@ -204,8 +287,6 @@ HierLayout hier_layout(int B, int S_max, int Bk, int M) {
   off += align_up(lists * 2 * sizeof(uint32_t));
   L.cand = off;
   off += align_up(lists * L.chunk_keys * sizeof(uint2));
-  L.topk_ws = off;
-  off += align_up(topk_workspace_bytes(B, 1, static_cast<int>(nblk), M, 0, 0));
   L.total = off + kWorkspaceAlign;
   return L;
 }
@@ -253,7 +334,6 @@ hipError_t launch_hier_index_topk(const uint16_t* q_idx, const float* w, const u
   int32_t* nb = reinterpret_cast<int32_t*>(ws + L.nb);
   int32_t* kept = reinterpret_cast<int32_t*>(ws + L.kept);
   int32_t* kept_n = reinterpret_cast<int32_t*>(ws + L.kept_n);
-  void* tws = ws + L.topk_ws;
   P.topk = topk;
   P.chunk_keys = L.chunk_keys;
   P.chunks = L.chunks;
@@ -270,12 +350,14 @@ hipError_t launch_hier_index_topk(const uint16_t* q_idx, const float* w, const u
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // the M best blocks of each row (every block when nb <= M)
-  if ((err = launch_topk(blk_scores, nb, B, 1, nblk, M, 0, 0, kept, kept_n, tws, stream)) != hipSuccess)
-    return err;
-  // stage 2: candidate lists of the kept blocks' tokens, then the exact merge
-  P.keys = k_idx;
+  if (nblk > kMaxSelBlocks) return hipErrorInvalidConfiguration;
   P.kept = kept;
   P.kept_n = kept_n;
+  hipLaunchKernelGGL(hier_block_select_kernel, dim3(static_cast<unsigned>(B)), dim3(kSelThreads), 0,
+                     stream, P);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  // stage 2: candidate lists of the kept blocks' tokens, then the exact merge
+  P.keys = k_idx;
   const int tiles = (M + 1) * ((Bk + 31) / 32);
   hipLaunchKernelGGL(hier_candidates_kernel, dim3(static_cast<unsigned>((tiles + 3) / 4), static_cast<unsigned>(B)),
                      dim3(kHierThreads), 0, stream, P);
