@@ -121,3 +121,18 @@ def test_too_few_kept_tokens_is_refused():
     bk = lsa.lsa_block_keys(k, seq, c.Bk)
     with pytest.raises(lsa.LsaError):  # 11 * 16 = 176 < topk - local = 192
         lsa.lsa_hier_index_topk(q, w, k, bk, seq, c.topk, c.init, c.local, c.Bk, 11)
+
+
+def test_all_scores_tied():
+    """Every key equal: every block and token score ties, so the lowest blocks are kept and the
+    lowest candidate positions chosen, as in the oracle."""
+    c = Case("tied", 3, 8192, (8192, 5000, 3001), 8, 64, 512, 8, 128, 32, 16, 707)
+    q, w, _, seq = make(c)
+    k = gen.device_tensor(c.seed, gen.TAGS["kidx"], (1, 1, c.Di), gen.DYADIC).expand(
+        c.B, c.S_max, c.Di).contiguous()
+    bk = lsa.lsa_block_keys(k, seq, c.Bk)
+    idx, nsel = lsa.lsa_hier_index_topk(q, w, k, bk, seq, c.topk, c.init, c.local, c.Bk, c.M)
+    torch.cuda.synchronize()
+    r_idx, r_nsel = oracle.hier_topk(bits(q), w.cpu().numpy(), bits(k), np.array(c.seqlens, np.int32),
+                                     c.topk, c.init, c.local, c.Bk, c.M)
+    assert np.array_equal(nsel.cpu().numpy(), r_nsel) and np.array_equal(idx.cpu().numpy(), r_idx)
