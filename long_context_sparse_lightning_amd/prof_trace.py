@@ -55,7 +55,8 @@ def summarize(stats_csv: str, title: str, command: str, bench: dict | None = Non
                          f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
     if bench:
         rf = bench["roofline"]
-        lines += ["", f"bench.py on the same build (HIP events, {bench['steps']} timed steps): "
+        lines += ["", f"bench.py's line from this traced run (HIP events, {bench['steps']} timed steps; the "
+                  f"profiler adds per-launch overhead, so unprofiled runs are faster): "
                   f"{bench['ms_per_step']} ms/step, {bench['value']} {bench['unit']}; {rf['kernel']} "
                   f"average launch {rf['avg_launch_ms'] * 1e3:.1f} us -> {rf['achieved']} {rf['unit']} "
                   f"algorithmic ({rf['frac'] * 100:.1f}% of {rf['peak']} {rf['unit']})."]

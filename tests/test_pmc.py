@@ -104,3 +104,4 @@ def test_trace_summary(tmp_path):
     assert "| index_scores_kernel<128, true> | 45 | 183.8 | 178.8 | 239.9 |" in text
     assert "| gen_fill_kernel (input setup, not a step) | 7 | 2.0 | 1.0 | 3.0 |" in text
     assert "average launch 204.1 us -> 5262.9 GB/s algorithmic (65.8% of 8000.0 GB/s)" in text
+    assert "profiler adds per-launch overhead" in text
