@@ -276,8 +276,10 @@ HierLayout hier_layout(int B, int S_max, int Bk, int M) {
   L.kept_n = off;
   off += align_up(static_cast<size_t>(B) * sizeof(int32_t));
   // candidate lists: a power-of-two chunk length (a multiple of every block size), at most
-  // topk_merge_max_chunks() lists per row
-  L.chunk_keys = 2048;
+  // topk_merge_max_chunks() lists per row.  16384 positions (8 lists at 128K) measured best for
+  // the merge: fewer lists cost less to walk, and each still fits its threads' registers when
+  // M*Bk stays near 2048 (2 or 64 lists were slower).
+  L.chunk_keys = 16384;
   while (static_cast<long>(L.chunk_keys) * topk_merge_max_chunks() < S_max) L.chunk_keys *= 2;
   L.chunks = (S_max + L.chunk_keys - 1) / L.chunk_keys;
   const size_t lists = static_cast<size_t>(B) * L.chunks;
