@@ -120,3 +120,24 @@ def test_appended_beyond_the_maximum_are_not_attended():
                                       c.Dv, 1.0 / np.sqrt(192.0), max_appended=2, lse=lse)
     torch.cuda.synchronize()
     compare(c, q, kv, idx, nsel, iseq, seq, 2, out, lse, "clamp")
+
+
+def test_dense_pass_then_drafts_is_dense_attention():
+    """A sequence shorter than topk: the index pass keeps every position, so each draft step's
+    selection is every position up to its own, i.e. dense attention (oracle, indices = None)."""
+    B, H, Dqk, Dv, S_max, topk, S0 = 3, 32, 576, 512, 3000, 2048, 1500
+    t = lambda name, shape: gen.device_tensor(611, gen.TAGS[name], shape, gen.NORMAL, device="cuda")
+    q, kv = t("q", (B, H, Dqk)), t("kv0", (B, S_max, Dqk))
+    idx = torch.full((B, topk), -1, dtype=torch.int32)
+    idx[:, :S0] = torch.arange(S0, dtype=torch.int32)
+    idx, nsel = idx.cuda(), torch.full((B,), S0, dtype=torch.int32, device="cuda")
+    iseq = torch.full((B,), S0, dtype=torch.int32, device="cuda")
+    scale = 1.0 / np.sqrt(192.0)
+    for j in range(3):
+        seq = iseq + j
+        lse = torch.empty(B, H, dtype=torch.float32, device="cuda")
+        out = lsa.lsa_mtp_draft_attention(q, kv, idx, nsel, iseq, seq, Dv, scale, max_appended=3, lse=lse)
+        torch.cuda.synchronize()
+        r_out, r_lse = oracle.sparse_mla(bits(q)[:, None], bits(kv), None, None, seq.cpu().numpy(), Dv, scale)
+        assert_attention_close(out.float().cpu().numpy(), r_out[:, 0], f"dense draft {j}")
+        assert np.max(np.abs(lse.cpu().numpy() - r_lse[:, 0])) <= LSE_ABS
