@@ -83,6 +83,8 @@ struct HierParams {
   uint32_t* count;         // [B, chunks]
   uint32_t* range;         // [B, chunks, 2] smallest and largest key of each list
   uint2* cand;             // [B, chunks, chunk_keys] (order key, position)
+  int32_t* indices;        // [B, topk] the selection
+  int32_t* n_sel;          // [B]
 };
 
 // Scores of key rows r0 .. r0 + 31 (row = lane & 31) against the row's heads; valid in every
@@ -256,6 +258,134 @@ __global__ __launch_bounds__(kHierThreads) void hier_candidates_kernel(HierParam
   if (cand) P.cand[lc * static_cast<size_t>(P.chunk_keys) + at] = make_uint2(key, static_cast<uint32_t>(s));
 }
 
+constexpr int kMergeItems = 4;                                  // candidates per thread
+constexpr int kMaxMergeCand = kSelThreads * kMergeItems;        // 4096
+constexpr int kMaxLists = 128;
+
+// grid (B): the selection of row b from its candidate lists when they hold at most
+// kMaxMergeCand = (M + 1) * Bk candidates: sink and window at the ends, the R = topk - init -
+// local best candidates (larger key, then lower position) in between, ascending.  A candidate's
+// slot is (its block's rank among the kept blocks, or kept_n for the partial block) * Bk + its
+// offset in the block, so slot order is position order.
+__global__ __launch_bounds__(kSelThreads) void hier_merge_kernel(HierParams P) {
+  __shared__ uint32_t hist[sel::kBins];
+  __shared__ uint32_t win[kMaxMergeCand / 32], tie[kMaxMergeCand / 32];
+  __shared__ uint32_t sh_scan[kSelWaves], sh_res[4], sh_off[kMaxLists + 1];
+  __shared__ int32_t sh_kept[kMaxMergeCand / 8];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int K = P.topk, I = P.init, W = P.local, R = K - I - W;
+  const int n = min(P.seqlens[b], P.S_max), p = n - 1;
+  int32_t* out = P.indices + static_cast<size_t>(b) * K;
+  if (n <= K) {  // dense: every visible position, then padding
+    for (int j = tid; j < K; j += kSelThreads) out[j] = j < n ? j : -1;
+    if (tid == 0) P.n_sel[b] = max(n, 0);
+    return;
+  }
+  for (int j = tid; j < I; j += kSelThreads) out[j] = j;
+  for (int j = tid; j < W; j += kSelThreads) out[K - W + j] = p - W + 1 + j;
+  if (tid == 0) P.n_sel[b] = K;
+  if (R == 0) return;
+  const int nb = max(p - P.local + 1, 0) / P.Bk;
+  const int kn = P.kept_n[b];
+  for (int i = tid; i < kn; i += kSelThreads) sh_kept[i] = P.kept[static_cast<size_t>(b) * P.M + i];
+  // list offsets
+  const uint32_t c_len = tid < P.chunks ? P.count[static_cast<size_t>(b) * P.chunks + tid] : 0u;
+  uint32_t nc;
+  const uint32_t at0 = sel::block_prefix<kSelWaves>(c_len, sh_scan, &nc);
+  if (tid < P.chunks) sh_off[tid] = at0;
+  __syncthreads();
+  // candidates into registers: entry q of the concatenated lists
+  uint32_t key[kMergeItems];
+  int32_t slot[kMergeItems];
+  uint32_t held = 0;
+#pragma unroll
+  for (int i = 0; i < kMergeItems; ++i) {
+    const uint32_t q = static_cast<uint32_t>(tid + kSelThreads * i);
+    key[i] = 0u;
+    slot[i] = 0;
+    if (q < nc) {
+      int lo = 0, hi = P.chunks - 1;  // last list c with sh_off[c] <= q
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sh_off[mid] <= q) lo = mid; else hi = mid - 1;
+      }
+      const uint2 v = P.cand[(static_cast<size_t>(b) * P.chunks + lo) * P.chunk_keys + (q - sh_off[lo])];
+      const int pos = static_cast<int>(v.y), blk = pos / P.Bk;
+      int r = kn;  // the partial block before the window
+      if (blk < nb) {
+        int a = 0, z = kn - 1;  // kept blocks ascending
+        while (a < z) {
+          const int mid = (a + z) >> 1;
+          if (sh_kept[mid] < blk) a = mid + 1; else z = mid;
+        }
+        r = a;
+      }
+      key[i] = v.x;
+      slot[i] = r * P.Bk + (pos - blk * P.Bk);
+      held |= 1u << i;
+    }
+  }
+  // the R-th largest key
+  uint32_t want = static_cast<uint32_t>(R), pref = 0;
+  for (int round = 0; round < 3; ++round) {
+    const int shift = round == 0 ? 20 : round == 1 ? 8 : 0;
+    const int prev = round == 1 ? 20 : 8;
+    const uint32_t mask = round < 2 ? 0xfffu : 0xffu;
+    for (int i = tid; i < sel::kBins; i += kSelThreads) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kMergeItems; ++i)
+      if ((held >> i & 1u) && (round == 0 || (key[i] >> prev) == pref))
+        atomicAdd(&hist[sel::bin_slot<kSelThreads>((key[i] >> shift) & mask)], 1u);
+    __syncthreads();
+    uint32_t c[kSelPer];
+#pragma unroll
+    for (int i = 0; i < kSelPer; ++i) c[i] = hist[i * kSelThreads + tid];
+    sel::select_bin<kSelPer, kSelWaves>(c, want, sh_scan, sh_res);
+    want -= sh_res[1];
+    pref = (pref << (round < 2 ? 12 : 8)) | sh_res[0];
+  }
+  // winners: keys above pref, and the `want` lowest slots whose key equals it
+  const int words = ((kn + 1) * P.Bk + 31) / 32;
+  for (int i = tid; i < words; i += kSelThreads) win[i] = tie[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kMergeItems; ++i) {
+    if (!(held >> i & 1u)) continue;
+    if (key[i] > pref) atomicOr(&win[slot[i] >> 5], 1u << (slot[i] & 31));
+    else if (key[i] == pref) atomicOr(&tie[slot[i] >> 5], 1u << (slot[i] & 31));
+  }
+  __syncthreads();
+  const int wpt = (words + kSelThreads - 1) / kSelThreads;
+  const int w0 = tid * wpt, w1 = min(words, w0 + wpt);
+  uint32_t mine = 0, total;
+  for (int w = w0; w < w1; ++w) mine += __popc(tie[w]);
+  uint32_t rank = sel::block_prefix<kSelWaves>(mine, sh_scan, &total);
+  for (int w = w0; w < w1 && rank < want; ++w) {
+    uint32_t bits = tie[w];
+    while (bits && rank < want) {
+      const uint32_t low = bits & (~bits + 1u);
+      win[w] |= low;
+      bits ^= low;
+      ++rank;
+    }
+  }
+  __syncthreads();
+  mine = 0;
+  for (int w = w0; w < w1; ++w) mine += __popc(win[w]);
+  uint32_t at = sel::block_prefix<kSelWaves>(mine, sh_scan, &total);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t bits = win[w];
+    while (bits) {
+      const int sl = 32 * w + __ffs(bits) - 1;
+      bits &= bits - 1;
+      const int r = sl / P.Bk, o = sl - r * P.Bk;
+      if (at < static_cast<uint32_t>(R)) out[I + at] = (r < kn ? sh_kept[r] : nb) * P.Bk + o;
+      ++at;
+    }
+  }
+}
+
 size_t align_up(size_t x) { return (x + kWorkspaceAlign - 1) & ~(kWorkspaceAlign - 1); }
 
 struct HierLayout {
@@ -364,6 +494,12 @@ hipError_t launch_hier_index_topk(const uint16_t* q_idx, const float* w, const u
   hipLaunchKernelGGL(hier_candidates_kernel, dim3(static_cast<unsigned>((tiles + 3) / 4), static_cast<unsigned>(B)),
                      dim3(kHierThreads), 0, stream, P);
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (static_cast<long>(M + 1) * Bk <= kMaxMergeCand && L.chunks <= kMaxLists) {
+    P.indices = indices;
+    P.n_sel = n_sel;
+    hipLaunchKernelGGL(hier_merge_kernel, dim3(static_cast<unsigned>(B)), dim3(kSelThreads), 0, stream, P);
+    return hipGetLastError();
+  }
   return launch_topk_merge(seqlens, 1, S_max, topk, init, local, 0, B, L.chunks, L.chunk_keys, P.count,
                            P.range, P.cand, indices, n_sel, stream);
 }
