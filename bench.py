@@ -84,6 +84,12 @@ def attn_row_bytes(wl, n, c):
     return rows * wl.Dqk * 2 + wl.H * wl.Dqk * 2 + wl.H * wl.Dv * 2 + wl.topk * 4
 
 
+def attention_call_bytes(wl, c=0):
+    """Algorithmic bytes of attention call c over the whole batch (decode rows)."""
+    return sum(attn_row_bytes(wl, wl.seqlens[b] - wl.Lq + i + 1, c)
+               for b in range(wl.B) for i in range(wl.Lq))
+
+
 def indexer_bytes(wl):
     """Algorithmic bytes of one indexer launch: keys of the visible positions, the index query
     and weights, and the fp32 score written per visible position."""
@@ -401,8 +407,7 @@ def main():
                 else indexer_bytes(wl))
     k1_gbs = k1_bytes / (k1_ms / 1e3) / 1e9
     step_gbs = alg / (ms_per_step / 1e3) / 1e9
-    mla_bytes = [sum(attn_row_bytes(wl, wl.seqlens[b] - wl.Lq + i + 1, c)
-                     for b in range(wl.B) for i in range(wl.Lq)) for c in range(wl.attn_calls)]
+    mla_bytes = [attention_call_bytes(wl, c) for c in range(wl.attn_calls)]
     if hier:
         # the index pass reads a small fraction of the keys; the attention call dominates
         att_ms = sum(st[2 + c] for st in stage_ms for c in range(wl.attn_calls)) / (
@@ -470,6 +475,8 @@ def main():
     def mean(j):
         return sum(st[j] for st in stage_ms) / args.steps
 
+    mla_ms = [mean(2 + c) for c in range(wl.attn_calls)]
+
     def pct(q):
         return round(step_list[min(len(step_list) - 1, int(q * len(step_list)))], 5) if step_list else None
 
@@ -490,9 +497,13 @@ def main():
         stages["topk_call_ms"] = round(mean(1), 5)
         stages["topk_call_gbs"] = round(topk_bytes / (mean(1) / 1e3) / 1e9, 1)
     for c in range(wl.attn_calls):
-        stages[f"mla{c}_call_ms"] = round(mean(2 + c), 5)
+        stages[f"mla{c}_call_ms"] = round(mla_ms[c], 5)
         if wl.decode:
-            stages[f"mla{c}_call_gbs"] = round(mla_bytes[c] / (mean(2 + c) / 1e3) / 1e9, 1)
+            stages[f"mla{c}_call_gbs"] = round(mla_bytes[c] / (mla_ms[c] / 1e3) / 1e9, 1)
+    att_traffic = load_traffic(wl.name, "attention") if wl.decode and not wl.draft_steps else None
+    if att_traffic:  # counter-measured HBM bytes of one attention call (current sources only)
+        stages["mla_call_traffic_bytes"] = att_traffic
+        stages["mla_call_traffic_over_alg"] = round(att_traffic / mla_bytes[0], 4)
     # the same step with one attention call (the shape of configurations with one sub-block)
     stages["one_mla_step_ms"] = round(mean(0) + mean(1) + mean(2), 5)
     # spread of step times in pass 2 (which carries the boundary events)

@@ -494,14 +494,16 @@ hipError_t launch_hier_index_topk(const uint16_t* q_idx, const float* w, const u
   hipLaunchKernelGGL(hier_candidates_kernel, dim3(static_cast<unsigned>((tiles + 3) / 4), static_cast<unsigned>(B)),
                      dim3(kHierThreads), 0, stream, P);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (static_cast<long>(M + 1) * Bk <= kMaxMergeCand && L.chunks <= kMaxLists) {
+  // the dedicated merge keeps the kept blocks' ids in LDS (sh_kept: kMaxMergeCand / 8 entries)
+  if (static_cast<long>(M + 1) * Bk <= kMaxMergeCand && M <= kMaxMergeCand / 8 &&
+      L.chunks <= kMaxLists) {
     P.indices = indices;
     P.n_sel = n_sel;
     hipLaunchKernelGGL(hier_merge_kernel, dim3(static_cast<unsigned>(B)), dim3(kSelThreads), 0, stream, P);
     return hipGetLastError();
   }
   return launch_topk_merge(seqlens, 1, S_max, topk, init, local, 0, B, L.chunks, L.chunk_keys, P.count,
-                           P.range, P.cand, indices, n_sel, stream);
+                           P.range, P.cand, nullptr, indices, n_sel, stream);
 }
 
 }  // namespace lsa

@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
     float* srow = P.scores + static_cast<size_t>(row) * S_max + start;
     for (int i = threadIdx.x; i < end - start; i += kThreads) srow[i] = stage[i];
   } else {
-    __shared__ uint32_t sh[sel::chunk_scratch_words<kThreads>()];
+    __shared__ uint32_t sh[sel::chunk_scratch_words<kThreads, kStageItems>()];
     const int a = comp_a, z = comp_z;  // competing positions here
     uint32_t key[kStageItems];
     uint32_t valid = 0;
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
       valid |= (ok ? 1u : 0u) << j;
     }
     sel::chunk_candidates<kThreads, kStageItems, true>(
-        key, valid, z - a + 1, P.R, start, hist, sh,
+        key, valid, z - a + 1, P.R, sel::list_cap(P.R), start, hist, sh,
         P.cand + static_cast<size_t>(blockIdx.x) * keys_per_wg, P.count + blockIdx.x,
         P.range + 2 * blockIdx.x, run_mn, run_mx);
   }
@@ -465,10 +465,10 @@ hipError_t launch_any(const IndexParams& P, int Di, long grid, hipStream_t strea
 struct FusedPlan {
   int keys_per_wg = kWgStride, chunks = 1;
   long rows = 0, group = 1;
-  size_t count_bytes = 0, range_bytes = 0, cand_bytes = 0;
+  size_t count_bytes = 0, range_bytes = 0, cand_bytes = 0, level1_bytes = 0;
 };
 
-FusedPlan fused_plan(int B, int Lq, int S_max) {
+FusedPlan fused_plan(int B, int Lq, int S_max, int topk, int init_tokens, int local_tokens) {
   FusedPlan pl;
   pl.rows = static_cast<long>(B) * Lq;
   pl.keys_per_wg = keys_per_workgroup(pl.rows, S_max, true);
@@ -478,6 +478,7 @@ FusedPlan fused_plan(int B, int Lq, int S_max) {
   pl.count_bytes = (static_cast<size_t>(pl.group) * pl.chunks * 4 + 255) & ~static_cast<size_t>(255);
   pl.range_bytes = (static_cast<size_t>(pl.group) * pl.chunks * 8 + 255) & ~static_cast<size_t>(255);
   pl.cand_bytes = static_cast<size_t>(pl.group) * per_row;
+  pl.level1_bytes = topk_merge_level1_bytes(pl.group, pl.chunks, topk, init_tokens, local_tokens);
   return pl;
 }
 
@@ -504,18 +505,15 @@ hipError_t launch_index_scores(const uint16_t* q_idx, const float* w, const uint
 }
 
 size_t index_topk_workspace_bytes(int B, int Lq, int S_max, int topk, int init_tokens, int local_tokens) {
-  (void)topk;
-  (void)init_tokens;
-  (void)local_tokens;
-  const FusedPlan pl = fused_plan(B, Lq, S_max);
-  return pl.count_bytes + pl.range_bytes + pl.cand_bytes + kWorkspaceAlign;
+  const FusedPlan pl = fused_plan(B, Lq, S_max, topk, init_tokens, local_tokens);
+  return pl.count_bytes + pl.range_bytes + pl.cand_bytes + pl.level1_bytes + kWorkspaceAlign;
 }
 
 hipError_t launch_index_topk(const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
                              const int32_t* seqlens, int B, int Lq, int Hi, int Di, int S_max,
                              int topk, int init_tokens, int local_tokens, int32_t* indices,
                              int32_t* n_sel, void* workspace, hipStream_t stream) {
-  const FusedPlan pl = fused_plan(B, Lq, S_max);
+  const FusedPlan pl = fused_plan(B, Lq, S_max, topk, init_tokens, local_tokens);
   if (pl.chunks > topk_merge_max_chunks()) return hipErrorInvalidConfiguration;
   IndexParams P{};
   P.q_idx = q_idx;
@@ -535,6 +533,7 @@ hipError_t launch_index_topk(const uint16_t* q_idx, const float* w, const uint16
   P.count = reinterpret_cast<uint32_t*>(ws);
   P.range = reinterpret_cast<uint32_t*>(ws + pl.count_bytes);
   P.cand = reinterpret_cast<uint2*>(ws + pl.count_bytes + pl.range_bytes);
+  void* level1 = pl.level1_bytes ? ws + pl.count_bytes + pl.range_bytes + pl.cand_bytes : nullptr;
   for (long r0 = 0; r0 < pl.rows; r0 += pl.group) {
     const long g = std::min(pl.group, pl.rows - r0);
     P.row0 = static_cast<int>(r0);
@@ -542,7 +541,7 @@ hipError_t launch_index_topk(const uint16_t* q_idx, const float* w, const uint16
     if (err != hipSuccess) return err;
     err = launch_topk_merge(seqlens, Lq, S_max, topk, init_tokens, local_tokens, static_cast<int>(r0),
                             static_cast<int>(g), pl.chunks, pl.keys_per_wg, P.count, P.range, P.cand,
-                            indices, n_sel, stream);
+                            level1, indices, n_sel, stream);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;

@@ -141,12 +141,14 @@ hipError_t launch_topk(const float* scores, const int32_t* seqlens, int B, int L
 // count[r][c] pairs (key, position) at cand[r][c][0 .. count), r relative to row0, each list the
 // candidates of positions [c * chunk_keys, (c + 1) * chunk_keys) (a superset of that chunk's
 // contribution to the row's top R, or all of its middle positions), with range[r][c][0..1]
-// bounding its keys.
+// bounding its keys.  Rows with more than 16 lists are merged in two levels when `level1` (a
+// device region of topk_merge_level1_bytes(rows, chunks, ...) bytes) is given, else in one.
 int topk_merge_max_chunks();
+size_t topk_merge_level1_bytes(long rows, int chunks, int topk, int init_tokens, int local_tokens);
 hipError_t launch_topk_merge(const int32_t* seqlens, int Lq, int S_max, int topk, int init_tokens,
                              int local_tokens, int row0, int rows, int chunks, int chunk_keys,
-                             uint32_t* count, uint32_t* range, uint2* cand, int32_t* indices,
-                             int32_t* n_sel, hipStream_t stream);
+                             uint32_t* count, uint32_t* range, uint2* cand, void* level1,
+                             int32_t* indices, int32_t* n_sel, hipStream_t stream);
 
 // Indexer and top-k in one pass: the scores never leave the chip.
 size_t index_topk_workspace_bytes(int B, int Lq, int S_max, int topk, int init_tokens, int local_tokens);

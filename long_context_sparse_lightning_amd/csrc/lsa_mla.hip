@@ -50,6 +50,7 @@ constexpr int kMaxRowsPerSplit = 2048;  // row positions of a split staged in LD
 constexpr int kPartStride = 20;   // floats per head in the partial-logit exchange (16 rows + pad)
 constexpr int kTargetWorkgroups = 512;  // two per CU
 constexpr int kCombineThreads = 256;   // four (row, head) pairs per workgroup
+constexpr int kXcds = 8;               // accelerator complex dies (one L2 each)
 constexpr float kRescaleSlack = 8.0f;   // log2 units the running max may exceed the reference
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -95,6 +96,7 @@ struct MlaParams {
   const int32_t* index_seqlens;
   int max_app;
   int Lq, H, S_max, topk;
+  int rows;                  // query rows (B * Lq)
   int hgroups, splits, kps;  // head groups, workgroups per (row, head group), rows per split
   int pairs;                 // query rows x heads
   float scale_log2;
@@ -108,13 +110,11 @@ struct MlaParams {
 // lds_base + 16 * lane.  It is issued from inline assembly on purpose: the compiler's waitcnt
 // pass would otherwise treat every later LDS transpose read as possibly aliasing an unfinished
 // DMA and drain the whole ring (vmcnt(0)) before it.  This kernel tracks the ring itself with
-// explicit vmcnt waits and barriers, and uses M0 for nothing else.  The instruction has no
-// destination registers.
+// explicit vmcnt waits and barriers.  The LDS destination goes in M0 as an input operand bound
+// to that register, so the compiler itself writes M0 and knows what it holds.  The instruction
+// has no destination registers.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(lds_base)
-               : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_base) : "memory");
 }
 
 // Workgroup barrier for the DMA ring.  __syncthreads() also releases this wavefront's pending
@@ -148,11 +148,26 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
   const int col = lane & 31, g = lane >> 5;   // 32x32 layouts
   const int c16 = lane & 15, q16 = lane >> 4;  // 16x16 layouts
-  int bid = blockIdx.x;
-  const int split = bid % P.splits;
-  bid /= P.splits;
-  const int hg = bid % P.hgroups;
-  const int row = bid / P.hgroups;
+  // XCD-aware work order: the dispatcher deals workgroup ids to the 8 XCDs in turn, so id b
+  // runs on XCD b % 8.  XCD x takes a contiguous run of (row, head group) units with all their
+  // splits: a unit's query is then fetched into one L2, and neighbouring prefill rows, whose
+  // selections share the sink and window rows, gather through the same L2.  Units past the
+  // last multiple of 8 keep the plain order.
+  const int bid = blockIdx.x;
+  const int units = P.rows * P.hgroups;
+  const int per_xcd = units / kXcds;  // units per XCD in the XCD-aware part
+  int unit, split;
+  if (bid < per_xcd * kXcds * P.splits) {
+    const int l = bid / kXcds;
+    unit = (bid % kXcds) * per_xcd + l / P.splits;
+    split = l % P.splits;
+  } else {
+    const int r = bid - per_xcd * kXcds * P.splits;
+    unit = per_xcd * kXcds + r / P.splits;
+    split = r % P.splits;
+  }
+  const int hg = unit % P.hgroups;
+  const int row = unit / P.hgroups;
   const int b = row / P.Lq;
   const int n = min(P.seqlens[b] - P.Lq + (row - b * P.Lq) + 1, P.S_max);
   constexpr bool sparse = SPARSE;
@@ -597,6 +612,7 @@ hipError_t launch_mla(const uint16_t* q, const uint16_t* kv, const int32_t* indi
   P.H = H;
   P.S_max = S_max;
   P.topk = topk;
+  P.rows = static_cast<int>(rows);
   P.hgroups = pl.hgroups;
   P.splits = pl.splits;
   P.kps = pl.kps;

@@ -122,30 +122,42 @@ __device__ __forceinline__ int digit_shift(uint32_t mn, uint32_t mx) {
   return max(0, bits - 11);
 }
 
-// LDS words chunk_candidates needs besides its histogram.
-template <int THREADS>
-constexpr int chunk_scratch_words() { return 3 * (THREADS / kWave) + 4; }
+// Most pairs a chunk list keeps for R free slots: the superset rule's list grows past R only by
+// the keys that share the R-th largest's digit; beyond R + R/4 the list is cut to the exact top R.
+// (The merge holds R + R/4 <= 1280 candidates per list in registers at R = 1008.)
+__host__ __device__ constexpr int list_cap(int R) { return R + (R >> 2); }
+
+// LDS words chunk_candidates needs besides its histogram (ITEMS: items per thread).
+template <int THREADS, int ITEMS = 32>
+constexpr int chunk_scratch_words() { return 3 * (THREADS / kWave) + 8 + ITEMS; }
 
 // Candidates of one chunk: item j of this thread (bit j of `valid`) holds the key at position
 // base + j*THREADS + threadIdx.x; m = number of valid items in the workgroup.  Writes to `out`
-// every valid key when m <= R, else those whose digit is at least that of the chunk's R-th
-// largest (always a superset of the chunk's contribution to the row's top R), as (key,
-// position) pairs, their number to *count, and bounds lo <= every written key <= hi to
-// range[0], range[1].  hist: 2*kBins words of LDS, zeroed here; sh:
-// chunk_scratch_words<THREADS>() words.  Call from every thread, with m >= 1.
+// every valid key when m <= R, else a superset of the chunk's contribution to the row's top R:
+// every key whose digit is at least that of the chunk's R-th largest.  When that superset would
+// exceed `cap` pairs (cap >= R; many keys share the R-th largest's digit), narrower digits are
+// taken inside the boundary bin until it fits, and if a single key value remains, the lowest
+// positions among its copies fill the list up to exactly R -- the chunk's exact top R by (key
+// descending, position ascending), which still holds every row winner from this chunk.  The
+// pairs (key, position) go to `out`, their number to *count, and bounds lo <= every written
+// key <= hi to range[0], range[1].  hist: 2*kBins words of LDS, zeroed here; sh:
+// chunk_scratch_words<THREADS, ITEMS>() words.  Call from every thread, with m >= 1.
 // PREPARED: the caller has already zeroed hist (and ordered that before this call by a
 // barrier) and passes in (mn, mx) bounds whose workgroup-wide min and max are those of the
 // valid keys -- a scan that produced the keys can track them on the way.
 template <int THREADS, int ITEMS, bool PREPARED = false>
 __device__ void chunk_candidates(const uint32_t (&key)[ITEMS], uint32_t valid, int m, int R,
-                                 int base, uint32_t* hist, uint32_t* sh, uint2* out,
+                                 int cap, int base, uint32_t* hist, uint32_t* sh, uint2* out,
                                  uint32_t* count, uint32_t* range, uint32_t mn = 0xffffffffu,
                                  uint32_t mx = 0u) {
   constexpr int WAVES = THREADS / kWave;
+  constexpr int kPer = kBins / THREADS;
+  static_assert(ITEMS <= 32, "valid/keep masks are 32 bits");
   uint32_t* sh_scan = sh;
   uint32_t* sh_mm = sh + WAVES;
   uint32_t* sh_out = sh + 3 * WAVES;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  uint32_t* sh_tie = sh + 3 * WAVES + 8;  // [ITEMS] tied items per item index
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
   uint32_t keep = valid;
   if constexpr (!PREPARED) {
     if (m > R)  // hist is 16-byte aligned
@@ -161,24 +173,81 @@ __device__ void chunk_candidates(const uint32_t (&key)[ITEMS], uint32_t valid, i
   block_minmax<WAVES>(mn, mx, sh_mm);  // its barrier also orders the zeroing
   uint32_t lo = mn;
   if (m > R) {
-    const int sh_bits = digit_shift(mn, mx);
-    const uint32_t dbase = mn >> sh_bits;
+    int s_in = digit_shift(mn, mx);
+    const uint32_t dbase = mn >> s_in;
     uint32_t* hw = hist + (wave & 1) * kBins;  // one copy per half of the waves
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j)
-      if (valid & (1u << j)) atomicAdd(&hw[bin_slot<THREADS>((key[j] >> sh_bits) - dbase)], 1u);
+      if (valid & (1u << j)) atomicAdd(&hw[bin_slot<THREADS>((key[j] >> s_in) - dbase)], 1u);
     __syncthreads();
-    constexpr int kPer = kBins / THREADS;
     uint32_t c[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) c[i] = hist[i * THREADS + tid] + hist[kBins + i * THREADS + tid];
     select_bin<kPer, WAVES>(c, static_cast<uint32_t>(R), sh_scan, sh_out);
-    const uint32_t dmin = sh_out[0];
-    lo = (dbase + dmin) << sh_bits;  // no kept key is below the first kept digit
+    // boundary bin: keys with (k >> s_in) == pref; `above` keys lie above it
+    uint32_t pref = dbase + sh_out[0], above = sh_out[1], inbin = sh_out[2];
+    bool tie_break = false;  // the boundary holds one key value; only some of its copies are kept
+    uint32_t need = static_cast<uint32_t>(R) - above;
+    while (above + inbin > static_cast<uint32_t>(cap)) {
+      if (s_in == 0) {
+        tie_break = true;
+        break;
+      }
+      const int s2 = max(0, s_in - 12);
+      const uint32_t base2 = pref << (s_in - s2);  // digits below 2^12 = kBins
+      for (int i = tid; i < kBins; i += THREADS) hist[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j)
+        if ((valid & (1u << j)) && (key[j] >> s_in) == pref)
+          atomicAdd(&hist[bin_slot<THREADS>((key[j] >> s2) - base2)], 1u);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) c[i] = hist[i * THREADS + tid];
+      select_bin<kPer, WAVES>(c, need, sh_scan, sh_out);
+      pref = base2 + sh_out[0];
+      above += sh_out[1];
+      need -= sh_out[1];
+      inbin = sh_out[2];
+      s_in = s2;
+    }
+    lo = pref << s_in;  // no kept key is below the boundary bin
     keep = 0;
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j)
-      keep |= ((valid & (1u << j)) && (key[j] >> sh_bits) - dbase >= dmin ? 1u : 0u) << j;
+      keep |= ((valid & (1u << j)) && (key[j] >> s_in) >= pref ? 1u : 0u) << j;
+    if (tie_break) {
+      // `inbin` copies of the key `pref` and `need` of them kept: the lowest positions, i.e. by
+      // item index j, then thread -- count the copies per j, find the item index j* where the
+      // count reaches `need`, and rank the copies at j* by thread
+      if (tid < ITEMS) sh_tie[tid] = 0u;
+      __syncthreads();
+      uint32_t tied = 0;
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j) {
+        const bool t = (valid & (1u << j)) && key[j] == pref;
+        tied |= (t ? 1u : 0u) << j;
+        const uint32_t n = static_cast<uint32_t>(__popcll(wave_ballot(t)));
+        if (lane == 0 && n) atomicAdd(&sh_tie[j], n);
+      }
+      __syncthreads();
+      uint32_t before = 0;
+      int jstar = ITEMS;
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j) {
+        const uint32_t n = sh_tie[j];
+        if (jstar == ITEMS && before + n >= need) jstar = j;
+        else if (jstar == ITEMS) before += n;
+      }
+      uint32_t total;
+      const uint32_t rank = block_prefix<WAVES>(jstar < ITEMS ? (tied >> jstar) & 1u : 0u, sh_scan, &total);
+      // copies at j < j* are kept, at j* the first need - before by thread, after j* none
+      const uint32_t lower = (jstar >= 32) ? 0xffffffffu : ((1u << jstar) - 1u);
+      uint32_t drop = tied & ~lower;
+      if (jstar < ITEMS && rank < need - before) drop &= ~(1u << jstar);
+      keep &= ~drop;
+      __syncthreads();  // every thread has read sh_scan before the stores below reuse it
+    }
   }
   // Stores: the kept items of one wavefront and one item index j go to one contiguous run
   // (ordered by wavefront, then j, then lane; the list is a set).

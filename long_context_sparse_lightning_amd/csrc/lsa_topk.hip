@@ -49,28 +49,36 @@ constexpr int kMergeWaves = kMergeThreads / kWave;
 constexpr int kRegItems = 20;        // candidates held in registers per merge thread
 constexpr int kMaxPositions = 1 << 20;
 constexpr int kMaxChunks = 128;      // chunk lists per row the merge accepts
+constexpr int kGroupLists = 16;      // lists per first-level merge when a row has more
 constexpr int kTieList = kMergeThreads;             // ties ranked in LDS up to this many
 constexpr size_t kWorkspaceBudget = size_t(1024) << 20;
+static_assert(kMaxChunks <= kGroupLists * kGroupLists, "two merge levels cover every row");
 
 struct TopkParams {
   const float* scores;
   const int32_t* seqlens;
   int Lq, S_max, topk, init, local, R;
+  int cap;           // most pairs a chunk list holds (sel::chunk_candidates)
   int row0;          // first row of this group
   int chunks;        // chunk lists per row
-  int chunk_keys;    // positions per chunk (= capacity of its list)
+  int chunk_keys;    // capacity of each list
   uint32_t* count;   // [group rows][chunks]
   uint32_t* range;   // [group rows][chunks][2] bounds of each list's keys
   uint2* cand;       // [group rows][chunks][chunk_keys] (key, position)
   int32_t* indices;  // [rows][topk]
   int32_t* n_sel;    // [rows]
+  // first-level merge (lists [g * kGroupLists, ...) of a row -> one list of its exact top R):
+  int groups;        // first-level lists per row
+  uint32_t* g_count;  // [group rows][groups]
+  uint32_t* g_range;  // [group rows][groups][2]
+  uint2* g_cand;      // [group rows][groups][R]
 };
 
 // ------------------------------------------------------------------ 1. per-chunk candidates
 // at most 128 VGPRs, so two 512-thread workgroups share a CU and overlap their load waits
 __global__ __launch_bounds__(kChunkThreads, 4) void topk_chunk_kernel(TopkParams P) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[2 * kBins];
-  __shared__ uint32_t sh[sel::chunk_scratch_words<kChunkThreads>()];
+  __shared__ uint32_t sh[sel::chunk_scratch_words<kChunkThreads, kChunkItems>()];
   const int tid = threadIdx.x;
   const int grow = blockIdx.x / P.chunks;  // row within the group
   const int chunk = blockIdx.x - grow * P.chunks;
@@ -93,7 +101,7 @@ __global__ __launch_bounds__(kChunkThreads, 4) void topk_chunk_kernel(TopkParams
     key[j] = order_key(srow[min(max(s, a), z)]);
     valid |= ((s >= a && s <= z) ? 1u : 0u) << j;
   }
-  sel::chunk_candidates<kChunkThreads, kChunkItems>(key, valid, m, P.R, base, hist, sh,
+  sel::chunk_candidates<kChunkThreads, kChunkItems>(key, valid, m, P.R, P.cap, base, hist, sh,
                                                     P.cand + static_cast<size_t>(blockIdx.x) * kChunk,
                                                     P.count + blockIdx.x, P.range + 2 * blockIdx.x);
 }
@@ -109,6 +117,15 @@ static_assert(kMaxChunks <= kMergeThreads, "one thread per chunk list");
 constexpr int kMsBits = kMsHist + kBins;            // bitmap over the middle range
 static_assert(2 * kTieList <= kBins, "the rank list reuses the histogram");
 
+// One workgroup merges candidate lists into an exact top R by (key descending, position
+// ascending).  LIST_OUT = false: the row's final selection -- grid (rows), all `chunks` lists of
+// the row; winners are set in an LDS bitmap over the middle range and compacted into ascending
+// indices between the forced sink and window.  LIST_OUT = true: a first-level merge -- grid
+// (rows * groups), lists [g * kGroupLists, ...) of the row; the winners (min(R, candidates) of
+// them) are written as an unordered (key, position) list for the final merge, which sees each
+// group as one list.  Any top R of a union contains the top R of the whole row that falls in it
+// (the order is total), so the two levels select exactly what one merge would.
+template <bool LIST_OUT>
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   uint32_t* sh_scan = lds + kMsScan;
@@ -119,34 +136,49 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
   int32_t* sh_lp = reinterpret_cast<int32_t*>(lds + kMsHist + kTieList);  // rank list positions
   uint32_t* sh_bits = lds + kMsBits;
   const int tid = threadIdx.x;
-  const int grow = blockIdx.x;
+  const int grow = LIST_OUT ? static_cast<int>(blockIdx.x) / P.groups : static_cast<int>(blockIdx.x);
+  const int grp = LIST_OUT ? static_cast<int>(blockIdx.x) - grow * P.groups : 0;
+  const int c0 = LIST_OUT ? grp * kGroupLists : 0;                  // first list of this merge
+  const int nl = LIST_OUT ? min(kGroupLists, P.chunks - c0) : P.chunks;  // lists of this merge
   const int row = P.row0 + grow;
   const RowGeom g = row_geom(P.seqlens, row, P.Lq, P.S_max, P.topk, P.init, P.local);
   const int K = P.topk, I = P.init, W = P.local, R = P.R;
   int32_t* out = P.indices + static_cast<size_t>(row) * K;
-  if (g.dense) {  // every visible position, then padding
-    for (int j = tid; j < K; j += kMergeThreads) out[j] = j < g.n ? j : -1;
-    if (tid == 0) P.n_sel[row] = max(g.n, 0);
-    return;
+  uint2* gout = LIST_OUT ? P.g_cand + static_cast<size_t>(blockIdx.x) * R : nullptr;
+  if constexpr (LIST_OUT) {
+    if (g.dense || R == 0) {  // the final merge writes these rows without candidates
+      if (tid == 0) P.g_count[blockIdx.x] = 0u;
+      return;
+    }
+  } else {
+    if (g.dense) {  // every visible position, then padding
+      for (int j = tid; j < K; j += kMergeThreads) out[j] = j < g.n ? j : -1;
+      if (tid == 0) P.n_sel[row] = max(g.n, 0);
+      return;
+    }
+    // forced positions: the I lowest and the W highest fill the ends of the output
+    for (int j = tid; j < I; j += kMergeThreads) out[j] = j;
+    for (int j = tid; j < W; j += kMergeThreads) out[K - W + j] = g.p - W + 1 + j;
+    if (tid == 0) P.n_sel[row] = K;
+    if (R == 0) return;
   }
-  // forced positions: the I lowest and the W highest fill the ends of the output
-  for (int j = tid; j < I; j += kMergeThreads) out[j] = j;
-  for (int j = tid; j < W; j += kMergeThreads) out[K - W + j] = g.p - W + 1 + j;
-  if (tid == 0) P.n_sel[row] = K;
-  if (R == 0) return;
 
   const int mid_words = (g.hi - g.lo + 32) >> 5;
-  for (int i = tid; i < mid_words; i += kMergeThreads) sh_bits[i] = 0u;
+  if constexpr (!LIST_OUT)
+    for (int i = tid; i < mid_words; i += kMergeThreads) sh_bits[i] = 0u;
   for (int i = tid; i < kBins; i += kMergeThreads) sh_h[i] = 0u;
-  if (tid == 0) sh_res[8] = 0u;  // rank-list length
-  // list lengths and key bounds (thread c: list c), requested first: loads complete in order
-  const size_t lc = static_cast<size_t>(grow) * P.chunks + tid;
-  const uint32_t c_len = tid < P.chunks ? P.count[lc] : 0u;
-  const uint32_t c_lo = tid < P.chunks ? P.range[2 * lc] : 0xffffffffu;
-  const uint32_t c_hi = tid < P.chunks ? P.range[2 * lc + 1] : 0u;
+  if (tid == 0) {
+    sh_res[8] = 0u;   // rank-list length
+    sh_res[12] = 0u;  // winners written (LIST_OUT)
+  }
+  // list lengths and key bounds (thread c: list c0 + c), requested first: loads complete in order
+  const size_t lc = static_cast<size_t>(grow) * P.chunks + c0 + tid;
+  const uint32_t c_len = tid < nl ? P.count[lc] : 0u;
+  const uint32_t c_lo = tid < nl ? P.range[2 * lc] : 0xffffffffu;
+  const uint32_t c_hi = tid < nl ? P.range[2 * lc + 1] : 0u;
   const size_t ck = static_cast<size_t>(P.chunk_keys);
-  const uint2* crow = P.cand + static_cast<size_t>(grow) * P.chunks * ck;
-  // candidate offsets of the row's lists (thread c: list c), the longest list, the key bounds
+  const uint2* crow = P.cand + (static_cast<size_t>(grow) * P.chunks + c0) * ck;
+  // candidate offsets of the lists (thread c: list c), the longest list, the key bounds
   if (tid == 0) {
     sh_res[9] = 0u;
     sh_res[10] = 0xffffffffu;
@@ -155,7 +187,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
   {
     uint32_t total;
     const uint32_t at = block_prefix<kMergeWaves>(c_len, sh_scan, &total);
-    if (tid < P.chunks) {
+    if (tid < nl) {
       sh_off[tid] = at;
       atomicMax(&sh_res[9], c_len);
       if (c_len > 0) {
@@ -169,7 +201,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
   const uint32_t nc = sh_off[kMaxChunks];
   // candidate q of the concatenated lists -> its pair
   auto locate = [&](uint32_t q) -> const uint2* {
-    int lo = 0, hi = P.chunks - 1;  // last chunk c with sh_off[c] <= q
+    int lo = 0, hi = nl - 1;  // last list c with sh_off[c] <= q
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (sh_off[mid] <= q) lo = mid; else hi = mid - 1;
@@ -178,7 +210,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
   };
   // in registers: list c is held by the TPL threads [c * TPL, (c + 1) * TPL), entry j of it by
   // thread c * TPL + j % TPL in slot j / TPL -- when every list fits
-  const int tpl = kMergeThreads / P.chunks;
+  const int tpl = kMergeThreads / nl;
   const int my_list = tid / tpl, my_j = tid - my_list * tpl;
   const bool in_regs = sh_res[9] <= static_cast<uint32_t>(kRegItems * tpl);
   uint32_t rk[kRegItems];
@@ -186,8 +218,8 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
   uint32_t held = 0;  // bit i: slot i holds a candidate
   if (in_regs) {
     const uint32_t my_cnt =
-        my_list < P.chunks ? (my_list + 1 < P.chunks ? sh_off[my_list + 1] : nc) - sh_off[my_list] : 0u;
-    const uint2* lst = crow + static_cast<size_t>(my_list < P.chunks ? my_list : 0) * ck;
+        my_list < nl ? (my_list + 1 < nl ? sh_off[my_list + 1] : nc) - sh_off[my_list] : 0u;
+    const uint2* lst = crow + static_cast<size_t>(my_list < nl ? my_list : 0) * ck;
 #pragma unroll
     for (int i = 0; i < kRegItems; ++i) {  // all loads issued at once, from in-range addresses
       const uint32_t j = static_cast<uint32_t>(my_j + i * tpl);
@@ -210,110 +242,157 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
       }
     }
   };
-  // radix rounds over adaptive digits.  Keys still in play are those with (k >> s_in) == pref
-  // (all of them while s_in == 32); a round histograms the digit (k >> s) - dbase of those keys,
-  // finds the digit of the need-th largest and narrows to it.  The first window comes from the
-  // key bounds the chunk lists carry.
-  const uint32_t mn = sh_res[10], mx = sh_res[11];
-  int s_in = 32, s = digit_shift(mn, mx);
-  uint32_t pref = 0, dbase = mn >> s;
-  uint32_t need = static_cast<uint32_t>(R), pop;
-  auto in_play = [&](uint32_t k) { return s_in >= 32 || (k >> s_in) == pref; };
-  for (;;) {
-    each([&](uint32_t k, int32_t) {
-      if (in_play(k)) atomicAdd(&sh_h[bin_slot<kMergeThreads>((k >> s) - dbase)], 1u);
-    });
-    __syncthreads();
-    constexpr int kPer = kBins / kMergeThreads;
-    uint32_t c[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) c[i] = sh_h[i * kMergeThreads + tid];
-    select_bin<kPer, kMergeWaves>(c, need, sh_scan, sh_res);
-    need -= sh_res[1];
-    pop = sh_res[2];
-    pref = dbase + sh_res[0];
-    s_in = s;
-    if (pop <= static_cast<uint32_t>(kTieList) || s == 0) break;
-    const int s_next = max(0, s - 12);
-    dbase = pref << (s - s_next);
-    s = s_next;
-    for (int i = tid; i < kBins; i += kMergeThreads) sh_h[i] = 0u;
-    __syncthreads();
-  }
-  // keys above the final bin win; `need` of the `pop` keys in it win too
   const int lo = g.lo;
-  auto set_bit = [&](int32_t p) { atomicOr(&sh_bits[(p - lo) >> 5], 1u << ((p - lo) & 31)); };
-  each([&](uint32_t k, int32_t p) {
-    if ((k >> s_in) > pref || (need == pop && (k >> s_in) == pref)) set_bit(p);
-  });
-  if (need < pop) {
-    if (pop <= static_cast<uint32_t>(kTieList)) {
-      // rank the bin's keys by (key descending, position ascending)
-      each([&](uint32_t k, int32_t p) {
-        if ((k >> s_in) == pref) {
-          const uint32_t slot = atomicAdd(&sh_res[8], 1u);
-          sh_lk[slot] = k;
-          sh_lp[slot] = p;
-        }
+  // a winner: a bit in the middle bitmap, or (LIST_OUT) a pair of the output list
+  auto win = [&](uint32_t k, int32_t p) {
+    if constexpr (LIST_OUT) {
+      gout[atomicAdd(&sh_res[12], 1u)] = make_uint2(k, static_cast<uint32_t>(p));
+    } else {
+      atomicOr(&sh_bits[(p - lo) >> 5], 1u << ((p - lo) & 31));
+    }
+  };
+  const uint32_t mn = sh_res[10], mx = sh_res[11];
+  uint32_t out_lo = mn;  // lower bound of the winners' keys (LIST_OUT)
+  if (nc <= static_cast<uint32_t>(R)) {
+    // every candidate wins (a first-level group with few positions; the final merge always has
+    // more candidates than R, since each chunk keeps at least min(R, its positions))
+    each([&](uint32_t k, int32_t p) { win(k, p); });
+  } else {
+    // radix rounds over adaptive digits.  Keys still in play are those with (k >> s_in) == pref
+    // (all of them while s_in == 32); a round histograms the digit (k >> s) - dbase of those
+    // keys, finds the digit of the need-th largest and narrows to it.  The first window comes
+    // from the key bounds the lists carry.
+    int s_in = 32, s = digit_shift(mn, mx);
+    uint32_t pref = 0, dbase = mn >> s;
+    uint32_t need = static_cast<uint32_t>(R), pop;
+    auto in_play = [&](uint32_t k) { return s_in >= 32 || (k >> s_in) == pref; };
+    for (;;) {
+      each([&](uint32_t k, int32_t) {
+        if (in_play(k)) atomicAdd(&sh_h[bin_slot<kMergeThreads>((k >> s) - dbase)], 1u);
       });
       __syncthreads();
-      if (static_cast<uint32_t>(tid) < pop) {
-        const uint32_t kt = sh_lk[tid];
-        const int32_t pt = sh_lp[tid];
-        uint32_t rank = 0;
-        for (uint32_t u = 0; u < pop; ++u) {
-          const uint32_t ku = sh_lk[u];
-          rank += (ku > kt || (ku == kt && sh_lp[u] < pt)) ? 1u : 0u;
-        }
-        if (rank < need) set_bit(pt);
-      }
-    } else {
-      // more than kTieList equal keys (s_in == 0): the `need` lowest positions among them, by a
-      // radix select on the position (below 2^20): its top 12 bits, then its low 8.  Digits are
-      // mirrored so that select_bin's target-th largest is the target-th lowest position.
       constexpr int kPer = kBins / kMergeThreads;
-      uint32_t want = need, hi_digit = 0, cut = 0;
-      for (int round = 0; round < 2; ++round) {
-        for (int i = tid; i < kBins; i += kMergeThreads) sh_h[i] = 0u;
-        __syncthreads();
+      uint32_t c[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) c[i] = sh_h[i * kMergeThreads + tid];
+      select_bin<kPer, kMergeWaves>(c, need, sh_scan, sh_res);
+      need -= sh_res[1];
+      pop = sh_res[2];
+      pref = dbase + sh_res[0];
+      s_in = s;
+      if (pop <= static_cast<uint32_t>(kTieList) || s == 0) break;
+      const int s_next = max(0, s - 12);
+      dbase = pref << (s - s_next);
+      s = s_next;
+      for (int i = tid; i < kBins; i += kMergeThreads) sh_h[i] = 0u;
+      __syncthreads();
+    }
+    out_lo = pref << s_in;
+    // keys above the final bin win; `need` of the `pop` keys in it win too
+    each([&](uint32_t k, int32_t p) {
+      if ((k >> s_in) > pref || (need == pop && (k >> s_in) == pref)) win(k, p);
+    });
+    if (need < pop) {
+      if (pop <= static_cast<uint32_t>(kTieList)) {
+        // rank the bin's keys by (key descending, position ascending)
         each([&](uint32_t k, int32_t p) {
-          const uint32_t u = static_cast<uint32_t>(p);
-          if (k != pref) return;
-          if (round == 0) atomicAdd(&sh_h[bin_slot<kMergeThreads>(kBins - 1 - (u >> 8))], 1u);
-          else if ((u >> 8) == hi_digit) atomicAdd(&sh_h[bin_slot<kMergeThreads>(kBins - 1 - (u & 255u))], 1u);
+          if ((k >> s_in) == pref) {
+            const uint32_t slot = atomicAdd(&sh_res[8], 1u);
+            sh_lk[slot] = k;
+            sh_lp[slot] = p;
+          }
         });
         __syncthreads();
-        uint32_t c[kPer];
+        if (static_cast<uint32_t>(tid) < pop) {
+          const uint32_t kt = sh_lk[tid];
+          const int32_t pt = sh_lp[tid];
+          uint32_t rank = 0;
+          for (uint32_t u = 0; u < pop; ++u) {
+            const uint32_t ku = sh_lk[u];
+            rank += (ku > kt || (ku == kt && sh_lp[u] < pt)) ? 1u : 0u;
+          }
+          if (rank < need) win(kt, pt);
+        }
+      } else {
+        // more than kTieList equal keys (s_in == 0): the `need` lowest positions among them, by
+        // a radix select on the position (below 2^20): its top 12 bits, then its low 8.  Digits
+        // are mirrored so that select_bin's target-th largest is the target-th lowest position.
+        constexpr int kPer = kBins / kMergeThreads;
+        uint32_t want = need, hi_digit = 0, cut = 0;
+        for (int round = 0; round < 2; ++round) {
+          for (int i = tid; i < kBins; i += kMergeThreads) sh_h[i] = 0u;
+          __syncthreads();
+          each([&](uint32_t k, int32_t p) {
+            const uint32_t u = static_cast<uint32_t>(p);
+            if (k != pref) return;
+            if (round == 0) atomicAdd(&sh_h[bin_slot<kMergeThreads>(kBins - 1 - (u >> 8))], 1u);
+            else if ((u >> 8) == hi_digit) atomicAdd(&sh_h[bin_slot<kMergeThreads>(kBins - 1 - (u & 255u))], 1u);
+          });
+          __syncthreads();
+          uint32_t c[kPer];
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) c[i] = sh_h[i * kMergeThreads + tid];
-        select_bin<kPer, kMergeWaves>(c, want, sh_scan, sh_res);
-        want -= sh_res[1];
-        const uint32_t d = kBins - 1 - sh_res[0];
-        if (round == 0) hi_digit = d;
-        else cut = (hi_digit << 8) | d;
+          for (int i = 0; i < kPer; ++i) c[i] = sh_h[i * kMergeThreads + tid];
+          select_bin<kPer, kMergeWaves>(c, want, sh_scan, sh_res);
+          want -= sh_res[1];
+          const uint32_t d = kBins - 1 - sh_res[0];
+          if (round == 0) hi_digit = d;
+          else cut = (hi_digit << 8) | d;
+        }
+        each([&](uint32_t k, int32_t p) {
+          if (k == pref && static_cast<uint32_t>(p) <= cut) win(k, p);
+        });
       }
-      each([&](uint32_t k, int32_t p) {
-        if (k == pref && static_cast<uint32_t>(p) <= cut) set_bit(p);
-      });
     }
   }
   __syncthreads();
-  // compact the middle bitmap into out[I .. I + R)
-  const int wpt = (mid_words + kMergeThreads - 1) / kMergeThreads;
-  const int w0 = tid * wpt, w1 = min(mid_words, w0 + wpt);
-  uint32_t mine = 0;
-  for (int w = w0; w < w1; ++w) mine += __popc(sh_bits[w]);
-  uint32_t total;
-  uint32_t at = block_prefix<kMergeWaves>(mine, sh_scan, &total);
-  for (int w = w0; w < w1; ++w) {
-    uint32_t bits = sh_bits[w];
-    while (bits) {
-      const int b = __ffs(bits) - 1;
-      bits &= bits - 1;
-      if (at < static_cast<uint32_t>(R)) out[I + at] = lo + 32 * w + b;
-      ++at;
+  if constexpr (LIST_OUT) {
+    if (tid == 0) {
+      P.g_count[blockIdx.x] = sh_res[12];
+      P.g_range[2 * blockIdx.x] = out_lo;
+      P.g_range[2 * blockIdx.x + 1] = mx;
     }
+  } else {
+    // compact the middle bitmap into out[I .. I + R)
+    const int wpt = (mid_words + kMergeThreads - 1) / kMergeThreads;
+    const int w0 = tid * wpt, w1 = min(mid_words, w0 + wpt);
+    uint32_t mine = 0;
+    for (int w = w0; w < w1; ++w) mine += __popc(sh_bits[w]);
+    uint32_t total;
+    uint32_t at = block_prefix<kMergeWaves>(mine, sh_scan, &total);
+    for (int w = w0; w < w1; ++w) {
+      uint32_t bits = sh_bits[w];
+      while (bits) {
+        const int b = __ffs(bits) - 1;
+        bits &= bits - 1;
+        if (at < static_cast<uint32_t>(R)) out[I + at] = lo + 32 * w + b;
+        ++at;
+      }
+    }
+    // fewer winners than slots only when the lists hold fewer than R candidates (not for valid
+    // inputs); the slots are then padded rather than left stale
+    for (uint32_t j = total + static_cast<uint32_t>(tid); j < static_cast<uint32_t>(R); j += kMergeThreads)
+      out[I + j] = -1;
   }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// First-level merge region for `rows` rows of `chunks` lists (empty when one merge takes them).
+struct Level1 {
+  int groups = 0;
+  size_t count_bytes = 0, range_bytes = 0, cand_bytes = 0;
+  size_t total() const { return count_bytes + range_bytes + cand_bytes; }
+};
+
+Level1 level1_plan(long rows, int chunks, int R) {
+  Level1 l;
+  if (chunks <= kGroupLists || R <= 0) return l;
+  l.groups = (chunks + kGroupLists - 1) / kGroupLists;
+  const size_t lists = static_cast<size_t>(rows) * l.groups;
+  l.count_bytes = align256(lists * 4);
+  l.range_bytes = align256(lists * 8);
+  l.cand_bytes = align256(lists * static_cast<size_t>(R) * sizeof(uint2));
+  return l;
 }
 
 struct Plan {
@@ -321,10 +400,9 @@ struct Plan {
   int R = 0, chunks = 1;
   long group = 1;  // rows per launch pair
   size_t count_bytes = 0, range_bytes = 0, cand_bytes = 0;
-  size_t total() const { return count_bytes + range_bytes + cand_bytes + kWorkspaceAlign; }
+  Level1 l1;
+  size_t total() const { return count_bytes + range_bytes + cand_bytes + l1.total() + kWorkspaceAlign; }
 };
-
-size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 Plan make_plan(int B, int Lq, int S_max, int topk, int init_tokens, int local_tokens) {
   Plan pl;
@@ -336,6 +414,7 @@ Plan make_plan(int B, int Lq, int S_max, int topk, int init_tokens, int local_to
   pl.count_bytes = align256(static_cast<size_t>(pl.group) * pl.chunks * 4);
   pl.range_bytes = align256(static_cast<size_t>(pl.group) * pl.chunks * 8);
   pl.cand_bytes = static_cast<size_t>(pl.group) * per_row;
+  pl.l1 = level1_plan(pl.group, pl.chunks, pl.R);
   return pl;
 }
 
@@ -345,6 +424,7 @@ size_t merge_lds_bytes(int S_max) {
 
 // The attribute is a maximum: it is raised only when a launch needs more than the device's
 // current setting, so calls of different sizes do not reset it back and forth.
+template <bool LIST_OUT>
 hipError_t set_merge_lds(size_t lds) {
   constexpr int kDevices = 64;
   static std::atomic<size_t> set_to[kDevices];
@@ -352,7 +432,7 @@ hipError_t set_merge_lds(size_t lds) {
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
   if (dev >= 0 && dev < kDevices && set_to[dev].load(std::memory_order_relaxed) >= lds) return hipSuccess;
-  err = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_merge_kernel),
+  err = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_merge_kernel<LIST_OUT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (err == hipSuccess && dev >= 0 && dev < kDevices) {
     size_t cur = set_to[dev].load(std::memory_order_relaxed);
@@ -360,6 +440,37 @@ hipError_t set_merge_lds(size_t lds) {
     }
   }
   return err;
+}
+
+// The merge of rows [P.row0, P.row0 + rows) from P's chunk lists: one merge per row, or, with
+// more than kGroupLists lists per row and a first-level region, a first-level merge per group of
+// kGroupLists lists and the final merge over the groups' lists.
+hipError_t launch_merges(TopkParams P, int rows, void* level1, hipStream_t stream) {
+  const size_t lds = merge_lds_bytes(P.S_max);
+  hipError_t err = set_merge_lds<false>(lds);
+  if (err != hipSuccess) return err;
+  const Level1 l1 = level1_plan(rows, P.chunks, P.R);
+  if (l1.groups > 0 && level1 != nullptr) {
+    // the first level keeps no bitmap: only the fixed part of the LDS layout
+    const size_t lds1 = sizeof(uint32_t) * static_cast<size_t>(kMsBits);
+    if ((err = set_merge_lds<true>(lds1)) != hipSuccess) return err;
+    char* r = static_cast<char*>(level1);
+    P.groups = l1.groups;
+    P.g_count = reinterpret_cast<uint32_t*>(r);
+    P.g_range = reinterpret_cast<uint32_t*>(r + l1.count_bytes);
+    P.g_cand = reinterpret_cast<uint2*>(r + l1.count_bytes + l1.range_bytes);
+    hipLaunchKernelGGL(topk_merge_kernel<true>, dim3(static_cast<unsigned>(rows * l1.groups)),
+                       dim3(kMergeThreads), lds1, stream, P);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    P.chunks = l1.groups;
+    P.chunk_keys = P.R;
+    P.count = P.g_count;
+    P.range = P.g_range;
+    P.cand = P.g_cand;
+  }
+  hipLaunchKernelGGL(topk_merge_kernel<false>, dim3(static_cast<unsigned>(rows)), dim3(kMergeThreads), lds,
+                     stream, P);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -375,9 +486,6 @@ hipError_t launch_topk(const float* scores, const int32_t* seqlens, int B, int L
                        int32_t* n_sel, void* workspace, hipStream_t stream) {
   const Plan pl = make_plan(B, Lq, S_max, topk, init_tokens, local_tokens);
   if (pl.group * pl.chunks > 0x7fffffffL || pl.rows > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  const size_t lds = merge_lds_bytes(S_max);
-  hipError_t err = set_merge_lds(lds);
-  if (err != hipSuccess) return err;
   TopkParams P{};
   P.scores = scores;
   P.seqlens = seqlens;
@@ -387,12 +495,14 @@ hipError_t launch_topk(const float* scores, const int32_t* seqlens, int B, int L
   P.init = init_tokens;
   P.local = local_tokens;
   P.R = pl.R;
+  P.cap = sel::list_cap(pl.R);
   P.chunks = pl.chunks;
   P.chunk_keys = kChunk;
   char* ws = align_workspace(workspace);
   P.count = reinterpret_cast<uint32_t*>(ws);
   P.range = reinterpret_cast<uint32_t*>(ws + pl.count_bytes);
   P.cand = reinterpret_cast<uint2*>(ws + pl.count_bytes + pl.range_bytes);
+  void* level1 = pl.l1.groups ? ws + pl.count_bytes + pl.range_bytes + pl.cand_bytes : nullptr;
   P.indices = indices;
   P.n_sel = n_sel;
   for (long r0 = 0; r0 < pl.rows; r0 += pl.group) {
@@ -400,23 +510,24 @@ hipError_t launch_topk(const float* scores, const int32_t* seqlens, int B, int L
     P.row0 = static_cast<int>(r0);
     hipLaunchKernelGGL(topk_chunk_kernel, dim3(static_cast<unsigned>(g * pl.chunks)), dim3(kChunkThreads), 0,
                        stream, P);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(topk_merge_kernel, dim3(static_cast<unsigned>(g)), dim3(kMergeThreads), lds, stream, P);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if ((err = launch_merges(P, static_cast<int>(g), level1, stream)) != hipSuccess) return err;
   }
   return hipSuccess;
 }
 
 int topk_merge_max_chunks() { return kMaxChunks; }
 
+size_t topk_merge_level1_bytes(long rows, int chunks, int topk, int init_tokens, int local_tokens) {
+  return level1_plan(rows, chunks, topk - init_tokens - local_tokens).total();
+}
+
 hipError_t launch_topk_merge(const int32_t* seqlens, int Lq, int S_max, int topk, int init_tokens,
                              int local_tokens, int row0, int rows, int chunks, int chunk_keys,
-                             uint32_t* count, uint32_t* range, uint2* cand, int32_t* indices,
-                             int32_t* n_sel, hipStream_t stream) {
+                             uint32_t* count, uint32_t* range, uint2* cand, void* level1,
+                             int32_t* indices, int32_t* n_sel, hipStream_t stream) {
   if (chunks > kMaxChunks || rows <= 0) return hipErrorInvalidConfiguration;
-  const size_t lds = merge_lds_bytes(S_max);
-  hipError_t err = set_merge_lds(lds);
-  if (err != hipSuccess) return err;
   TopkParams P{};
   P.seqlens = seqlens;
   P.Lq = Lq;
@@ -425,6 +536,7 @@ hipError_t launch_topk_merge(const int32_t* seqlens, int Lq, int S_max, int topk
   P.init = init_tokens;
   P.local = local_tokens;
   P.R = topk - init_tokens - local_tokens;
+  P.cap = sel::list_cap(P.R);
   P.row0 = row0;
   P.chunks = chunks;
   P.chunk_keys = chunk_keys;
@@ -433,8 +545,7 @@ hipError_t launch_topk_merge(const int32_t* seqlens, int Lq, int S_max, int topk
   P.cand = cand;
   P.indices = indices;
   P.n_sel = n_sel;
-  hipLaunchKernelGGL(topk_merge_kernel, dim3(static_cast<unsigned>(rows)), dim3(kMergeThreads), lds, stream, P);
-  return hipGetLastError();
+  return launch_merges(P, rows, level1, stream);
 }
 
 }  // namespace lsa

@@ -104,22 +104,65 @@ def _want(t, name, dtype, ndim):
         raise ValueError(f"{name}: expected {ndim} dims, got shape {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name}: must be a device tensor")
+
+
+def _want_shape(t, name, dtype, shape):
+    """A tensor that must match exactly: dtype, shape, contiguous, on a device."""
+    _want(t, name, dtype, len(shape))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _same_device(name, *ts):
+    """Every tensor given is a device tensor, all on one device (checked after the shapes)."""
+    devs = {t.device for t in ts if t is not None}
+    if any(d.type != "cuda" for d in devs):
+        raise ValueError(f"{name}: every tensor must be a device tensor, got {sorted(map(str, devs))}")
+    if len(devs) > 1:
+        raise ValueError(f"{name}: tensors on different devices {sorted(map(str, devs))}")
+
+
+def _index_inputs(fn, q_idx, w, k_idx, seqlens):
+    """Shapes of the indexer inputs, checked against each other: (B, Lq, Hi, Di, S_max)."""
+    _want(q_idx, "q_idx", torch.bfloat16, 4)
+    B, Lq, Hi, Di = q_idx.shape
+    _want_shape(w, "w", torch.float32, (B, Lq, Hi))
+    _want(k_idx, "k_idx", torch.bfloat16, 3)
+    if k_idx.shape[0] != B or k_idx.shape[2] != Di:
+        raise ValueError(f"{fn}: k_idx shape {tuple(k_idx.shape)} does not match q_idx "
+                         f"{tuple(q_idx.shape)} (expected [{B}, S_max, {Di}])")
+    _want_shape(seqlens, "seqlens", torch.int32, (B,))
+    return B, Lq, Hi, Di, k_idx.shape[1]
+
+
+def _selection_outputs(indices, n_sel, B, Lq, topk, dev):
+    """Caller-supplied (or new) indices [B, Lq, topk] and n_sel [B, Lq]."""
+    if indices is None:
+        indices = torch.empty(B, Lq, topk, dtype=torch.int32, device=dev)
+    _want_shape(indices, "indices", torch.int32, (B, Lq, topk))
+    if n_sel is None:
+        n_sel = torch.empty(B, Lq, dtype=torch.int32, device=dev)
+    _want_shape(n_sel, "n_sel", torch.int32, (B, Lq))
+    return indices, n_sel
+
+
+def _workspace(workspace, need, dev):
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None and (workspace.device.type != "cuda" or not workspace.is_contiguous()):
+        raise ValueError("workspace: must be a contiguous device tensor")
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return workspace, wbytes
 
 
 def lsa_index_scores(q_idx, w, k_idx, seqlens, scores=None):
     """q_idx bf16 [B,Lq,Hi,Di], w f32 [B,Lq,Hi], k_idx bf16 [B,S_max,Di], seqlens i32 [B]
     -> scores f32 [B,Lq,S_max] (entries after each query's position are left untouched)."""
-    _want(q_idx, "q_idx", torch.bfloat16, 4)
-    _want(w, "w", torch.float32, 3)
-    _want(k_idx, "k_idx", torch.bfloat16, 3)
-    _want(seqlens, "seqlens", torch.int32, 1)
-    B, Lq, Hi, Di = q_idx.shape
-    S_max = k_idx.shape[1]
+    B, Lq, Hi, Di, S_max = _index_inputs("lsa_index_scores", q_idx, w, k_idx, seqlens)
     if scores is None:
         scores = torch.empty(B, Lq, S_max, dtype=torch.float32, device=q_idx.device)
-    _want(scores, "scores", torch.float32, 3)
+    _want_shape(scores, "scores", torch.float32, (B, Lq, S_max))
+    _same_device("lsa_index_scores", q_idx, w, k_idx, seqlens, scores)
     _check(lib().lsa_index_scores(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(seqlens), B, Lq, Hi, Di,
                                   S_max, _ptr(scores), _stream(q_idx)))
     return scores
@@ -133,17 +176,13 @@ def lsa_topk_select(scores, seqlens, topk, init_tokens, local_tokens, indices=No
                     workspace=None):
     """scores f32 [B,Lq,S_max] -> (indices i32 [B,Lq,topk] ascending, -1 padded; n_sel i32 [B,Lq])."""
     _want(scores, "scores", torch.float32, 3)
-    _want(seqlens, "seqlens", torch.int32, 1)
     B, Lq, S_max = scores.shape
+    _want_shape(seqlens, "seqlens", torch.int32, (B,))
     dev = scores.device
-    if indices is None:
-        indices = torch.empty(B, Lq, topk, dtype=torch.int32, device=dev)
-    if n_sel is None:
-        n_sel = torch.empty(B, Lq, dtype=torch.int32, device=dev)
+    indices, n_sel = _selection_outputs(indices, n_sel, B, Lq, topk, dev)
+    _same_device("lsa_topk_select", scores, seqlens, indices, n_sel)
     need = lsa_topk_workspace_bytes(B, Lq, S_max, topk, init_tokens, local_tokens)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, wbytes = _workspace(workspace, need, dev)
     _check(lib().lsa_topk_select(_ptr(scores), _ptr(seqlens), B, Lq, S_max, topk, init_tokens,
                                  local_tokens, _ptr(indices), _ptr(n_sel), _ptr(workspace), wbytes,
                                  _stream(scores)))
@@ -158,21 +197,12 @@ def lsa_index_topk(q_idx, w, k_idx, seqlens, topk, init_tokens, local_tokens, in
                    n_sel=None, workspace=None):
     """Indexer + top-k in one pass (no score array): the inputs of lsa_index_scores ->
     (indices i32 [B,Lq,topk] ascending, -1 padded; n_sel i32 [B,Lq])."""
-    _want(q_idx, "q_idx", torch.bfloat16, 4)
-    _want(w, "w", torch.float32, 3)
-    _want(k_idx, "k_idx", torch.bfloat16, 3)
-    _want(seqlens, "seqlens", torch.int32, 1)
-    B, Lq, Hi, Di = q_idx.shape
-    S_max = k_idx.shape[1]
+    B, Lq, Hi, Di, S_max = _index_inputs("lsa_index_topk", q_idx, w, k_idx, seqlens)
     dev = q_idx.device
-    if indices is None:
-        indices = torch.empty(B, Lq, topk, dtype=torch.int32, device=dev)
-    if n_sel is None:
-        n_sel = torch.empty(B, Lq, dtype=torch.int32, device=dev)
+    indices, n_sel = _selection_outputs(indices, n_sel, B, Lq, topk, dev)
+    _same_device("lsa_index_topk", q_idx, w, k_idx, seqlens, indices, n_sel)
     need = lsa_index_topk_workspace_bytes(B, Lq, S_max, topk, init_tokens, local_tokens)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, wbytes = _workspace(workspace, need, dev)
     _check(lib().lsa_index_topk(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(seqlens), B, Lq, Hi, Di,
                                 S_max, topk, init_tokens, local_tokens, _ptr(indices), _ptr(n_sel),
                                 _ptr(workspace), wbytes, _stream(q_idx)))
@@ -184,31 +214,39 @@ def lsa_mla_workspace_bytes(B, Lq, H, Dv, S_max, topk, dense) -> int:
 
 
 def _mla(decode, q, kv, indices, n_sel, seqlens, Dv, softmax_scale, out, lse, workspace):
-    _want(kv, "kv", torch.bfloat16, 3)
-    _want(seqlens, "seqlens", torch.int32, 1)
     if decode:
         _want(q, "q", torch.bfloat16, 3)
         B, H, Dqk = q.shape
         Lq = 1
-        out_shape = (B, H, Dv)
+        rows = (B,)
     else:
         _want(q, "q", torch.bfloat16, 4)
         B, Lq, H, Dqk = q.shape
-        out_shape = (B, Lq, H, Dv)
+        rows = (B, Lq)
+    _want(kv, "kv", torch.bfloat16, 3)
+    if kv.shape[0] != B or kv.shape[2] != Dqk:
+        raise ValueError(f"kv: shape {tuple(kv.shape)} does not match q {tuple(q.shape)} "
+                         f"(expected [{B}, S_max, {Dqk}])")
+    _want_shape(seqlens, "seqlens", torch.int32, (B,))
     S_max = kv.shape[1]
     dense = indices is None
     topk = 0
     if not dense:
-        _want(indices, "indices", torch.int32, 2 if decode else 3)
-        _want(n_sel, "n_sel", torch.int32, 1 if decode else 2)
+        _want(indices, "indices", torch.int32, len(rows) + 1)
         topk = indices.shape[-1]
+        _want_shape(indices, "indices", torch.int32, rows + (topk,))
+        if n_sel is None:
+            raise ValueError("n_sel: required with indices")
+        _want_shape(n_sel, "n_sel", torch.int32, rows)
     dev = q.device
     if out is None:
-        out = torch.empty(out_shape, dtype=torch.bfloat16, device=dev)
+        out = torch.empty(rows + (H, Dv), dtype=torch.bfloat16, device=dev)
+    _want_shape(out, "out", torch.bfloat16, rows + (H, Dv))
+    if lse is not None:
+        _want_shape(lse, "lse", torch.float32, rows + (H,))
+    _same_device("attention", q, kv, seqlens, indices, n_sel, out, lse)
     need = lsa_mla_workspace_bytes(B, Lq, H, Dv, S_max, topk, dense)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, wbytes = _workspace(workspace, need, dev)
     if decode:
         st = lib().lsa_sparse_mla_decode(_ptr(q), _ptr(kv), _ptr(indices), _ptr(n_sel),
                                          _ptr(seqlens), B, H, Dqk, Dv, S_max, topk,
@@ -248,19 +286,25 @@ def lsa_mtp_draft_attention(q, kv, indices, n_sel, index_seqlens, seqlens, Dv, s
     seqlens[b] - 1 and also attends to the positions appended since (at most max_appended)
     -> out bf16 [B,H,Dv] (lse f32 [B,H] written if given)."""
     _want(q, "q", torch.bfloat16, 3)
-    _want(kv, "kv", torch.bfloat16, 3)
-    _want(indices, "indices", torch.int32, 2)
-    _want(n_sel, "n_sel", torch.int32, 1)
-    _want(index_seqlens, "index_seqlens", torch.int32, 1)
-    _want(seqlens, "seqlens", torch.int32, 1)
     B, H, Dqk = q.shape
+    _want(kv, "kv", torch.bfloat16, 3)
+    if kv.shape[0] != B or kv.shape[2] != Dqk:
+        raise ValueError(f"kv: shape {tuple(kv.shape)} does not match q {tuple(q.shape)} "
+                         f"(expected [{B}, S_max, {Dqk}])")
+    _want(indices, "indices", torch.int32, 2)
     S_max, topk = kv.shape[1], indices.shape[1]
+    _want_shape(indices, "indices", torch.int32, (B, topk))
+    _want_shape(n_sel, "n_sel", torch.int32, (B,))
+    _want_shape(index_seqlens, "index_seqlens", torch.int32, (B,))
+    _want_shape(seqlens, "seqlens", torch.int32, (B,))
     if out is None:
         out = torch.empty(B, H, Dv, dtype=torch.bfloat16, device=q.device)
+    _want_shape(out, "out", torch.bfloat16, (B, H, Dv))
+    if lse is not None:
+        _want_shape(lse, "lse", torch.float32, (B, H))
+    _same_device("lsa_mtp_draft_attention", q, kv, indices, n_sel, index_seqlens, seqlens, out, lse)
     need = lsa_mtp_draft_workspace_bytes(B, H, Dv, S_max, topk, max_appended)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, wbytes = _workspace(workspace, need, q.device)
     _check(lib().lsa_mtp_draft_attention(_ptr(q), _ptr(kv), _ptr(indices), _ptr(n_sel),
                                          _ptr(index_seqlens), _ptr(seqlens), B, H, Dqk, Dv, S_max,
                                          topk, int(max_appended), float(softmax_scale), _ptr(out),
@@ -279,6 +323,7 @@ def lsa_block_keys(k_idx, seqlens, Bk, block_keys=None, first_block=0):
     _want(block_keys, "block_keys", torch.bfloat16, 3)
     if block_keys.shape != (B, S_max // Bk, Di) or seqlens.shape[0] != B:
         raise ValueError("lsa_block_keys: inconsistent shapes")
+    _same_device("lsa_block_keys", k_idx, seqlens, block_keys)
     _check(lib().lsa_block_keys(_ptr(k_idx), _ptr(seqlens), B, S_max, Di, int(Bk), int(first_block),
                                 _ptr(block_keys), _stream(k_idx)))
     return block_keys
@@ -306,12 +351,13 @@ def lsa_hier_index_topk(q_idx, w, k_idx, block_keys, seqlens, topk, init_tokens,
     dev = q_idx.device
     if indices is None:
         indices = torch.empty(B, topk, dtype=torch.int32, device=dev)
+    _want_shape(indices, "indices", torch.int32, (B, topk))
     if n_sel is None:
         n_sel = torch.empty(B, dtype=torch.int32, device=dev)
+    _want_shape(n_sel, "n_sel", torch.int32, (B,))
+    _same_device("lsa_hier_index_topk", q_idx, w, k_idx, block_keys, seqlens, indices, n_sel)
     need = lsa_hier_workspace_bytes(B, S_max, Bk, topk, init_tokens, local_tokens, M)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, wbytes = _workspace(workspace, need, dev)
     _check(lib().lsa_hier_index_topk(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(block_keys),
                                      _ptr(seqlens), B, Hi, Di, S_max, topk, init_tokens, local_tokens,
                                      int(Bk), int(M), _ptr(indices), _ptr(n_sel), _ptr(workspace),
@@ -349,12 +395,14 @@ def lsa_index_frontend(cq, hid, wq_b, wk, k_norm_gain, w_proj, seqlens, k_cache,
     dev = cq.device
     if q_idx is None:
         q_idx = torch.empty(B, Lq, Hi, Di, dtype=torch.bfloat16, device=dev)
+    _want_shape(q_idx, "q_idx", torch.bfloat16, (B, Lq, Hi, Di))
     if w is None:
         w = torch.empty(B, Lq, Hi, dtype=torch.float32, device=dev)
+    _want_shape(w, "w", torch.float32, (B, Lq, Hi))
+    _same_device("lsa_index_frontend", cq, hid, wq_b, wk, k_norm_gain, w_proj, seqlens, k_cache,
+                 q_idx, w)
     need = lsa_index_frontend_workspace_bytes(B, Lq, q_lora, hidden, Hi, Di)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, wbytes = _workspace(workspace, need, dev)
     _check(lib().lsa_index_frontend(_ptr(cq), _ptr(hid), _ptr(wq_b), _ptr(wk), _ptr(k_norm_gain),
                                     _ptr(w_proj), _ptr(seqlens), B, Lq, q_lora, hidden, Hi, Di,
                                     rope_dim, rope_theta, norm_eps, S_max, _ptr(q_idx), _ptr(w),

@@ -31,6 +31,9 @@ PATHS = {
     "fused": {"name": "index_topk", "kernels": ("index_scores_kernel", "topk_merge_kernel"),
               "sources": ("csrc/lsa_indexer.hip", "csrc/lsa_select.h", "csrc/lsa_topk.hip",
                           "csrc/lsa_internal.h")},
+    # one decode attention call (lsa_sparse_mla_decode): the split kernel and the combine
+    "attention": {"name": "attention", "kernels": ("sparse_mla_kernel", "mla_combine_kernel"),
+                  "sources": ("csrc/lsa_mla.hip", "csrc/lsa_internal.h")},
 }
 COPY_MATCH = "copyBuffer"
 
@@ -84,15 +87,18 @@ def summarize(fetch_csv, write_csv, calib_mib, workload, path, alg_bytes, cmd_fe
             raise SystemExit(f"{csv_path}: no {COPY_MATCH} dispatch")
         factor = max(c) / calib  # the largest copy is the calibration copy
         raw, ndisp = 0.0, []
+        per_kernel = {}
         for kname in kernels:  # one dispatch of each per call: sum of the per-kernel means
             k = [v * 1024.0 for n, v in disp.values() if kname in n]
             if not k:
                 raise SystemExit(f"{csv_path}: no {kname} dispatches")
             raw += statistics.mean(k)
             ndisp.append(len(k))
+            per_kernel[kname] = statistics.mean(k) / factor
         res[counter] = {"kernel_raw_bytes_mean": raw, "dispatches": min(ndisp),
                         "copy_raw_bytes": max(c), "factor": factor,
-                        "kernel_bytes_per_launch": raw / factor}
+                        "kernel_bytes_per_launch": raw / factor,
+                        "bytes_per_kernel": {k: round(v) for k, v in per_kernel.items()}}
     traffic = res["FETCH_SIZE"]["kernel_bytes_per_launch"] + res["WRITE_SIZE"]["kernel_bytes_per_launch"]
     rec = {"kernels": list(kernels), "path": path, "workload": workload,
            "traffic_bytes_per_launch": round(traffic),
@@ -132,10 +138,11 @@ def main():
     a = ap.parse_args()
     import sys
     sys.path.insert(0, ROOT)
-    from bench import fused_call_bytes, indexer_bytes
+    from bench import attention_call_bytes, fused_call_bytes, indexer_bytes
     from long_context_sparse_lightning_amd.workloads import WORKLOADS
     wl = WORKLOADS[a.workload]
-    alg = fused_call_bytes(wl) if a.path == "fused" else indexer_bytes(wl)
+    alg = {"fused": fused_call_bytes, "split": indexer_bytes,
+           "attention": attention_call_bytes}[a.path](wl)
     rec = summarize(a.fetch_csv, a.write_csv, a.calib_mib, a.workload, a.path, alg,
                     a.command_fetch, a.command_write)
     print(json.dumps({k: rec[k] for k in ("traffic_bytes_per_launch", "alg_bytes_per_launch",

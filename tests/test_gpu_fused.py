@@ -82,3 +82,30 @@ def test_fused_is_deterministic_and_ignores_workspace_contents():
                            workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("B,S,seqlens", [
+    # chunks of 3200 keys (63 lists per row): every chunk cuts its tied list to its exact top R,
+    # then two merge levels
+    (8, 200000, (200000, 150001, 99999, 2049, 2048, 60000, 131072, 7000)),
+    # chunks of 896 keys (112 lists per row): every middle key is a candidate, two merge levels
+    (2, 100000, (100000, 33333)),
+])
+def test_fused_all_equal_scores_many_lists(B, S, seqlens):
+    """Zero index queries make every score 0: the selection is then decided by positions alone
+    (the lowest middle positions), through the chunks' exact cut and the two-level merge."""
+    print(f"case all-equal B={B} S={S}", flush=True)
+    wl = Workload("f_tied", B=B, S_max=S, Lq=1, seqlens=seqlens, Hi=8, Di=128, topk=2048, init=16,
+                  local=1024, H=4, Dqk=80, Dv=64, seed=96)
+    X = device_inputs(wl)
+    q0 = torch.zeros_like(X["qidx"])
+    idx_f, ns_f = lsa.lsa_index_topk(q0, X["w"], X["kidx"], X["seqlens"], wl.topk, wl.init, wl.local)
+    sc = lsa.lsa_index_scores(q0, X["w"], X["kidx"], X["seqlens"])
+    idx_u, ns_u = lsa.lsa_topk_select(sc, X["seqlens"], wl.topk, wl.init, wl.local)
+    torch.cuda.synchronize()
+    zeros = np.zeros((B, 1, S), np.float32)
+    ref_idx, ref_n = oracle.topk_select(zeros, np.array(seqlens, np.int32), wl.topk, wl.init,
+                                        wl.local)
+    assert np.array_equal(ns_f.cpu().numpy(), ref_n) and np.array_equal(ns_u.cpu().numpy(), ref_n)
+    assert np.array_equal(idx_f.cpu().numpy(), ref_idx)
+    assert np.array_equal(idx_u.cpu().numpy(), ref_idx)

@@ -2,8 +2,8 @@
 index queries and keys (every score and block mean is exact in fp32 and bf16, so selections
 compare bit for bit): block keys equal the bf16 block means; selections equal the oracle's for
 dense rows, rows whose blocks are all kept, kept blocks holding exactly the middle budget, block
-sizes 8 to 1024, a 1M-token context (chunk lists of 8192); with every block kept the result is
-lsa_index_topk's; too few kept tokens for the budget is refused."""
+sizes 8 to 1024, a 1M-token context (candidate lists of 16384 positions); with every block kept
+the result is lsa_index_topk's; too few kept tokens for the budget is refused."""
 import dataclasses
 
 import numpy as np
