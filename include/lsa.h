@@ -38,7 +38,8 @@
  *   regions inside); their contents on entry do not matter, and two calls in flight must not
  *   share one.
  * - Results are deterministic: identical inputs give bit-identical outputs.
- * - No global mutable state except the thread-local error text.
+ * - No global mutable state except the thread-local error text and the static workspace of
+ *   lsa_index_topk_noalloc (one per device).
  */
 #ifndef LSA_H_
 #define LSA_H_
@@ -132,6 +133,26 @@ lsa_status lsa_index_topk(const void* q_idx, const float* w, const void* k_idx,
                           const int32_t* seqlens, int B, int Lq, int Hi, int Di, int S_max, int topk,
                           int init_tokens, int local_tokens, int32_t* indices, int32_t* n_sel,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of the static device workspace of lsa_index_topk_noalloc (48 MiB per device). */
+#define LSA_INDEX_TOPK_SCRATCH_BYTES (48u << 20)
+
+/*
+ * lsa_index_topk without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation and results as lsa_index_topk (bit for bit), with its workspace in a static
+ * array of LSA_INDEX_TOPK_SCRATCH_BYTES that the library holds on each device it runs on until
+ * the process ends (its device address is looked up on the first call for a device).  The call
+ * allocates nothing.  Every call on a device shares that device's array: calls that may overlap
+ * on one device (different streams, or several host threads) race on it and must be ordered by
+ * the caller.  Arguments and errors as lsa_index_topk, without workspace/workspace_bytes; sizes
+ * whose lsa_index_topk_workspace_bytes exceeds LSA_INDEX_TOPK_SCRATCH_BYTES return
+ * LSA_ERR_WORKSPACE before anything is enqueued.
+ */
+lsa_status lsa_index_topk_noalloc(const void* q_idx, const float* w, const void* k_idx,
+                                  const int32_t* seqlens, int B, int Lq, int Hi, int Di, int S_max,
+                                  int topk, int init_tokens, int local_tokens, int32_t* indices,
+                                  int32_t* n_sel, void* stream);
 
 /* Largest selection the attention takes: 64 partial splits of at most 2048 rows each. */
 #define LSA_MLA_MAX_TOPK 131072

@@ -4,6 +4,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "lsa.h"
 #include "lsa_internal.h"
 
@@ -30,6 +33,51 @@ lsa_status launched(hipError_t err, const char* what) {
   return ok();
 }
 
+}  // namespace
+
+// ------------------------------------------------------------------ no-allocation variant
+// The workspace of lsa_index_topk_noalloc: one static array per device the library runs on,
+// resident until the process ends.  Host code never uses the array's name as an address (in
+// host code it names a host-side stand-in): its device address is looked up once per device
+// with hipGetSymbolAddress, with that device current, and kept in scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[LSA_INDEX_TOPK_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_ptr[kMaxDevices];
+std::mutex scratch_mu;
+
+// Device address of `scratch` on the device that runs `stream` (the current device for the
+// NULL stream), looked up on the first call for that device.
+lsa_status scratch_for(hipStream_t stream, void** out, const char* fn) {
+  int dev = 0;
+  hipError_t err = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (err != hipSuccess) return fail(LSA_ERR_LAUNCH, "%s: no device for the stream: %s", fn, hipGetErrorString(err));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(LSA_ERR_UNSUPPORTED, "%s: device %d beyond the %d the static workspace covers", fn, dev, kMaxDevices);
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    p = scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      int cur = 0;
+      if ((err = hipGetDevice(&cur)) != hipSuccess)
+        return fail(LSA_ERR_LAUNCH, "%s: hipGetDevice: %s", fn, hipGetErrorString(err));
+      if (cur != dev && (err = hipSetDevice(dev)) != hipSuccess)
+        return fail(LSA_ERR_LAUNCH, "%s: hipSetDevice(%d): %s", fn, dev, hipGetErrorString(err));
+      err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+      if (err != hipSuccess || !p)
+        return fail(LSA_ERR_LAUNCH, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                    hipGetErrorString(err));
+      if (back != hipSuccess)
+        return fail(LSA_ERR_LAUNCH, "%s: hipSetDevice(%d): %s", fn, cur, hipGetErrorString(back));
+      scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return LSA_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -140,6 +188,32 @@ lsa_status lsa_index_topk(const void* q_idx, const float* w, const void* k_idx,
                                          S_max, topk, init_tokens, local_tokens, indices, n_sel,
                                          workspace, static_cast<hipStream_t>(stream)),
                   "lsa_index_topk");
+}
+
+// lsa_index_topk without a workspace argument: its workspace is the static `scratch` array.
+lsa_status lsa_index_topk_noalloc(const void* q_idx, const float* w, const void* k_idx,
+                                  const int32_t* seqlens, int B, int Lq, int Hi, int Di, int S_max,
+                                  int topk, int init_tokens, int local_tokens, int32_t* indices,
+                                  int32_t* n_sel, void* stream) {
+  const char* fn = "lsa_index_topk_noalloc";
+  lsa_status st = check_index(fn, B, Lq, Hi, Di, S_max);
+  if (st != LSA_OK) return st;
+  st = check_topk(B, Lq, S_max, topk, init_tokens, local_tokens);
+  if (st != LSA_OK) return st;
+  if (B == 0 || Lq == 0) return ok();
+  if (!q_idx || !w || !k_idx || !seqlens || !indices || !n_sel)
+    return fail(LSA_ERR_NULL_ARG, "%s: NULL q_idx/w/k_idx/seqlens/indices/n_sel", fn);
+  const size_t need = lsa::index_topk_workspace_bytes(B, Lq, S_max, topk, init_tokens, local_tokens);
+  if (need > LSA_INDEX_TOPK_SCRATCH_BYTES)
+    return fail(LSA_ERR_WORKSPACE, "%s: these sizes need %zu bytes of workspace, more than the %zu of the static one",
+                fn, need, static_cast<size_t>(LSA_INDEX_TOPK_SCRATCH_BYTES));
+  void* ws = nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = scratch_for(s, &ws, fn)) != LSA_OK) return st;
+  return launched(lsa::launch_index_topk(static_cast<const uint16_t*>(q_idx), w,
+                                         static_cast<const uint16_t*>(k_idx), seqlens, B, Lq, Hi, Di,
+                                         S_max, topk, init_tokens, local_tokens, indices, n_sel, ws, s),
+                  fn);
 }
 
 static bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }

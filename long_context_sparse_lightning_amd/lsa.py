@@ -24,7 +24,9 @@ EXPORTED = ["lsa_status_str", "lsa_last_error", "lsa_index_scores", "lsa_topk_wo
             "lsa_mla_workspace_bytes", "lsa_sparse_mla_decode", "lsa_sparse_mla_prefill",
             "lsa_index_frontend_workspace_bytes", "lsa_index_frontend",
             "lsa_mtp_draft_workspace_bytes", "lsa_mtp_draft_attention", "lsa_block_keys",
-            "lsa_hier_workspace_bytes", "lsa_hier_index_topk"]
+            "lsa_hier_workspace_bytes", "lsa_hier_index_topk", "lsa_index_topk_noalloc"]
+
+INDEX_TOPK_SCRATCH_BYTES = 48 << 20  # LSA_INDEX_TOPK_SCRATCH_BYTES
 
 
 class LsaError(RuntimeError):
@@ -59,6 +61,8 @@ def lib():
         L.lsa_index_topk_workspace_bytes.restype = Z
         L.lsa_index_topk.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, P, P, P, Z, P]
         L.lsa_index_topk.restype = I
+        L.lsa_index_topk_noalloc.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, P, P, P]
+        L.lsa_index_topk_noalloc.restype = I
         L.lsa_mla_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
         L.lsa_mla_workspace_bytes.restype = Z
         L.lsa_sparse_mla_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, P, P, P, Z, P]
@@ -206,6 +210,21 @@ def lsa_index_topk(q_idx, w, k_idx, seqlens, topk, init_tokens, local_tokens, in
     _check(lib().lsa_index_topk(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(seqlens), B, Lq, Hi, Di,
                                 S_max, topk, init_tokens, local_tokens, _ptr(indices), _ptr(n_sel),
                                 _ptr(workspace), wbytes, _stream(q_idx)))
+    return indices, n_sel
+
+
+def lsa_index_topk_noalloc(q_idx, w, k_idx, seqlens, topk, init_tokens, local_tokens, indices,
+                           n_sel):
+    """lsa_index_topk with the library's static per-device workspace instead of a caller one
+    (no allocation at all: indices and n_sel must be given).  Calls overlapping on one device
+    race on that workspace."""
+    B, Lq, Hi, Di, S_max = _index_inputs("lsa_index_topk_noalloc", q_idx, w, k_idx, seqlens)
+    _want_shape(indices, "indices", torch.int32, (B, Lq, topk))
+    _want_shape(n_sel, "n_sel", torch.int32, (B, Lq))
+    _same_device("lsa_index_topk_noalloc", q_idx, w, k_idx, seqlens, indices, n_sel)
+    _check(lib().lsa_index_topk_noalloc(_ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(seqlens), B, Lq, Hi,
+                                        Di, S_max, topk, init_tokens, local_tokens, _ptr(indices),
+                                        _ptr(n_sel), _stream(q_idx)))
     return indices, n_sel
 
 

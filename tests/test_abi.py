@@ -92,6 +92,25 @@ def test_index_topk_argument_errors_and_workspace():
     assert L.lsa_index_topk_workspace_bytes(1, 1, 4096, 8, 5, 4) == 0  # invalid -> 0
 
 
+def test_index_topk_noalloc_argument_errors():
+    """The static-workspace variant checks like lsa_index_topk and refuses sizes whose workspace
+    exceeds LSA_INDEX_TOPK_SCRATCH_BYTES, all before touching a device."""
+    L = lsa.lib()
+    p = ctypes.c_void_p(16)
+    f = L.lsa_index_topk_noalloc
+    assert f(p, p, p, p, 1, 1, 33, 128, 4096, 256, 4, 64, p, p, None) == 3  # Hi > 32
+    assert f(p, p, p, p, 1, 1, 32, 128, 4096, 8, 5, 4, p, p, None) == 2  # init + local > topk
+    assert f(p, None, p, p, 1, 1, 32, 128, 4096, 256, 4, 64, p, p, None) == 1
+    assert f(None, None, None, None, 0, 1, 32, 128, 4096, 256, 4, 64, None, None, None) == 0
+    big = L.lsa_index_topk_workspace_bytes(64, 1, 131072, 2048, 16, 1024)
+    assert big > lsa.INDEX_TOPK_SCRATCH_BYTES
+    assert f(p, p, p, p, 64, 1, 32, 128, 131072, 2048, 16, 1024, p, p, None) == 4
+    assert "static" in _err()
+    # the bench shapes fit
+    for B, S in ((32, 131072), (8, 32768), (4, 983040)):
+        assert L.lsa_index_topk_workspace_bytes(B, 1, S, 2048, 16, 1024) <= lsa.INDEX_TOPK_SCRATCH_BYTES
+
+
 def test_mla_argument_errors_and_workspace():
     L = lsa.lib()
     p = ctypes.c_void_p(16)
