@@ -427,9 +427,14 @@ hipError_t launch_qb(const uint16_t* q_idx, const float* w, const uint16_t* k_id
 // Keys per workgroup: about 512 workgroups (two per CU, all resident at once) with whole
 // workgroup steps per chunk; long chunks amortise the query/weight loads and the ramp of each
 // workgroup.  The fused variant also keeps at most 128 chunks per row (the merge's limit).
+// Keys per workgroup: enough workgroups to fill the chip twice, at most 8192 keys (the LDS score
+// stage).  The fused call also keeps a row to at most 16 candidate lists where the cap allows, so
+// one merge takes them all (decode_32k: 16 chunks of 2048 keys, 14 us for its merge, against 64
+// chunks of 512 keys and two merge levels, 23 us; decode_1m: 8192-key chunks scan 2% faster than
+// 7680-key ones).
 int keys_per_workgroup(long rows, int S_max, bool fused) {
   long per = (rows * S_max + 511) / 512;
-  if (fused) per = std::max<long>(per, (S_max + 127) / 128);
+  if (fused) per = std::max<long>(per, std::max<long>((S_max + 127) / 128, (S_max + 15) / 16));
   per = ((per + kWgStride - 1) / kWgStride) * kWgStride;
   if (per < kWgStride) per = kWgStride;
   if (per > kMaxKeysPerWg) per = kMaxKeysPerWg;

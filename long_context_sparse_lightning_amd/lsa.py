@@ -151,6 +151,7 @@ def _selection_outputs(indices, n_sel, B, Lq, topk, dev):
 
 
 def _workspace(workspace, need, dev):
+    """The caller's workspace (contents on entry do not matter), or a new one."""
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace is not None and (workspace.device.type != "cuda" or not workspace.is_contiguous()):

@@ -271,3 +271,34 @@ def test_prefill_rows_equal_decode_calls():
         assert int(dn[0, 0]) == int(nsel[0, i])
         assert torch.equal(di[0, 0], idx[0, i]), f"row {i}"
         assert_attention_close(bf16_to_f64(out[0]), bf16_to_f64(outs[0][0, i]), f"row {i}")
+
+
+def test_attention_workspace_reused_across_calls():
+    """One attention workspace, holding the previous call's partials, serves calls of different
+    shapes in a row (split and dense, 32 and 40 heads): every call equals the same call on a
+    fresh workspace, bit for bit."""
+    big = Workload("reuse_big", B=8, S_max=5000, Lq=1, seqlens=(5000, 4000, 3000, 2100, 5000, 4999,
+                                                            2500, 4097), Hi=8, Di=64, topk=1024,
+                   init=16, local=256, H=32, Dqk=576, Dv=512, seed=98)
+    small = Workload("reuse_small", B=3, S_max=3000, Lq=1, seqlens=(3000, 2000, 2600), Hi=8, Di=64,
+                     topk=512, init=4, local=64, H=40, Dqk=576, Dv=512, seed=99)
+    cases = []
+    for wl in (big, small):
+        X = device_inputs(wl)
+        _, idx, nsel, _, _ = run_path(wl, X)
+        cases.append((wl, X, idx, nsel))
+    need = max(lsa.lsa_mla_workspace_bytes(wl.B, 1, wl.H, wl.Dv, wl.S_max, wl.topk, dense)
+               for wl, _, _, _ in cases for dense in (False, True))
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
+    for rnd in range(2):
+        for wl, X, idx, nsel in cases:
+            for dense in (False, True):
+                print(f"case reuse {wl.name} dense={dense} round {rnd}", flush=True)
+                args = (X["q0"][:, 0], X["kv0"], None if dense else idx[:, 0],
+                        None if dense else nsel[:, 0], X["seqlens"], wl.Dv, wl.scale)
+                lse_a = torch.empty(wl.B, wl.H, dtype=torch.float32, device="cuda")
+                lse_b = torch.empty_like(lse_a)
+                a = lsa.lsa_sparse_mla_decode(*args, lse=lse_a, workspace=ws)
+                b = lsa.lsa_sparse_mla_decode(*args, lse=lse_b)  # a fresh workspace
+                torch.cuda.synchronize()
+                assert torch.equal(a, b) and torch.equal(lse_a, lse_b), (wl.name, dense)

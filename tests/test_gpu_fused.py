@@ -85,10 +85,12 @@ def test_fused_is_deterministic_and_ignores_workspace_contents():
 
 
 @pytest.mark.parametrize("B,S,seqlens", [
-    # chunks of 3200 keys (63 lists per row): every chunk cuts its tied list to its exact top R,
+    # chunks of 8192 keys (25 lists per row): every chunk cuts its tied list to its exact top R,
     # then two merge levels
     (8, 200000, (200000, 150001, 99999, 2049, 2048, 60000, 131072, 7000)),
-    # chunks of 896 keys (112 lists per row): every middle key is a candidate, two merge levels
+    # 37 lists per row, two merge levels, rows of very different lengths
+    (2, 300000, (300000, 5000)),
+    # chunks of 6272 keys (16 lists per row): the cut lists, one merge
     (2, 100000, (100000, 33333)),
 ])
 def test_fused_all_equal_scores_many_lists(B, S, seqlens):
