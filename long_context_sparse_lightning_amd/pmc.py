@@ -120,6 +120,10 @@ def summarize(fetch_csv, write_csv, calib_mib, workload, path, alg_bytes, cmd_fe
         for cn, r in res.items():
             f.write(f"| {cn} | {r['kernel_raw_bytes_mean'] / 1e6:.1f} MB ({r['dispatches']} dispatches) | "
                     f"{r['copy_raw_bytes'] / 1e6:.1f} MB | {r['factor']:.4f} | {r['kernel_bytes_per_launch'] / 1e6:.1f} MB |\n")
+        f.write("\n| kernel | FETCH_SIZE bytes per call | WRITE_SIZE bytes per call |\n|---|---|---|\n")
+        for kname in kernels:
+            f.write(f"| {kname} | {res['FETCH_SIZE']['bytes_per_kernel'][kname] / 1e6:.1f} MB | "
+                    f"{res['WRITE_SIZE']['bytes_per_kernel'][kname] / 1e6:.1f} MB |\n")
         f.write(f"\nTraffic per call: {traffic / 1e6:.1f} MB; algorithmic bytes per call: "
                 f"{alg_bytes / 1e6:.1f} MB (ratio {traffic / alg_bytes:.4f}).  Calibration: one "
                 f"device copy of {calib_mib} MiB in the same process.\n")
