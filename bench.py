@@ -182,6 +182,16 @@ def time_frontend(wl, dev, stream, calls=20):
     return a.elapsed_time(b) / calls
 
 
+def host_cpu():
+    """Model name and logical CPU count of the host (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            names = [l.split(":", 1)[1].strip() for l in f if l.startswith("model name")]
+    except OSError:
+        names = []
+    return f"{names[0] if names else 'unknown CPU'} ({os.cpu_count()} logical CPUs on the host)"
+
+
 def cpu_baseline(wl, sample_rows, gpu=None):
     """Time the CPU oracle (as it stands) on a bounded sample of the same workload.  With `gpu`
     (host copies of the timed run's indices, n_sel and attention outputs) also re-check parity
@@ -245,6 +255,7 @@ def cpu_baseline(wl, sample_rows, gpu=None):
                 worst_max = max(worst_max, float(np.abs(err).max() / max(np.abs(ref).max(), 1e-300)))
                 worst_l2 = max(worst_l2, float(np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-300)))
     res = {"value": len(rows) / t_total, "unit": "queries/s", "cores": cores, "kind": "oracle",
+           "cpu": host_cpu(),
            "sample": f"{len(rows)} query-row evaluations over the {len(every)} query rows of "
                      f"{wl.name} (each: full indexer scan, top-k and {wl.attn_calls} MLA call(s)); "
                      f"{t_total:.2f} s wall on {cores} threads"}

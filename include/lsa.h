@@ -26,7 +26,10 @@
  * - Sequences: B sequences, the cache of sequence b holds seqlens[b] tokens (device int32),
  *   the last Lq of which are the current queries.  Query i of sequence b sits at position
  *   p = seqlens[b] - Lq + i and may see keys [0, p] (n = p + 1 keys).
- *   Caller preconditions (device-side, not checked): Lq <= seqlens[b] <= S_max.
+ *   Caller preconditions (device-side, not checked): Lq <= seqlens[b] <= S_max.  With the
+ *   environment variable LSA_DEBUG_BOUNDS set (to anything but "0"), every entry point copies
+ *   seqlens (and index_seqlens) to the host, waits for them and returns LSA_ERR_BAD_SHAPE when a
+ *   precondition fails, before launching anything: a debugging mode that synchronises the stream.
  * - bf16 tensors are passed as raw 16-bit storage (`const void*`).  All layouts are dense,
  *   row-major, with the last dimension contiguous.
  * - Errors: host-checkable problems return a non-zero status BEFORE anything is enqueued, and
@@ -65,6 +68,11 @@ const char* lsa_status_str(lsa_status s);
 /* Detail of the last failure on the calling thread ("" if none).  Valid until the next call
  * on this thread. */
 const char* lsa_last_error(void);
+
+/* The device-side precondition on sequence lengths, checked on a HOST copy: returns the first
+ * b with seqlens_host[b] < Lq or seqlens_host[b] > S_max, or -1 when every length is valid.
+ * (The LSA_DEBUG_BOUNDS mode applies it to each call's seqlens.) */
+int lsa_check_seqlens(const int32_t* seqlens_host, int B, int Lq, int S_max);
 
 /*
  * Lightning-indexer scores ("LSA" section; the fused epilogue of "预填充优化" accumulates

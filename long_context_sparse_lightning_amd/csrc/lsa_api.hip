@@ -4,8 +4,12 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <stdlib.h>
+#include <string.h>
+
 #include <atomic>
 #include <mutex>
+#include <vector>
 
 #include "lsa.h"
 #include "lsa_internal.h"
@@ -31,6 +35,39 @@ lsa_status launched(hipError_t err, const char* what) {
   if (err != hipSuccess)
     return fail(LSA_ERR_LAUNCH, "%s: kernel launch failed: %s", what, hipGetErrorString(err));
   return ok();
+}
+
+// LSA_DEBUG_BOUNDS set (and not "0") in the environment: every entry point copies its sequence
+// lengths to the host, waits for them and checks the device-side preconditions before
+// launching (a debugging mode: it synchronises the stream on every call).
+bool debug_bounds() {
+  static const bool on = [] {
+    const char* e = getenv("LSA_DEBUG_BOUNDS");
+    return e != nullptr && *e != '\0' && strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+lsa_status debug_check(const char* fn, const int32_t* seqlens, int B, int Lq, int S_max, void* stream,
+                       const int32_t* index_seqlens = nullptr) {
+  if (!debug_bounds() || B <= 0) return LSA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<int32_t> h(static_cast<size_t>(B)), hi(index_seqlens ? static_cast<size_t>(B) : 0);
+  hipError_t err = hipMemcpyAsync(h.data(), seqlens, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (err == hipSuccess && index_seqlens)
+    err = hipMemcpyAsync(hi.data(), index_seqlens, hi.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (err == hipSuccess) err = hipStreamSynchronize(s);
+  if (err != hipSuccess)
+    return fail(LSA_ERR_LAUNCH, "%s: LSA_DEBUG_BOUNDS copy of seqlens failed: %s", fn, hipGetErrorString(err));
+  const int bad = lsa_check_seqlens(h.data(), B, Lq, S_max);
+  if (bad >= 0)
+    return fail(LSA_ERR_BAD_SHAPE, "%s: seqlens[%d] = %d outside [Lq = %d, S_max = %d] (LSA_DEBUG_BOUNDS)", fn,
+                bad, h[bad], Lq, S_max);
+  for (int b = 0; b < static_cast<int>(hi.size()); ++b)
+    if (hi[b] < 0 || hi[b] > h[b])
+      return fail(LSA_ERR_BAD_SHAPE, "%s: index_seqlens[%d] = %d outside [0, seqlens[%d] = %d] (LSA_DEBUG_BOUNDS)",
+                  fn, b, hi[b], b, h[b]);
+  return LSA_OK;
 }
 
 }  // namespace
@@ -96,6 +133,12 @@ const char* lsa_status_str(lsa_status s) {
 
 const char* lsa_last_error(void) { return g_last_error; }
 
+int lsa_check_seqlens(const int32_t* seqlens_host, int B, int Lq, int S_max) {
+  for (int b = 0; b < B; ++b)
+    if (seqlens_host[b] < Lq || seqlens_host[b] > S_max) return b;
+  return -1;
+}
+
 lsa_status lsa_index_scores(const void* q_idx, const float* w, const void* k_idx,
                             const int32_t* seqlens, int B, int Lq, int Hi, int Di, int S_max,
                             float* scores, void* stream) {
@@ -108,6 +151,7 @@ lsa_status lsa_index_scores(const void* q_idx, const float* w, const void* k_idx
   if (B == 0 || Lq == 0) return ok();
   if (!q_idx || !w || !k_idx || !seqlens || !scores)
     return fail(LSA_ERR_NULL_ARG, "lsa_index_scores: NULL q_idx/w/k_idx/seqlens/scores");
+  if (lsa_status st = debug_check("lsa_index_scores", seqlens, B, Lq, S_max, stream)) return st;
   return launched(lsa::launch_index_scores(static_cast<const uint16_t*>(q_idx), w,
                                            static_cast<const uint16_t*>(k_idx), seqlens, B, Lq, Hi,
                                            Di, S_max, scores, static_cast<hipStream_t>(stream)),
@@ -146,6 +190,7 @@ lsa_status lsa_topk_select(const float* scores, const int32_t* seqlens, int B, i
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(LSA_ERR_WORKSPACE, "lsa_topk_select: workspace %zu bytes at %p, need %zu",
                 workspace_bytes, workspace, need);
+  if ((st = debug_check("lsa_topk_select", seqlens, B, Lq, S_max, stream))) return st;
   return launched(lsa::launch_topk(scores, seqlens, B, Lq, S_max, topk, init_tokens, local_tokens,
                                    indices, n_sel, workspace, static_cast<hipStream_t>(stream)),
                   "lsa_topk_select");
@@ -183,6 +228,7 @@ lsa_status lsa_index_topk(const void* q_idx, const float* w, const void* k_idx,
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(LSA_ERR_WORKSPACE, "lsa_index_topk: workspace %zu bytes at %p, need %zu",
                 workspace_bytes, workspace, need);
+  if ((st = debug_check("lsa_index_topk", seqlens, B, Lq, S_max, stream))) return st;
   return launched(lsa::launch_index_topk(static_cast<const uint16_t*>(q_idx), w,
                                          static_cast<const uint16_t*>(k_idx), seqlens, B, Lq, Hi, Di,
                                          S_max, topk, init_tokens, local_tokens, indices, n_sel,
@@ -207,6 +253,7 @@ lsa_status lsa_index_topk_noalloc(const void* q_idx, const float* w, const void*
   if (need > LSA_INDEX_TOPK_SCRATCH_BYTES)
     return fail(LSA_ERR_WORKSPACE, "%s: these sizes need %zu bytes of workspace, more than the %zu of the static one",
                 fn, need, static_cast<size_t>(LSA_INDEX_TOPK_SCRATCH_BYTES));
+  if ((st = debug_check(fn, seqlens, B, Lq, S_max, stream))) return st;
   void* ws = nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = scratch_for(s, &ws, fn)) != LSA_OK) return st;
@@ -236,6 +283,7 @@ lsa_status lsa_block_keys(const void* k_idx, const int32_t* seqlens, int B, int 
   if (first_block < 0) return fail(LSA_ERR_BAD_SHAPE, "%s: first_block=%d < 0", fn, first_block);
   if (B == 0) return ok();
   if (!k_idx || !seqlens || !block_keys) return fail(LSA_ERR_NULL_ARG, "%s: NULL k_idx/seqlens/block_keys", fn);
+  if ((st = debug_check(fn, seqlens, B, 0, S_max, stream))) return st;
   return launched(lsa::launch_block_keys(static_cast<const uint16_t*>(k_idx), seqlens, B, S_max, Di, Bk,
                                          first_block, static_cast<uint16_t*>(block_keys),
                                          static_cast<hipStream_t>(stream)),
@@ -282,6 +330,7 @@ lsa_status lsa_hier_index_topk(const void* q_idx, const float* w, const void* k_
   if (!workspace || workspace_bytes < need)
     return fail(LSA_ERR_WORKSPACE, "%s: workspace %zu bytes at %p, need %zu", fn, workspace_bytes,
                 workspace, need);
+  if ((st = debug_check(fn, seqlens, B, 1, S_max, stream))) return st;
   return launched(lsa::launch_hier_index_topk(static_cast<const uint16_t*>(q_idx), w,
                                               static_cast<const uint16_t*>(k_idx),
                                               static_cast<const uint16_t*>(block_keys), seqlens, B,
@@ -328,6 +377,7 @@ static lsa_status run_mla(const char* fn, const void* q, const void* kv, const i
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(LSA_ERR_WORKSPACE, "%s: workspace %zu bytes at %p, need %zu", fn, workspace_bytes,
                 workspace, need);
+  if ((st = debug_check(fn, seqlens, B, Lq, S_max, stream))) return st;
   return launched(lsa::launch_mla(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv),
                                   indices, n_sel, seqlens, B, Lq, H, Dqk, Dv, S_max, dense ? 0 : topk,
                                   softmax_scale, static_cast<uint16_t*>(out), lse, workspace,
@@ -382,6 +432,7 @@ lsa_status lsa_mtp_draft_attention(const void* q, const void* kv, const int32_t*
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(LSA_ERR_WORKSPACE, "%s: workspace %zu bytes at %p, need %zu", fn, workspace_bytes,
                 workspace, need);
+  if ((st = debug_check(fn, seqlens, B, 1, S_max, stream, index_seqlens))) return st;
   return launched(lsa::launch_mla(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv),
                                   indices, n_sel, seqlens, B, 1, H, Dqk, Dv, S_max, topk, softmax_scale,
                                   static_cast<uint16_t*>(out), lse, workspace,
@@ -432,6 +483,7 @@ lsa_status lsa_index_frontend(const void* cq, const void* hid, const void* wq_b,
   if (!workspace || workspace_bytes < need)
     return fail(LSA_ERR_WORKSPACE, "%s: workspace %zu bytes at %p, need %zu", fn, workspace_bytes,
                 workspace, need);
+  if ((st = debug_check(fn, seqlens, B, Lq, S_max, stream))) return st;
   return launched(lsa::launch_frontend(static_cast<const uint16_t*>(cq), static_cast<const uint16_t*>(hid),
                                        static_cast<const uint16_t*>(wq_b), static_cast<const uint16_t*>(wk),
                                        k_norm_gain, static_cast<const uint16_t*>(w_proj), seqlens, B, Lq,

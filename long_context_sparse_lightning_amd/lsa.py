@@ -24,7 +24,8 @@ EXPORTED = ["lsa_status_str", "lsa_last_error", "lsa_index_scores", "lsa_topk_wo
             "lsa_mla_workspace_bytes", "lsa_sparse_mla_decode", "lsa_sparse_mla_prefill",
             "lsa_index_frontend_workspace_bytes", "lsa_index_frontend",
             "lsa_mtp_draft_workspace_bytes", "lsa_mtp_draft_attention", "lsa_block_keys",
-            "lsa_hier_workspace_bytes", "lsa_hier_index_topk", "lsa_index_topk_noalloc"]
+            "lsa_hier_workspace_bytes", "lsa_hier_index_topk", "lsa_index_topk_noalloc",
+            "lsa_check_seqlens"]
 
 INDEX_TOPK_SCRATCH_BYTES = 48 << 20  # LSA_INDEX_TOPK_SCRATCH_BYTES
 
@@ -51,6 +52,8 @@ def lib():
         L.lsa_status_str.restype = ctypes.c_char_p
         L.lsa_last_error.argtypes = []
         L.lsa_last_error.restype = ctypes.c_char_p
+        L.lsa_check_seqlens.argtypes = [P, I, I, I]
+        L.lsa_check_seqlens.restype = I
         L.lsa_index_scores.argtypes = [P, P, P, P, I, I, I, I, I, P, P]
         L.lsa_index_scores.restype = I
         L.lsa_topk_workspace_bytes.argtypes = [I, I, I, I, I, I]
@@ -86,6 +89,16 @@ def lib():
         L.lsa_hier_index_topk.restype = I
         _lib = L
     return _lib
+
+
+def check_seqlens(seqlens, Lq, S_max) -> int:
+    """The device-side precondition Lq <= seqlens[b] <= S_max on a host copy of the lengths:
+    the first b that violates it, or -1 (the check LSA_DEBUG_BOUNDS=1 makes on every call)."""
+    import numpy as np
+
+    h = np.ascontiguousarray(np.asarray(seqlens.cpu() if hasattr(seqlens, "cpu") else seqlens,
+                                        dtype=np.int32))
+    return int(lib().lsa_check_seqlens(h.ctypes.data_as(ctypes.c_void_p), h.size, Lq, S_max))
 
 
 def _check(status: int) -> None:

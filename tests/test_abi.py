@@ -227,3 +227,14 @@ def test_binding_rejects_host_tensors():
         lsa.lsa_index_scores(torch.zeros(1, 1, 4, 32, dtype=torch.bfloat16),
                              torch.zeros(1, 1, 4), torch.zeros(1, 64, 32, dtype=torch.bfloat16),
                              torch.tensor([64], dtype=torch.int32))
+
+
+def test_check_seqlens_host_side():
+    """The precondition check of LSA_DEBUG_BOUNDS mode on host arrays: Lq <= seqlens[b] <= S_max."""
+    assert lsa.check_seqlens([5, 100, 1000], 1, 1000) == -1
+    assert lsa.check_seqlens([5, 100, 1001], 1, 1000) == 2     # beyond the cache
+    assert lsa.check_seqlens([5, 0, 1000], 1, 1000) == 1       # no room for the query
+    assert lsa.check_seqlens([50, 49], 50, 100) == 1           # prefill chunk longer than seq
+    assert lsa.check_seqlens([-3], 0, 10) == 0
+    assert lsa.check_seqlens([], 1, 10) == -1
+    assert lsa.check_seqlens([0, 10], 0, 10) == -1             # block keys: Lq = 0
