@@ -142,8 +142,8 @@ lsa_status lsa_index_topk(const void* q_idx, const float* w, const void* k_idx,
                           int init_tokens, int local_tokens, int32_t* indices, int32_t* n_sel,
                           void* workspace, size_t workspace_bytes, void* stream);
 
-/* Size of the static device workspace of lsa_index_topk_noalloc (48 MiB per device). */
-#define LSA_INDEX_TOPK_SCRATCH_BYTES (48u << 20)
+/* Size of the static device workspace of lsa_index_topk_noalloc (16 MiB per device). */
+#define LSA_INDEX_TOPK_SCRATCH_BYTES (16u << 20)
 
 /*
  * lsa_index_topk without a caller workspace, for callers that cannot allocate device memory

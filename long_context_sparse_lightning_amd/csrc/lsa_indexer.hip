@@ -69,7 +69,8 @@ struct IndexParams {
   int row0, topk, init, local, R;
   uint32_t* count;  // [group rows][chunks]
   uint32_t* range;  // [group rows][chunks][2]
-  uint2* cand;      // [group rows][chunks][keys_per_wg]
+  uint2* cand;      // [group rows][chunks][list_stride]
+  int list_stride;  // sel::list_capacity(R, keys_per_wg)
 };
 
 template <int DI, bool FUSED>
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
     }
     sel::chunk_candidates<kThreads, kStageItems, true>(
         key, valid, z - a + 1, P.R, sel::list_cap(P.R), start, hist, sh,
-        P.cand + static_cast<size_t>(blockIdx.x) * keys_per_wg, P.count + blockIdx.x,
+        P.cand + static_cast<size_t>(blockIdx.x) * P.list_stride, P.count + blockIdx.x,
         P.range + 2 * blockIdx.x, run_mn, run_mx);
   }
 }
@@ -468,7 +469,7 @@ hipError_t launch_any(const IndexParams& P, int Di, long grid, hipStream_t strea
 }
 
 struct FusedPlan {
-  int keys_per_wg = kWgStride, chunks = 1;
+  int keys_per_wg = kWgStride, chunks = 1, stride = 1;  // stride: of the candidate lists
   long rows = 0, group = 1;
   size_t count_bytes = 0, range_bytes = 0, cand_bytes = 0, level1_bytes = 0;
 };
@@ -478,7 +479,8 @@ FusedPlan fused_plan(int B, int Lq, int S_max, int topk, int init_tokens, int lo
   pl.rows = static_cast<long>(B) * Lq;
   pl.keys_per_wg = keys_per_workgroup(pl.rows, S_max, true);
   pl.chunks = (S_max + pl.keys_per_wg - 1) / pl.keys_per_wg;
-  const size_t per_row = static_cast<size_t>(pl.chunks) * pl.keys_per_wg * sizeof(uint2);
+  pl.stride = std::max(1, sel::list_capacity(topk - init_tokens - local_tokens, pl.keys_per_wg));
+  const size_t per_row = static_cast<size_t>(pl.chunks) * pl.stride * sizeof(uint2);
   pl.group = std::max<long>(1, std::min<long>(pl.rows, static_cast<long>(kFusedBudget / per_row)));
   pl.count_bytes = (static_cast<size_t>(pl.group) * pl.chunks * 4 + 255) & ~static_cast<size_t>(255);
   pl.range_bytes = (static_cast<size_t>(pl.group) * pl.chunks * 8 + 255) & ~static_cast<size_t>(255);
@@ -530,6 +532,7 @@ hipError_t launch_index_topk(const uint16_t* q_idx, const float* w, const uint16
   P.S_max = S_max;
   P.keys_per_wg = pl.keys_per_wg;
   P.chunks_per_row = pl.chunks;
+  P.list_stride = pl.stride;
   P.topk = topk;
   P.init = init_tokens;
   P.local = local_tokens;
@@ -545,7 +548,7 @@ hipError_t launch_index_topk(const uint16_t* q_idx, const float* w, const uint16
     hipError_t err = launch_any<true>(P, Di, g * pl.chunks, stream);
     if (err != hipSuccess) return err;
     err = launch_topk_merge(seqlens, Lq, S_max, topk, init_tokens, local_tokens, static_cast<int>(r0),
-                            static_cast<int>(g), pl.chunks, pl.keys_per_wg, P.count, P.range, P.cand,
+                            static_cast<int>(g), pl.chunks, pl.stride, P.count, P.range, P.cand,
                             level1, indices, n_sel, stream);
     if (err != hipSuccess) return err;
   }

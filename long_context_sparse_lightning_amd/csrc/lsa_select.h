@@ -127,6 +127,12 @@ __device__ __forceinline__ int digit_shift(uint32_t mn, uint32_t mx) {
 // (The merge holds R + R/4 <= 1280 candidates per list in registers at R = 1008.)
 __host__ __device__ constexpr int list_cap(int R) { return R + (R >> 2); }
 
+// Pairs a candidate list of a chunk of `chunk` positions can hold: at most list_cap(R), and never
+// more than the chunk has positions.  The lists are laid out with this stride.
+__host__ __device__ constexpr int list_capacity(int R, int chunk) {
+  return list_cap(R) < chunk ? list_cap(R) : chunk;
+}
+
 // LDS words chunk_candidates needs besides its histogram (ITEMS: items per thread).
 template <int THREADS, int ITEMS = 32>
 constexpr int chunk_scratch_words() { return 3 * (THREADS / kWave) + 8 + ITEMS; }

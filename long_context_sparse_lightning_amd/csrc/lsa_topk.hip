@@ -61,7 +61,7 @@ struct TopkParams {
   int cap;           // most pairs a chunk list holds (sel::chunk_candidates)
   int row0;          // first row of this group
   int chunks;        // chunk lists per row
-  int chunk_keys;    // capacity of each list
+  int chunk_keys;    // capacity of each list (the stride of cand)
   uint32_t* count;   // [group rows][chunks]
   uint32_t* range;   // [group rows][chunks][2] bounds of each list's keys
   uint2* cand;       // [group rows][chunks][chunk_keys] (key, position)
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kChunkThreads, 4) void topk_chunk_kernel(TopkParams
     valid |= ((s >= a && s <= z) ? 1u : 0u) << j;
   }
   sel::chunk_candidates<kChunkThreads, kChunkItems>(key, valid, m, P.R, P.cap, base, hist, sh,
-                                                    P.cand + static_cast<size_t>(blockIdx.x) * kChunk,
+                                                    P.cand + static_cast<size_t>(blockIdx.x) * P.chunk_keys,
                                                     P.count + blockIdx.x, P.range + 2 * blockIdx.x);
 }
 
@@ -397,7 +397,7 @@ Level1 level1_plan(long rows, int chunks, int R) {
 
 struct Plan {
   long rows = 0;
-  int R = 0, chunks = 1;
+  int R = 0, chunks = 1, cap = 1;  // cap: the lists' stride (sel::list_capacity)
   long group = 1;  // rows per launch pair
   size_t count_bytes = 0, range_bytes = 0, cand_bytes = 0;
   Level1 l1;
@@ -409,7 +409,8 @@ Plan make_plan(int B, int Lq, int S_max, int topk, int init_tokens, int local_to
   pl.rows = static_cast<long>(B) * Lq;
   pl.R = topk - init_tokens - local_tokens;
   pl.chunks = (S_max + kChunk - 1) / kChunk;
-  const size_t per_row = static_cast<size_t>(pl.chunks) * kChunk * sizeof(uint2);
+  pl.cap = sel::list_capacity(pl.R, kChunk);
+  const size_t per_row = static_cast<size_t>(pl.chunks) * std::max(pl.cap, 1) * sizeof(uint2);
   pl.group = std::max<long>(1, std::min<long>(pl.rows, static_cast<long>(kWorkspaceBudget / per_row)));
   pl.count_bytes = align256(static_cast<size_t>(pl.group) * pl.chunks * 4);
   pl.range_bytes = align256(static_cast<size_t>(pl.group) * pl.chunks * 8);
@@ -497,7 +498,7 @@ hipError_t launch_topk(const float* scores, const int32_t* seqlens, int B, int L
   P.R = pl.R;
   P.cap = sel::list_cap(pl.R);
   P.chunks = pl.chunks;
-  P.chunk_keys = kChunk;
+  P.chunk_keys = std::max(pl.cap, 1);
   char* ws = align_workspace(workspace);
   P.count = reinterpret_cast<uint32_t*>(ws);
   P.range = reinterpret_cast<uint32_t*>(ws + pl.count_bytes);

@@ -27,7 +27,7 @@ EXPORTED = ["lsa_status_str", "lsa_last_error", "lsa_index_scores", "lsa_topk_wo
             "lsa_hier_workspace_bytes", "lsa_hier_index_topk", "lsa_index_topk_noalloc",
             "lsa_check_seqlens"]
 
-INDEX_TOPK_SCRATCH_BYTES = 48 << 20  # LSA_INDEX_TOPK_SCRATCH_BYTES
+INDEX_TOPK_SCRATCH_BYTES = 16 << 20  # LSA_INDEX_TOPK_SCRATCH_BYTES
 
 
 class LsaError(RuntimeError):

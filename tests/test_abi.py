@@ -102,9 +102,9 @@ def test_index_topk_noalloc_argument_errors():
     assert f(p, p, p, p, 1, 1, 32, 128, 4096, 8, 5, 4, p, p, None) == 2  # init + local > topk
     assert f(p, None, p, p, 1, 1, 32, 128, 4096, 256, 4, 64, p, p, None) == 1
     assert f(None, None, None, None, 0, 1, 32, 128, 4096, 256, 4, 64, None, None, None) == 0
-    big = L.lsa_index_topk_workspace_bytes(64, 1, 131072, 2048, 16, 1024)
+    big = L.lsa_index_topk_workspace_bytes(256, 1, 131072, 2048, 16, 1024)
     assert big > lsa.INDEX_TOPK_SCRATCH_BYTES
-    assert f(p, p, p, p, 64, 1, 32, 128, 131072, 2048, 16, 1024, p, p, None) == 4
+    assert f(p, p, p, p, 256, 1, 32, 128, 131072, 2048, 16, 1024, p, p, None) == 4
     assert "static" in _err()
     # the bench shapes fit
     for B, S in ((32, 131072), (8, 32768), (4, 983040)):
