@@ -48,7 +48,8 @@ constexpr int kHeadGroup = 32;    // heads per workgroup
 constexpr int kMaxSplits = 64;    // one per lane in the combine
 constexpr int kMaxRowsPerSplit = 2048;  // row positions of a split staged in LDS
 constexpr int kPartStride = 20;   // floats per head in the partial-logit exchange (16 rows + pad)
-constexpr int kTargetWorkgroups = 512;  // two per CU
+constexpr int kTargetWorkgroups = 256;  // one per CU (see make_plan)
+constexpr int kMinKeysPerSplit = 64;    // four tiles
 constexpr int kCombineThreads = 256;   // four (row, head) pairs per workgroup
 constexpr int kXcds = 8;               // accelerator complex dies (one L2 each)
 constexpr float kRescaleSlack = 8.0f;   // log2 units the running max may exceed the reference
@@ -540,9 +541,13 @@ MlaPlan make_plan(long rows, int H, int Dv, int S_max, int topk, int dense, int 
   pl.hgroups = (H + kHeadGroup - 1) / kHeadGroup;
   const long keys = dense ? S_max : topk;
   const long units = rows * pl.hgroups;
-  // two workgroups per CU are resident (LDS); aim to fill the 256 CUs twice
+  // Decode splits: about one workgroup per CU, each streaming at least four tiles.  Two
+  // workgroups fit on a CU, but every split pays a prologue of two dependent memory round trips
+  // (indices, then rows) and writes a partial that the combine reads back, so fewer, longer
+  // splits win: measured per decode call, 16 tiles x 8 splits beat 8 x 16 at 32 rows, 4 x 32
+  // beat 2 x 64 at 8 rows, and 4 tiles x 32 splits beat 2 x 64 at 4 rows.
   long splits = units > 0 ? (kTargetWorkgroups + units - 1) / units : 1;
-  splits = std::min<long>(splits, (keys + kTile - 1) / kTile);
+  splits = std::min<long>(splits, (keys + kMinKeysPerSplit - 1) / kMinKeysPerSplit);
   splits = std::min<long>(splits, kMaxSplits);
   if (!dense) splits = std::max<long>(splits, (keys + kMaxRowsPerSplit - 1) / kMaxRowsPerSplit);
   splits = std::max<long>(splits, 1);

@@ -12,13 +12,18 @@
 // compete, for the R = topk - I - W slots in between.
 //  1. chunk (many workgroups per row, one per 16384 positions): each keeps a superset of its
 //     local top R -- every middle key whose digit is at least that of its local R-th largest,
-//     found with an LDS histogram -- and writes them as (key, position) pairs with a count.
-//     No global atomics and nothing that must be cleared beforehand.
+//     found with an LDS histogram -- and writes them as (key, position) pairs with a count.  A
+//     list never exceeds R + R/4 pairs: when ties would overfill it, it is cut to the chunk's
+//     exact top R by (key descending, position ascending), which still holds every row winner
+//     from that chunk.  Lists sit at that fixed stride.  No global atomics and nothing that
+//     must be cleared beforehand.
 //  2. merge (one workgroup per row): an exact radix select over the union of the chunk lists
 //     (candidates held in registers) narrows the threshold to a bin of at most 1024 keys, which
 //     are then ranked by (key descending, position ascending) in LDS.  Winners are set in an
 //     LDS bitmap over the middle range, which a popcount prefix compacts into ascending
-//     indices.
+//     indices.  A row with more than 16 lists first merges them in groups of 16, each group
+//     into one list of its exact top R (a first-level launch), so the final merge never holds
+//     more than 16 lists.
 // Digits adapt to the data: a digit is a window of key bits placed from the min/max of the keys
 // still in play ((k >> s) - base, at most 2^11 + 1 values), so scores concentrated in a narrow
 // range still spread over the histogram instead of piling into a few bins.
