@@ -1,8 +1,9 @@
-"""Prefill attention on calls of at least 512 query rows (one workgroup per row, no split of the
-selection), against the oracle: on lists from the top-k (ragged rows and dense [0, n) rows, odd
-row counts, a second head group with padding, small windows) and on arbitrary lists a caller may
-pass (shuffled, repeated positions, overlapping runs, random, empty), which are also compared
-with the same rows computed by a call of fewer rows (split selections and the combine)."""
+"""Prefill attention on calls of at least 256 (query row, head group) units (one workgroup per
+unit, no split of the selection), against the oracle: on lists from the top-k (ragged rows and
+dense [0, n) rows, odd row counts, a second head group with padding, small windows, the small
+80/64 head dims) and on arbitrary lists a caller may pass (shuffled, repeated positions,
+overlapping runs, random, empty), which are also compared with the same rows computed by a call
+of fewer rows (split selections and the combine)."""
 import numpy as np
 import pytest
 import torch
@@ -35,13 +36,17 @@ CASES = [
     (Workload("pb_small_window", B=1, S_max=5000, Lq=512, seqlens=(5000,), Hi=8, Di=64,
               topk=384, init=2, local=8, H=32, seed=304, **MLA),
      [(0, 0), (0, 1), (0, 511)]),
+    # the small head dims (80 / 64: a tile is not a whole number of DMA instructions)
+    (Workload("pb_small_dims", B=1, S_max=3000, Lq=300, seqlens=(3000,), Hi=4, Di=32, topk=256,
+              init=4, local=64, H=4, Dqk=80, Dv=64, scale=1.0 / 80 ** 0.5, seed=306),
+     [(0, 0), (0, 1), (0, 150), (0, 299)]),
 ]
 
 
 @pytest.mark.parametrize("wl,rows", CASES, ids=[c[0].name for c in CASES])
 def test_prefill_rows_against_oracle(wl, rows):
     print(f"case {wl.name}", flush=True)
-    assert wl.B * wl.Lq >= 512  # one workgroup per row
+    assert wl.B * wl.Lq * ((wl.H + 31) // 32) >= 256  # one workgroup per unit
     X = device_inputs(wl)
     sc, idx, nsel, outs, lses = run_path(wl, X)
     torch.cuda.synchronize()
