@@ -11,9 +11,9 @@
 // rows) and runs four wavefronts; its LDS stays under 80 KB so that two workgroups share a CU
 // and hide each other's latency (prefill rows; decode splits are sized for about one per CU).
 // The slice is cut into 16-row tiles that stream through a 3-stage LDS ring filled by LDS-DMA
-// loads (global_load_lds_dwordx4: a lane names one 16-byte
-// piece of a latent row and the hardware writes it straight into LDS), so one to two tiles are
-// in flight while one is computed, without holding any of it in registers.  Every 1152-byte
+// loads (global_load_lds_dwordx4: a lane names one 16-byte piece of a latent row and the
+// hardware writes it straight into LDS), so one to two tiles are in flight while one is
+// computed, without holding any of it in registers.  Every 1152-byte
 // row is read whole by consecutive lanes.  Within LDS, tile row r is rotated by r 16-byte
 // units, which keeps every access pattern below free of bank conflicts.
 //  * logits: S (32 heads x 16 rows) = Q . KV_tile^T on the 16x16x32 bf16 matrix core, the
