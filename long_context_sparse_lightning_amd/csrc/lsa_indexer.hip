@@ -50,11 +50,12 @@
 namespace lsa {
 namespace {
 
-constexpr int kThreads = 256;             // 4 wavefronts
+constexpr int kThreads = 256;             // 4 wavefronts (the default workgroup)
+constexpr int kWideThreads = 512;         // 8 wavefronts: fused launches of few workgroups
+constexpr int kWideMaxGrid = 128;         // ... at most this many (one per CU at 136 VGPRs)
 constexpr int kTileKeys = 32;             // keys per wavefront step
-constexpr int kWgStride = kTileKeys * 4;  // keys per workgroup step
+constexpr int kWgStride = kTileKeys * 4;  // keys per step of a 4-wavefront workgroup
 constexpr int kMaxKeysPerWg = 8192;       // LDS score staging: 32 KB
-constexpr int kStageItems = kMaxKeysPerWg / kThreads;  // staged scores per thread (fused epilogue)
 constexpr size_t kFusedBudget = size_t(256) << 20;     // candidate lists of one row group
 
 struct IndexParams {
@@ -73,9 +74,13 @@ struct IndexParams {
   int list_stride;  // sel::list_capacity(R, keys_per_wg)
 };
 
-template <int DI, bool FUSED>
-__global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
+// THREADS: 256, or 512 for a fused launch too small to fill the chip (each wavefront keeps one
+// key tile in flight, so more wavefronts per workgroup stream more bytes per CU).
+template <int DI, bool FUSED, int THREADS = kThreads>
+__global__ __launch_bounds__(THREADS) void index_scores_kernel(IndexParams P) {
   constexpr int NC = DI / 16;  // matrix-core steps over the head dimension
+  constexpr int WG_STRIDE = kTileKeys * (THREADS / 64);  // keys per workgroup step
+  constexpr int STAGE_ITEMS = kMaxKeysPerWg / THREADS;   // staged scores per thread (fused)
   const uint16_t* __restrict__ q_idx = P.q_idx;
   const float* __restrict__ w = P.w;
   const uint16_t* __restrict__ k_idx = P.k_idx;
@@ -130,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
   // now, while the query loads are in flight, so the selection after the scan starts with it
   uint32_t* hist = reinterpret_cast<uint32_t*>(stage + keys_per_wg);  // keys_per_wg % 128 == 0
   if constexpr (FUSED)
-    for (int i = threadIdx.x; i < 2 * sel::kBins / 4; i += kThreads)
+    for (int i = threadIdx.x; i < 2 * sel::kBins / 4; i += THREADS)
       reinterpret_cast<u32x4*>(hist)[i] = u32x4{0u, 0u, 0u, 0u};
   wait_vmcnt<0>();  // the query and weights are in: only key tiles are in flight below
 
@@ -162,52 +167,52 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexParams P) {
     }
   };
 
-  // tiles of this wavefront: t0 + i * kWgStride for i < ntiles; two per iteration, so both
+  // tiles of this wavefront: t0 + i * WG_STRIDE for i < ntiles; two per iteration, so both
   // register buffers have fixed roles and the loop has no exit in the middle
   int t = start + wave * kTileKeys;
-  const int ntiles = t < end ? (end - t + kWgStride - 1) / kWgStride : 0;
+  const int ntiles = t < end ? (end - t + WG_STRIDE - 1) / WG_STRIDE : 0;
   bf16x8 ka[NC], kc[NC];
   load_tile(ka, t);
   int i = 0;
   for (; i + 3 <= ntiles; i += 2) {  // both prefetches of an iteration are tiles of this wavefront
-    load_tile(kc, t + kWgStride);
+    load_tile(kc, t + WG_STRIDE);
     __builtin_amdgcn_sched_barrier(0);  // keep the whole prefetch ahead of the matrix-core work
     score_tile(ka, t);
-    load_tile(ka, t + 2 * kWgStride);
+    load_tile(ka, t + 2 * WG_STRIDE);
     __builtin_amdgcn_sched_barrier(0);
-    score_tile(kc, t + kWgStride);
-    t += 2 * kWgStride;
+    score_tile(kc, t + WG_STRIDE);
+    t += 2 * WG_STRIDE;
   }
   // the last one or two tiles, with no load past the end: nothing is left in flight for the
   // selection that follows to wait for
   if (i + 2 <= ntiles) {
-    load_tile(kc, t + kWgStride);
+    load_tile(kc, t + WG_STRIDE);
     __builtin_amdgcn_sched_barrier(0);
     score_tile(ka, t);
-    score_tile(kc, t + kWgStride);
+    score_tile(kc, t + WG_STRIDE);
   } else if (i < ntiles) {
     score_tile(ka, t);
   }
   __syncthreads();
   if constexpr (!FUSED) {
     float* srow = P.scores + static_cast<size_t>(row) * S_max + start;
-    for (int i = threadIdx.x; i < end - start; i += kThreads) srow[i] = stage[i];
+    for (int i = threadIdx.x; i < end - start; i += THREADS) srow[i] = stage[i];
   } else {
-    __shared__ uint32_t sh[sel::chunk_scratch_words<kThreads, kStageItems>()];
+    __shared__ uint32_t sh[sel::chunk_scratch_words<THREADS, STAGE_ITEMS>()];
     const int a = comp_a, z = comp_z;  // competing positions here
-    uint32_t key[kStageItems];
+    uint32_t key[STAGE_ITEMS];
     uint32_t valid = 0;
 #pragma unroll
-    for (int j = 0; j < kStageItems; ++j) {
-      // read unconditionally (the dynamic LDS holds at least kStageItems * kThreads words), so
+    for (int j = 0; j < STAGE_ITEMS; ++j) {
+      // read unconditionally (the dynamic LDS holds at least STAGE_ITEMS * THREADS words), so
       // no read waits behind a branch
-      const float v = stage[j * kThreads + static_cast<int>(threadIdx.x)];
-      const int s = start + j * kThreads + static_cast<int>(threadIdx.x);
+      const float v = stage[j * THREADS + static_cast<int>(threadIdx.x)];
+      const int s = start + j * THREADS + static_cast<int>(threadIdx.x);
       const bool ok = s >= a && s <= z;
       key[j] = ok ? sel::order_key(v) : 0u;
       valid |= (ok ? 1u : 0u) << j;
     }
-    sel::chunk_candidates<kThreads, kStageItems, true>(
+    sel::chunk_candidates<THREADS, STAGE_ITEMS, true>(
         key, valid, z - a + 1, P.R, sel::list_cap(P.R), start, hist, sh,
         P.cand + static_cast<size_t>(blockIdx.x) * P.list_stride, P.count + blockIdx.x,
         P.range + 2 * blockIdx.x, run_mn, run_mx);
@@ -425,12 +430,10 @@ hipError_t launch_qb(const uint16_t* q_idx, const float* w, const uint16_t* k_id
   return hipGetLastError();
 }
 
-// Keys per workgroup: about 512 workgroups (two per CU, all resident at once) with whole
-// workgroup steps per chunk; long chunks amortise the query/weight loads and the ramp of each
-// workgroup.  The fused variant also keeps at most 128 chunks per row (the merge's limit).
-// Keys per workgroup: enough workgroups to fill the chip twice, at most 8192 keys (the LDS score
-// stage).  The fused call also keeps a row to at most 16 candidate lists where the cap allows, so
-// one merge takes them all (decode_32k: 16 chunks of 2048 keys, 14 us for its merge, against 64
+// Keys per workgroup: about 512 workgroups (two per CU, all resident at once), whole workgroup
+// steps per chunk (long chunks amortise the query/weight loads and the ramp of each workgroup),
+// at most 8192 keys (the LDS score stage).  The fused call also keeps a row to at most 16
+// candidate lists where the cap allows, so one merge takes them all (decode_32k: 16 chunks of 2048 keys, 14 us for its merge, against 64
 // chunks of 512 keys and two merge levels, 23 us; decode_1m: 8192-key chunks scan 2% faster than
 // 7680-key ones).
 int keys_per_workgroup(long rows, int S_max, bool fused) {
@@ -442,28 +445,37 @@ int keys_per_workgroup(long rows, int S_max, bool fused) {
   return static_cast<int>(per);
 }
 
-template <int DI, bool FUSED>
+template <int DI, bool FUSED, int THREADS>
 hipError_t launch_kernel(const IndexParams& P, long grid, hipStream_t stream) {
   if (grid > 0x7fffffffL) return hipErrorInvalidConfiguration;
   size_t lds = static_cast<size_t>(P.keys_per_wg) * sizeof(float);
   if (FUSED) {
     lds += static_cast<size_t>(2 * sel::kBins) * sizeof(uint32_t);  // the selection's histogram
-    const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(index_scores_kernel<DI, FUSED>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               static_cast<int>(lds));
+    const hipError_t err = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(index_scores_kernel<DI, FUSED, THREADS>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL((index_scores_kernel<DI, FUSED>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
-                     lds, stream, P);
+  hipLaunchKernelGGL((index_scores_kernel<DI, FUSED, THREADS>), dim3(static_cast<unsigned>(grid)),
+                     dim3(THREADS), lds, stream, P);
   return hipGetLastError();
 }
 
+// wide: 512-thread workgroups (fused launches only; keys_per_wg a multiple of their step)
 template <bool FUSED>
-hipError_t launch_any(const IndexParams& P, int Di, long grid, hipStream_t stream) {
+hipError_t launch_any(const IndexParams& P, int Di, long grid, hipStream_t stream, bool wide = false) {
+  if (FUSED && wide) {
+    switch (Di) {
+      case 32: return launch_kernel<32, FUSED, kWideThreads>(P, grid, stream);
+      case 64: return launch_kernel<64, FUSED, kWideThreads>(P, grid, stream);
+      case 128: return launch_kernel<128, FUSED, kWideThreads>(P, grid, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (Di) {
-    case 32: return launch_kernel<32, FUSED>(P, grid, stream);
-    case 64: return launch_kernel<64, FUSED>(P, grid, stream);
-    case 128: return launch_kernel<128, FUSED>(P, grid, stream);
+    case 32: return launch_kernel<32, FUSED, kThreads>(P, grid, stream);
+    case 64: return launch_kernel<64, FUSED, kThreads>(P, grid, stream);
+    case 128: return launch_kernel<128, FUSED, kThreads>(P, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -545,7 +557,9 @@ hipError_t launch_index_topk(const uint16_t* q_idx, const float* w, const uint16
   for (long r0 = 0; r0 < pl.rows; r0 += pl.group) {
     const long g = std::min(pl.group, pl.rows - r0);
     P.row0 = static_cast<int>(r0);
-    hipError_t err = launch_any<true>(P, Di, g * pl.chunks, stream);
+    // a launch too small to fill the chip runs 8-wavefront workgroups (one per CU either way)
+    const bool wide = g * pl.chunks <= kWideMaxGrid && pl.keys_per_wg % (kTileKeys * kWideThreads / 64) == 0;
+    hipError_t err = launch_any<true>(P, Di, g * pl.chunks, stream, wide);
     if (err != hipSuccess) return err;
     err = launch_topk_merge(seqlens, Lq, S_max, topk, init_tokens, local_tokens, static_cast<int>(r0),
                             static_cast<int>(g), pl.chunks, pl.stride, P.count, P.range, P.cand,
