@@ -146,7 +146,8 @@ constexpr int chunk_scratch_words() { return 3 * (THREADS / kWave) + 8 + ITEMS; 
 // positions among its copies fill the list up to exactly R -- the chunk's exact top R by (key
 // descending, position ascending), which still holds every row winner from this chunk.  The
 // pairs (key, position) go to `out`, their number to *count, and bounds lo <= every written
-// key <= hi to range[0], range[1].  hist: 2*kBins words of LDS, zeroed here; sh:
+// key <= hi to range[0], range[1].  hist: 2*kBins words of LDS (8-byte aligned; it also
+// stages the list before the stores), zeroed here; sh:
 // chunk_scratch_words<THREADS, ITEMS>() words.  Call from every thread, with m >= 1.
 // PREPARED: the caller has already zeroed hist (and ordered that before this call by a
 // barrier) and passes in (mn, mx) bounds whose workgroup-wide min and max are those of the
@@ -255,25 +256,25 @@ __device__ void chunk_candidates(const uint32_t (&key)[ITEMS], uint32_t valid, i
       __syncthreads();  // every thread has read sh_scan before the stores below reuse it
     }
   }
-  // Stores: the kept items of one wavefront and one item index j go to one contiguous run
-  // (ordered by wavefront, then j, then lane; the list is a set).
-  uint32_t mine = 0;  // this wavefront's kept items
+  // Stores: each thread's kept items form one contiguous run at the exclusive prefix of the
+  // kept counts (ordered by thread, then j; the list is a set).  A list of at most kBins pairs is
+  // staged in LDS first -- the histogram is free once the prefix's barrier has passed -- so that
+  // it leaves as consecutive 8-byte pairs across the lanes; a longer one is written directly.
+  uint32_t total;
+  uint32_t at = block_prefix<WAVES>(static_cast<uint32_t>(__popc(keep)), sh_scan, &total);
+  if (total <= static_cast<uint32_t>(kBins)) {
+    uint2* staged = reinterpret_cast<uint2*>(hist);  // 2 * kBins words
 #pragma unroll
-  for (int j = 0; j < ITEMS; ++j) mine += static_cast<uint32_t>(__popcll(wave_ballot((keep >> j) & 1u)));
-  if ((tid & (kWave - 1)) == 0) sh_scan[wave] = mine;
-  __syncthreads();
-  uint32_t at = 0, total = 0;
+    for (int j = 0; j < ITEMS; ++j)
+      if ((keep >> j) & 1u)
+        staged[at++] = make_uint2(key[j], static_cast<uint32_t>(base + j * THREADS + tid));
+    __syncthreads();
+    for (uint32_t i = tid; i < total; i += THREADS) out[i] = staged[i];
+  } else {
 #pragma unroll
-  for (int w = 0; w < WAVES; ++w) {
-    at += w < wave ? sh_scan[w] : 0u;
-    total += sh_scan[w];
-  }
-#pragma unroll
-  for (int j = 0; j < ITEMS; ++j) {
-    const uint64_t bj = wave_ballot((keep >> j) & 1u);
-    if ((keep >> j) & 1u)
-      out[at + lanes_below(bj)] = make_uint2(key[j], static_cast<uint32_t>(base + j * THREADS + tid));
-    at += static_cast<uint32_t>(__popcll(bj));
+    for (int j = 0; j < ITEMS; ++j)
+      if ((keep >> j) & 1u)
+        out[at++] = make_uint2(key[j], static_cast<uint32_t>(base + j * THREADS + tid));
   }
   if (tid == 0) {
     *count = total;
