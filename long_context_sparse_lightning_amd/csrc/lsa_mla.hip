@@ -206,11 +206,13 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
                       : zero_bf16x8();
     }
   }
-  // this split's row positions (clamped into the cache) staged in LDS
+  // this split's row positions (clamped into the cache) staged in LDS, padded to whole tiles
+  // with the last one (rows past the slice repeat its last row), so a tile's lookups need no
+  // clamp
   if constexpr (sparse) {
     const int32_t* ilist = P.indices + static_cast<size_t>(row) * P.topk;
-    for (int j = tid; j < j1 - j0; j += kThreads) {
-      const int jj = j0 + j;
+    for (int j = tid; j < ntiles * kTile; j += kThreads) {
+      const int jj = j0 + min(j, j1 - j0 - 1);
       slice[j] = jj < cnt_sel ? min(max(ilist[jj], 0), P.S_max - 1) : app0 + (jj - cnt_sel);
     }
   }
@@ -232,17 +234,15 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
   // cache row positions of the next tile to be issued, read from LDS one step ahead so that
   // the issue itself waits on nothing
   int pos[C::DPW];
-  auto fetch_pos = [&](int tile) {
+  auto fetch_pos = [&](int tile) {  // tile < ntiles
     const int jb = tile * kTile;  // relative to j0
 #pragma unroll
     for (int k = 0; k < C::DPW; ++k) {
-      const int j = min(jb + dma_r[k], j1 - j0 - 1);  // rows past the slice repeat its last row
-      if constexpr (sparse) pos[k] = slice[j];
-      else pos[k] = j0 + j;
+      if constexpr (sparse) pos[k] = slice[jb + dma_r[k]];
+      else pos[k] = j0 + min(jb + dma_r[k], j1 - j0 - 1);  // past the end: the last row again
     }
   };
-  auto issue = [&](int tile) {
-    uint16_t* stage = ring[tile % kStages];
+  auto issue = [&](uint16_t* stage) {
 #pragma unroll
     for (int k = 0; k < C::DPW; ++k) {
       const uint16_t* src = kv_b + static_cast<size_t>(pos[k]) * DQK + 8 * dma_c[k];
@@ -252,10 +252,34 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
   };
   if (ntiles > 0) {
     fetch_pos(0);
-    issue(0);
-    fetch_pos(1);
-    if (ntiles > 1) issue(1);
-    fetch_pos(2);
+    issue(ring[0]);
+    if (ntiles > 1) {
+      fetch_pos(1);
+      issue(ring[1]);
+    }
+    if (ntiles > 2) fetch_pos(2);
+  }
+
+  // LDS element offsets of this lane's fragment reads within a stage.  Keys: step i reads
+  // logical unit c0 + 16 i of tile row c16; the swizzle only permutes units inside groups of
+  // eight, so steps before the last sit at k_lane + 128 i, and the last step, which may lie past
+  // Dqk (it then meets a zero query fragment), reads a clamped in-row unit.  Values: column
+  // block wave + 4 i starts at unit 4 (wave + 4 i), i.e. at v_lane + 128 i, for transpose-read
+  // row group h2 (rows 8 h2 + 4 (G >> 1) + (jl >> 2), 4 columns per lane group).
+  static_assert(C::KSW == 1 || 16 * (C::KSW - 1) <= C::SWZ_UNITS, "key steps before the last are swizzled");
+  static_assert(C::NBW == 1 || DV / 8 <= C::SWZ_UNITS, "value units are swizzled");
+  const int c0 = 4 * wave + q16;
+  const int k_lane = C::slot(c16, min(c0, C::UNITS - 1)) * 8;
+  const int k_last = C::slot(c16, min(c0 + 16 * (C::KSW - 1), C::UNITS - 1)) * 8;
+  int v_lane[2];
+  {
+    const int G = lane >> 4, jl = lane & 15;
+    const int dim0 = 32 * wave + 16 * (G & 1) + 4 * (jl & 3);
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int vr = 8 * h2 + 4 * (G >> 1) + (jl >> 2);  // = acc_row(4*h2 + k, g) for slot k
+      v_lane[h2] = C::slot(vr, min(dim0 >> 3, C::UNITS - 1)) * 8 + (dim0 & 7);
+    }
   }
 
   float m_ref = -INFINITY, l_run = 0.0f;  // for head `col` (identical in every wavefront)
@@ -263,18 +287,21 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
 #pragma unroll
   for (int i = 0; i < C::NBW; ++i) o[i] = f32x16{};
 
-  for (int t = 0; t < ntiles; ++t) {
+  // Tile t, in ring stage S = t % kStages.  The loop below is unrolled by kStages so that S is
+  // a compile-time constant: every LDS address is then a per-lane register plus an immediate.
+  auto tile_step = [&](const int t, auto stage) {
+    constexpr int S = decltype(stage)::value;
     if (t + 1 < ntiles) wait_vmcnt<C::DPW>();  // tile t+1 may still be in flight
     else wait_vmcnt<0>();
     ring_barrier();  // every wavefront's pieces of tile t are in LDS; tile t - 1 is consumed
     // tile t + 2 goes into the stage of tile t - 1: every wavefront has passed the barrier
     // above, so all of its reads of that stage (and of the partial logits) are complete
     if (t + 2 < ntiles) {
-      issue(t + 2);
-      fetch_pos(t + 3);
+      issue(ring[(S + 2) % kStages]);
+      if (t + 3 < ntiles) fetch_pos(t + 3);
     }
 
-    const uint16_t* kvt = ring[t % kStages];
+    const uint16_t* kvt = ring[S];
     // ---- partial logits over this wavefront's Dqk steps, as S^T = KV_tile . Q^T so that a
     // lane holds one head (c16) for four consecutive tile rows (4*q16 + r): one 16-byte LDS
     // write per head block
@@ -284,11 +311,9 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
       f32x4 acc0 = {}, acc1 = {};
       bf16x8 kb[C::KSW];
 #pragma unroll
-      for (int i = 0; i < C::KSW; ++i) {
-        const int c = 4 * (wave + 4 * i) + q16;  // logical unit
+      for (int i = 0; i < C::KSW; ++i)
         kb[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                               &kvt[C::slot(c16, min(c, C::UNITS - 1)) * 8]));
-      }
+                                               kvt + (i + 1 < C::KSW ? k_lane + 128 * i : k_last)));
 #pragma unroll
       for (int i = 0; i < C::KSW; ++i) {
         acc0 = mfma16(kb[i], qf[0][i], acc0);
@@ -323,33 +348,28 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
     // the probabilities, so they are requested here and arrive during the softmax.  Each B
     // operand (8 tile rows of one column per lane) is two LDS transpose reads.
     u32x2 hv[C::NBW][2];
-    {
-      const int G = lane >> 4, jl = lane & 15;  // transpose reads: 16 columns x 4 rows per group
 #pragma unroll
-      for (int i = 0; i < C::NBW; ++i) {
-        const int nb = wave + 4 * i;
-        if (C::NB % 4 == 0 || nb < C::NB) {  // statically true when the blocks divide evenly
-          const int dim0 = 32 * nb + 16 * (G & 1) + 4 * (jl & 3);
-          const int unit = dim0 >> 3, eoff = dim0 & 7;
+    for (int i = 0; i < C::NBW; ++i) {
+      if (C::NB % 4 == 0 || wave + 4 * i < C::NB) {  // statically true when the blocks divide evenly
 #pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const int vr = 8 * h2 + 4 * (G >> 1) + (jl >> 2);  // = acc_row(4*h2 + k, g) for slot k
-            hv[i][h2] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(&kvt[C::slot(vr, unit) * 8 + eoff])));
-          }
-        }
+        for (int h2 = 0; h2 < 2; ++h2)
+          hv[i][h2] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(kvt + v_lane[h2] + 128 * i)));
       }
     }
 
     // ---- online softmax for head `col` (every wavefront computes the same values)
     const int tile_j = j0 + t * kTile;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sv[e] *= P.scale_log2;
+    if (tile_j + kTile > j1) {  // the slice's last, partial tile: rows past its end drop out
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (tile_j + acc_row(e, g) >= j1) sv[e] = -INFINITY;
+    }
     float mloc = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const bool ok = tile_j + acc_row(e, g) < j1;
-      sv[e] = ok ? sv[e] * P.scale_log2 : -INFINITY;
-      mloc = fmaxf(mloc, sv[e]);
-    }
+    for (int e = 0; e < 8; ++e) mloc = fmaxf(mloc, sv[e]);
     mloc = fmaxf(mloc, xor32(mloc));
     const bool grow = mloc > m_ref + kRescaleSlack;
     if (__ballot(grow)) {
@@ -389,6 +409,12 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
         o[i] = mfma32(pa, __builtin_bit_cast(bf16x8, u32x4{hv[i][0].x, hv[i][0].y, hv[i][1].x, hv[i][1].y}),
                       o[i]);
     }
+  };
+  static_assert(kStages == 3, "the tile loop is unrolled by the ring depth");
+  for (int t = 0; t < ntiles; t += kStages) {
+    tile_step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) tile_step(t + 1, std::integral_constant<int, 1>{});
+    if (t + 2 < ntiles) tile_step(t + 2, std::integral_constant<int, 2>{});
   }
   wait_vmcnt<0>();
   if (wave == 0 && g == 0) inv_head[col] = l_run > 0.0f ? 1.0f / l_run : 0.0f;
