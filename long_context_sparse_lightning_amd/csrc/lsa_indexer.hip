@@ -223,7 +223,6 @@ constexpr int kQbWaves = 8;        // wavefronts per workgroup (two per SIMD)
 constexpr int kQbRowsPerWave = 2;  // query rows per wavefront (4 at one wavefront per SIMD,
                                    // 416 registers, is 13% slower: nothing hides the barriers)
 constexpr int kQbMinRows = 16;     // row count from which the query-blocked scan is used
-constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3 for gfx9-family raw buffers
 constexpr int kDropOffset = 1 << 30;      // beyond any row: such stores are dropped
 
 struct QbParams {

@@ -15,6 +15,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3 for gfx9-family raw buffers
 
 // 16-byte global load of 8 bf16 values.
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
