@@ -200,20 +200,17 @@ __global__ __launch_bounds__(THREADS) void index_scores_kernel(IndexParams P) {
   } else {
     __shared__ uint32_t sh[sel::chunk_scratch_words<THREADS, STAGE_ITEMS>()];
     const int a = comp_a, z = comp_z;  // competing positions here
-    uint32_t key[STAGE_ITEMS];
-    uint32_t valid = 0;
+    uint32_t key[STAGE_ITEMS];  // 0: the position does not compete
 #pragma unroll
     for (int j = 0; j < STAGE_ITEMS; ++j) {
       // read unconditionally (the dynamic LDS holds at least STAGE_ITEMS * THREADS words), so
       // no read waits behind a branch
       const float v = stage[j * THREADS + static_cast<int>(threadIdx.x)];
       const int s = start + j * THREADS + static_cast<int>(threadIdx.x);
-      const bool ok = s >= a && s <= z;
-      key[j] = ok ? sel::order_key(v) : 0u;
-      valid |= (ok ? 1u : 0u) << j;
+      key[j] = (s >= a && s <= z) ? sel::order_key(v) : 0u;
     }
     sel::chunk_candidates<THREADS, STAGE_ITEMS, true>(
-        key, valid, z - a + 1, P.R, sel::list_cap(P.R), start, hist, sh,
+        key, z - a + 1, P.R, sel::list_cap(P.R), start, hist, sh,
         P.cand + static_cast<size_t>(blockIdx.x) * P.list_stride, P.count + blockIdx.x,
         P.range + 2 * blockIdx.x, run_mn, run_mx);
   }

@@ -137,8 +137,12 @@ __host__ __device__ constexpr int list_capacity(int R, int chunk) {
 template <int THREADS, int ITEMS = 32>
 constexpr int chunk_scratch_words() { return 3 * (THREADS / kWave) + 8 + ITEMS; }
 
-// Candidates of one chunk: item j of this thread (bit j of `valid`) holds the key at position
-// base + j*THREADS + threadIdx.x; m = number of valid items in the workgroup.  Writes to `out`
+// Candidates of one chunk: item j of this thread holds the key at position
+// base + j*THREADS + threadIdx.x, or 0 if that position does not compete; m = number of
+// competing items in the workgroup.  No per-item validity mask is kept: scores are finite, so a
+// competing key is at least order_key(-inf) = 0x007fffff and the digit window, which starts at
+// the smallest competing key >> s (s <= 21), starts at 1 or above; the absent key 0 therefore
+// never enters a histogram, a boundary bin or the list.  Writes to `out`
 // every valid key when m <= R, else a superset of the chunk's contribution to the row's top R:
 // every key whose digit is at least that of the chunk's R-th largest.  When that superset would
 // exceed `cap` pairs (cap >= R; many keys share the R-th largest's digit), narrower digits are
@@ -153,29 +157,31 @@ constexpr int chunk_scratch_words() { return 3 * (THREADS / kWave) + 8 + ITEMS; 
 // barrier) and passes in (mn, mx) bounds whose workgroup-wide min and max are those of the
 // valid keys -- a scan that produced the keys can track them on the way.
 template <int THREADS, int ITEMS, bool PREPARED = false>
-__device__ void chunk_candidates(const uint32_t (&key)[ITEMS], uint32_t valid, int m, int R,
+__device__ void chunk_candidates(const uint32_t (&key)[ITEMS], int m, int R,
                                  int cap, int base, uint32_t* hist, uint32_t* sh, uint2* out,
                                  uint32_t* count, uint32_t* range, uint32_t mn = 0xffffffffu,
                                  uint32_t mx = 0u) {
   constexpr int WAVES = THREADS / kWave;
   constexpr int kPer = kBins / THREADS;
-  static_assert(ITEMS <= 32, "valid/keep masks are 32 bits");
+  static_assert(ITEMS <= 32, "keep masks are 32 bits");
   uint32_t* sh_scan = sh;
   uint32_t* sh_mm = sh + WAVES;
   uint32_t* sh_out = sh + 3 * WAVES;
   uint32_t* sh_tie = sh + 3 * WAVES + 8;  // [ITEMS] tied items per item index
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & (kWave - 1);
-  uint32_t keep = valid;
+  uint32_t keep = 0;
   if constexpr (!PREPARED) {
     if (m > R)  // hist is 16-byte aligned
       for (int i = tid; i < 2 * kBins / 4; i += THREADS) reinterpret_cast<u32x4*>(hist)[i] = u32x4{0u, 0u, 0u, 0u};
+    // key - 1 wraps the absent key 0 to the largest value, so it never lowers the minimum; it
+    // never raises the maximum
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
-      if (valid & (1u << j)) {
-        mn = min(mn, key[j]);
-        mx = max(mx, key[j]);
-      }
+      mn = min(mn, key[j] - 1u);
+      mx = max(mx, key[j]);
     }
+    mn += 1u;  // a thread with no competing item keeps 0xffffffff (wrapped back to 0 here)
+    mn = mn ? mn : 0xffffffffu;
   }
   block_minmax<WAVES>(mn, mx, sh_mm);  // its barrier also orders the zeroing
   uint32_t lo = mn;
@@ -184,8 +190,10 @@ __device__ void chunk_candidates(const uint32_t (&key)[ITEMS], uint32_t valid, i
     const uint32_t dbase = mn >> s_in;
     uint32_t* hw = hist + (wave & 1) * kBins;  // one copy per half of the waves
 #pragma unroll
-    for (int j = 0; j < ITEMS; ++j)
-      if (valid & (1u << j)) atomicAdd(&hw[bin_slot<THREADS>((key[j] >> s_in) - dbase)], 1u);
+    for (int j = 0; j < ITEMS; ++j) {
+      const uint32_t d = (key[j] >> s_in) - dbase;  // wraps past kBins for the absent key 0
+      if (d < static_cast<uint32_t>(kBins)) atomicAdd(&hw[bin_slot<THREADS>(d)], 1u);
+    }
     __syncthreads();
     uint32_t c[kPer];
 #pragma unroll
@@ -206,7 +214,7 @@ __device__ void chunk_candidates(const uint32_t (&key)[ITEMS], uint32_t valid, i
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < ITEMS; ++j)
-        if ((valid & (1u << j)) && (key[j] >> s_in) == pref)
+        if ((key[j] >> s_in) == pref)
           atomicAdd(&hist[bin_slot<THREADS>((key[j] >> s2) - base2)], 1u);
       __syncthreads();
 #pragma unroll
@@ -219,10 +227,9 @@ __device__ void chunk_candidates(const uint32_t (&key)[ITEMS], uint32_t valid, i
       s_in = s2;
     }
     lo = pref << s_in;  // no kept key is below the boundary bin
-    keep = 0;
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j)
-      keep |= ((valid & (1u << j)) && (key[j] >> s_in) >= pref ? 1u : 0u) << j;
+      keep |= ((key[j] >> s_in) >= pref ? 1u : 0u) << j;
     if (tie_break) {
       // `inbin` copies of the key `pref` and `need` of them kept: the lowest positions, i.e. by
       // item index j, then thread -- count the copies per j, find the item index j* where the
@@ -232,7 +239,7 @@ __device__ void chunk_candidates(const uint32_t (&key)[ITEMS], uint32_t valid, i
       uint32_t tied = 0;
 #pragma unroll
       for (int j = 0; j < ITEMS; ++j) {
-        const bool t = (valid & (1u << j)) && key[j] == pref;
+        const bool t = key[j] == pref;
         tied |= (t ? 1u : 0u) << j;
         const uint32_t n = static_cast<uint32_t>(__popcll(wave_ballot(t)));
         if (lane == 0 && n) atomicAdd(&sh_tie[j], n);
@@ -255,6 +262,9 @@ __device__ void chunk_candidates(const uint32_t (&key)[ITEMS], uint32_t valid, i
       keep &= ~drop;
       __syncthreads();  // every thread has read sh_scan before the stores below reuse it
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) keep |= (key[j] != 0u ? 1u : 0u) << j;
   }
   // Stores: each thread's kept items form one contiguous run at the exclusive prefix of the
   // kept counts (ordered by thread, then j; the list is a set).  A list of at most kBins pairs is

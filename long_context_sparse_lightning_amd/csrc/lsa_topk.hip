@@ -97,20 +97,19 @@ __global__ __launch_bounds__(kChunkThreads, 4) void topk_chunk_kernel(TopkParams
     return;
   }
   // all loads issued at once, as buffer loads over the row (one lane offset, a scalar offset per
-  // item): positions past the row read 0, and they and every other position outside [a, z] are
-  // masked
+  // item): positions past the row read 0; they and every other position outside [a, z] get the
+  // absent key 0
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(P.scores + static_cast<size_t>(row) * P.S_max), 0, 4 * P.S_max, kBufferFlags);
   uint32_t key[kChunkItems];
-  uint32_t valid = 0;
 #pragma unroll
   for (int j = 0; j < kChunkItems; ++j) {
     const int s = base + j * kChunkThreads + tid;
-    key[j] = order_key(__uint_as_float(
+    const uint32_t k = order_key(__uint_as_float(
         __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * tid, 4 * (base + j * kChunkThreads), 0)));
-    valid |= ((s >= a && s <= z) ? 1u : 0u) << j;
+    key[j] = (s >= a && s <= z) ? k : 0u;
   }
-  sel::chunk_candidates<kChunkThreads, kChunkItems>(key, valid, m, P.R, P.cap, base, hist, sh,
+  sel::chunk_candidates<kChunkThreads, kChunkItems>(key, m, P.R, P.cap, base, hist, sh,
                                                     P.cand + static_cast<size_t>(blockIdx.x) * P.chunk_keys,
                                                     P.count + blockIdx.x, P.range + 2 * blockIdx.x);
 }
