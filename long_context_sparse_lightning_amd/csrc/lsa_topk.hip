@@ -56,6 +56,7 @@ constexpr int kMaxPositions = 1 << 20;
 constexpr int kMaxChunks = 128;      // chunk lists per row the merge accepts
 constexpr int kGroupLists = 16;      // lists per first-level merge when a row has more
 constexpr int kTieList = kMergeThreads;             // ties ranked in LDS up to this many
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 constexpr size_t kWorkspaceBudget = size_t(1024) << 20;
 static_assert(kMaxChunks <= kGroupLists * kGroupLists, "two merge levels cover every row");
 
@@ -123,7 +124,7 @@ constexpr int kMsOff = kMsCnt + 2 * kMergeWaves;    // [kMaxChunks + 1] candidat
 constexpr int kMsHist = kMsOff + kMaxChunks + 16;   // [kBins] radix rounds, then the rank list
 static_assert(kMaxChunks <= kMergeThreads, "one thread per chunk list");
 constexpr int kMsBits = kMsHist + kBins;            // bitmap over the middle range
-static_assert(2 * kTieList <= kBins, "the rank list reuses the histogram");
+static_assert(2 * (kTieList + 1) <= kBins, "the rank list (64-bit entries and a pad) reuses the histogram");
 
 // One workgroup merges candidate lists into an exact top R by (key descending, position
 // ascending).  LIST_OUT = false: the row's final selection -- grid (rows), all `chunks` lists of
@@ -140,8 +141,8 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
   uint32_t* sh_res = lds + kMsRes;
   uint32_t* sh_off = lds + kMsOff;
   uint32_t* sh_h = lds + kMsHist;
-  uint32_t* sh_lk = lds + kMsHist;                                     // rank list keys
-  int32_t* sh_lp = reinterpret_cast<int32_t*>(lds + kMsHist + kTieList);  // rank list positions
+  // rank list: (key << 32) | ~position, so that a larger entry ranks first
+  uint64_t* sh_l = reinterpret_cast<uint64_t*>(lds + kMsHist);
   uint32_t* sh_bits = lds + kMsBits;
   const int tid = threadIdx.x;
   const int grow = LIST_OUT ? static_cast<int>(blockIdx.x) / P.groups : static_cast<int>(blockIdx.x);
@@ -302,24 +303,24 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
     });
     if (need < pop) {
       if (pop <= static_cast<uint32_t>(kTieList)) {
-        // rank the bin's keys by (key descending, position ascending)
+        // rank the bin's keys by (key descending, position ascending): one 64-bit entry per
+        // key, and each thread counts the entries above its own, two per LDS read
         each([&](uint32_t k, int32_t p) {
           if ((k >> s_in) == pref) {
             const uint32_t slot = atomicAdd(&sh_res[8], 1u);
-            sh_lk[slot] = k;
-            sh_lp[slot] = p;
+            sh_l[slot] = (static_cast<uint64_t>(k) << 32) | ~static_cast<uint32_t>(p);
           }
         });
+        if (tid == 0) sh_l[pop] = 0u;  // pads an odd count (below every entry)
         __syncthreads();
         if (static_cast<uint32_t>(tid) < pop) {
-          const uint32_t kt = sh_lk[tid];
-          const int32_t pt = sh_lp[tid];
+          const uint64_t mine = sh_l[tid];
           uint32_t rank = 0;
-          for (uint32_t u = 0; u < pop; ++u) {
-            const uint32_t ku = sh_lk[u];
-            rank += (ku > kt || (ku == kt && sh_lp[u] < pt)) ? 1u : 0u;
+          for (uint32_t u = 0; u < pop; u += 2) {
+            const u64x2 v = *reinterpret_cast<const u64x2*>(&sh_l[u]);
+            rank += (v.x > mine ? 1u : 0u) + (v.y > mine ? 1u : 0u);
           }
-          if (rank < need) win(kt, pt);
+          if (rank < need) win(static_cast<uint32_t>(mine >> 32), static_cast<int32_t>(~static_cast<uint32_t>(mine)));
         }
       } else {
         // more than kTieList equal keys (s_in == 0): the `need` lowest positions among them, by
