@@ -81,6 +81,33 @@ def test_topk_on_tied_fp32_scores(S, topk, init, local, seqlens):
     assert np.array_equal(idx, ref_idx)
 
 
+def test_topk_extreme_finite_scores():
+    """Rows reaching -FLT_MAX and +FLT_MAX, subnormals and signed zeros, over several chunks
+    whose first and last ones are partial: the selection marks positions outside a chunk's
+    competing range with the key 0, which must stay below every finite score's key (the
+    smallest is that of -FLT_MAX) and out of every histogram and list."""
+    print("case topk extreme finite scores", flush=True)
+    S, B = 70000, 3
+    big = np.float32(np.finfo(np.float32).max)
+    tiny = np.float32(np.finfo(np.float32).smallest_subnormal)
+    h = gen.hashes(4343, gen.TAGS["scores"], np.arange(B * S, dtype=np.uint64))
+    vals = gen.bf16_bits_to_f32(gen.values_from_hashes(h, gen.NORMAL)).reshape(B, 1, S).copy()
+    vals[0, 0, ::7] = -big                   # the lowest key in every chunk
+    vals[0, 0, 5::11] = big                  # and the highest
+    vals[0, 0, 3::13] = tiny
+    vals[0, 0, 4::13] = -tiny
+    vals[1, 0, :] = -big                     # one key value everywhere but a few positions
+    vals[1, 0, 9000:9300] = -0.0
+    vals[1, 0, 30000:30010] = big
+    vals[2, 0, :] = 0.0                      # signed zeros and extremes only
+    vals[2, 0, 1::2] = -0.0
+    vals[2, 0, 17::1000] = -big
+    vals[2, 0, 18::1000] = big
+    idx, nsel, ref_idx, ref_n = _topk_both(vals, (70000, 40001, 16385), 2048, 16, 1024)
+    assert np.array_equal(nsel, ref_n)
+    assert np.array_equal(idx, ref_idx)
+
+
 def test_topk_all_equal_scores():
     S = 50000
     vals = np.zeros((2, 1, S), np.float32)
