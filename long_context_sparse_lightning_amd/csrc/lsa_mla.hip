@@ -389,12 +389,13 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
     // even conversion to bf16
     uint32_t pw[4];
     float psum = 0.0f;
+    const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bf16x2 pr = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[2 * i] - m_ref)),
                          static_cast<__bf16>(__builtin_amdgcn_exp2f(sv[2 * i + 1] - m_ref))};
       pw[i] = __builtin_bit_cast(uint32_t, pr);
-      psum += __uint_as_float(pw[i] << 16) + __uint_as_float(pw[i] & 0xffff0000u);
+      psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);  // both bf16 values, in fp32
     }
     psum += xor32(psum);
     l_run += psum;
