@@ -332,37 +332,56 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scores_qb_kernel(QbParams
   };
   // head sum across the lane pair and the range-checked store of query row q on tile t (tiles
   // outside [0, ntiles) store nothing)
-  auto store_row = [&](int q, int t, float part) {
+  // Tiles are stored in pairs: an even tile's sums wait in `held`, and with the odd tile after
+  // it lanes g = 0 store the even tile's 32 keys and lanes g = 1 the odd tile's, one store of 64
+  // consecutive keys.
+  float held[RPW];
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) held[q] = 0.0f;
+  auto store_row = [&](int q, int t, float part, bool odd) {
     part += xor32(part);
-    const int key = start + t * kTileKeys + col;  // < end within the last tile or dropped
-    const int off = (g == 0 && static_cast<unsigned>(t) < static_cast<unsigned>(ntiles)) ? 4 * key
-                                                                                         : kDropOffset;
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), rs[q], off, 0, 0);
+    if (!odd) {
+      held[q] = part;
+      return;
+    }
+    const int tt = t - 1 + g;
+    const int key = start + tt * kTileKeys + col;  // < end within the last tile or dropped
+    const int off = static_cast<unsigned>(tt) < static_cast<unsigned>(ntiles) ? 4 * key : kDropOffset;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(g ? part : held[q]), rs[q], off, 0, 0);
   };
 
   // Software pipeline.  Step t, with LDS slots rotating over 4:
-  //   - reads tile t+1's fragments from LDS into registers (written one step earlier),
-  //   - loads tile t+3 from memory into registers,
+  //   - reads tile t+1's fragments from LDS into registers (published at least one step earlier),
+  //   - on even t, loads tiles t+4 and t+5 from memory into one of two register pairs,
   //   - runs row 0's 8 dependent matrix-core steps on tile t, each followed by two elements of
   //     the last row's epilogue of tile t-1; then row r's steps (r >= 1) next to row r-1's
   //     epilogue of tile t, one step behind, so that accumulator is complete,
-  //   - writes tile t+2 (loaded two steps earlier) into its slot, then a barrier.
-  // After the barrier the matrix cores start at once on fragments already in registers.  The
+  //   - on even t, writes tiles t+2 and t+3 (loaded two steps earlier) into their slots, then a
+  //     barrier: the eight wavefronts meet every other step.  A slot is rewritten only after the
+  //     barrier that follows its last read.
+  // After a barrier the matrix cores start at once on fragments already in registers.  The
   // instruction order is fixed with scheduling barriers.  Four steps per iteration give every
   // register and slot a fixed role; steps past the end compute on clamped keys and store nothing.
   f32x16 acc[RPW];
 #pragma unroll
   for (int q = 0; q < RPW; ++q) acc[q] = f32x16{};
   bf16x8 kx[NC], ky[NC];
-  Piece rx = gload(start), ry = gload(start + kTileKeys);
-  lstore(0, rx);  // tile 0
-  rx = gload(start + 2 * kTileKeys);
-  lstore(1, ry);  // tile 1
+  Piece ra[2], rb[2];
+  ra[0] = gload(start);
+  ra[1] = gload(start + kTileKeys);
+  rb[0] = gload(start + 2 * kTileKeys);
+  rb[1] = gload(start + 3 * kTileKeys);
+  lstore(0, ra[0]);  // tile 0
+  lstore(1, ra[1]);  // tile 1
   barrier();
   kread(0, kx);
-  auto step = [&](int t, int slot, const bf16x8 (&kc)[NC], bf16x8 (&kn)[NC], Piece& rl, Piece& rn) {
+  auto step = [&](int t, int slot, const bf16x8 (&kc)[NC], bf16x8 (&kn)[NC], Piece* st, Piece* ld,
+                  bool t_odd) {
     kread(slot, kn);
-    rn = gload(start + (t + 3) * kTileKeys);
+    if (ld) {
+      ld[0] = gload(start + (t + 4) * kTileKeys);
+      ld[1] = gload(start + (t + 5) * kTileKeys);
+    }
     {
       float p = 0.0f;  // last row, tile t-1
 #pragma unroll
@@ -372,7 +391,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scores_qb_kernel(QbParams
         p += relu_w(RPW - 1, 2 * c + 1, acc[RPW - 1][2 * c + 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      store_row(RPW - 1, t - 1, p);
+      store_row(RPW - 1, t - 1, p, !t_odd);
     }
 #pragma unroll
     for (int q = 1; q < RPW; ++q) {
@@ -388,16 +407,21 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scores_qb_kernel(QbParams
       }
       p += relu_w(q - 1, 14, acc[q - 1][14]);
       p += relu_w(q - 1, 15, acc[q - 1][15]);
-      store_row(q - 1, t, p);
+      store_row(q - 1, t, p, t_odd);
     }
-    lstore(slot == 3 ? 0 : slot + 1, rl);
-    barrier();
+    if (st) {
+      lstore((slot + 1) & 3, st[0]);
+      lstore((slot + 2) & 3, st[1]);
+      barrier();
+    }
   };
-  for (int t = 0; t <= ntiles; t += 4) {
-    step(t, 1, kx, ky, rx, ry);
-    step(t + 1, 2, ky, kx, ry, rx);
-    step(t + 2, 3, kx, ky, rx, ry);
-    step(t + 3, 0, ky, kx, ry, rx);
+  // the last row stores tile t - 1 at step t, so its pair (ntiles - 1, ntiles) needs step
+  // ntiles + 1
+  for (int t = 0; t <= ntiles + 1; t += 4) {
+    step(t, 1, kx, ky, rb, ra, false);
+    step(t + 1, 2, ky, kx, nullptr, nullptr, true);
+    step(t + 2, 3, kx, ky, ra, rb, false);
+    step(t + 3, 0, ky, kx, nullptr, nullptr, true);
   }
 }
 
