@@ -55,7 +55,7 @@ constexpr int kRegItems = 20;        // candidates held in registers per merge t
 constexpr int kMaxPositions = 1 << 20;
 constexpr int kMaxChunks = 128;      // chunk lists per row the merge accepts
 constexpr int kGroupLists = 16;      // lists per first-level merge when a row has more
-constexpr int kTieList = kMergeThreads;             // ties ranked in LDS up to this many
+constexpr int kHalfMergeRows = 1024;  // rows from which a launch takes 512-thread merges
 typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 constexpr size_t kWorkspaceBudget = size_t(1024) << 20;
 static_assert(kMaxChunks <= kGroupLists * kGroupLists, "two merge levels cover every row");
@@ -122,9 +122,7 @@ constexpr int kMsRes = kMsScan + kMergeWaves;       // [16] results of select_bi
 constexpr int kMsCnt = kMsRes + 16;                 // [2][kMergeWaves] spare
 constexpr int kMsOff = kMsCnt + 2 * kMergeWaves;    // [kMaxChunks + 1] candidate offsets
 constexpr int kMsHist = kMsOff + kMaxChunks + 16;   // [kBins] radix rounds, then the rank list
-static_assert(kMaxChunks <= kMergeThreads, "one thread per chunk list");
 constexpr int kMsBits = kMsHist + kBins;            // bitmap over the middle range
-static_assert(2 * (kTieList + 1) <= kBins, "the rank list (64-bit entries and a pad) reuses the histogram");
 
 // One workgroup merges candidate lists into an exact top R by (key descending, position
 // ascending).  LIST_OUT = false: the row's final selection -- grid (rows), all `chunks` lists of
@@ -134,8 +132,12 @@ static_assert(2 * (kTieList + 1) <= kBins, "the rank list (64-bit entries and a 
 // them) are written as an unordered (key, position) list for the final merge, which sees each
 // group as one list.  Any top R of a union contains the top R of the whole row that falls in it
 // (the order is total), so the two levels select exactly what one merge would.
-template <bool LIST_OUT>
-__global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P) {
+template <bool LIST_OUT, int THREADS>
+__global__ __launch_bounds__(THREADS, 4) void topk_merge_kernel(TopkParams P) {  // <= 128 VGPRs
+  constexpr int WAVES = THREADS / kWave;
+  constexpr int kTie = THREADS;  // ties ranked in LDS up to this many
+  static_assert(kMaxChunks <= THREADS && 2 * (kTie + 1) <= kBins && THREADS <= kMergeThreads,
+                "one thread per chunk list; the rank list reuses the histogram; the LDS layout");
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   uint32_t* sh_scan = lds + kMsScan;
   uint32_t* sh_res = lds + kMsRes;
@@ -161,21 +163,21 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
     }
   } else {
     if (g.dense) {  // every visible position, then padding
-      for (int j = tid; j < K; j += kMergeThreads) out[j] = j < g.n ? j : -1;
+      for (int j = tid; j < K; j += THREADS) out[j] = j < g.n ? j : -1;
       if (tid == 0) P.n_sel[row] = max(g.n, 0);
       return;
     }
     // forced positions: the I lowest and the W highest fill the ends of the output
-    for (int j = tid; j < I; j += kMergeThreads) out[j] = j;
-    for (int j = tid; j < W; j += kMergeThreads) out[K - W + j] = g.p - W + 1 + j;
+    for (int j = tid; j < I; j += THREADS) out[j] = j;
+    for (int j = tid; j < W; j += THREADS) out[K - W + j] = g.p - W + 1 + j;
     if (tid == 0) P.n_sel[row] = K;
     if (R == 0) return;
   }
 
   const int mid_words = (g.hi - g.lo + 32) >> 5;
   if constexpr (!LIST_OUT)
-    for (int i = tid; i < mid_words; i += kMergeThreads) sh_bits[i] = 0u;
-  for (int i = tid; i < kBins; i += kMergeThreads) sh_h[i] = 0u;
+    for (int i = tid; i < mid_words; i += THREADS) sh_bits[i] = 0u;
+  for (int i = tid; i < kBins; i += THREADS) sh_h[i] = 0u;
   if (tid == 0) {
     sh_res[8] = 0u;   // rank-list length
     sh_res[12] = 0u;  // winners written (LIST_OUT)
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
   }
   {
     uint32_t total;
-    const uint32_t at = block_prefix<kMergeWaves>(c_len, sh_scan, &total);
+    const uint32_t at = block_prefix<WAVES>(c_len, sh_scan, &total);
     if (tid < nl) {
       sh_off[tid] = at;
       atomicMax(&sh_res[9], c_len);
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
   };
   // in registers: list c is held by the TPL threads [c * TPL, (c + 1) * TPL), entry j of it by
   // thread c * TPL + j % TPL in slot j / TPL -- when every list fits
-  const int tpl = kMergeThreads / nl;
+  const int tpl = THREADS / nl;
   const int my_list = tid / tpl, my_j = tid - my_list * tpl;
   const bool in_regs = sh_res[9] <= static_cast<uint32_t>(kRegItems * tpl);
   uint32_t rk[kRegItems];
@@ -245,7 +247,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
       for (int i = 0; i < kRegItems; ++i)
         if (held & (1u << i)) f(rk[i], rp[i]);
     } else {
-      for (uint32_t q = tid; q < nc; q += kMergeThreads) {
+      for (uint32_t q = tid; q < nc; q += THREADS) {
         const uint2 v = *locate(q);
         f(v.x, static_cast<int32_t>(v.y));
       }
@@ -277,23 +279,23 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
     auto in_play = [&](uint32_t k) { return s_in >= 32 || (k >> s_in) == pref; };
     for (;;) {
       each([&](uint32_t k, int32_t) {
-        if (in_play(k)) atomicAdd(&sh_h[bin_slot<kMergeThreads>((k >> s) - dbase)], 1u);
+        if (in_play(k)) atomicAdd(&sh_h[bin_slot<THREADS>((k >> s) - dbase)], 1u);
       });
       __syncthreads();
-      constexpr int kPer = kBins / kMergeThreads;
+      constexpr int kPer = kBins / THREADS;
       uint32_t c[kPer];
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) c[i] = sh_h[i * kMergeThreads + tid];
-      select_bin<kPer, kMergeWaves>(c, need, sh_scan, sh_res);
+      for (int i = 0; i < kPer; ++i) c[i] = sh_h[i * THREADS + tid];
+      select_bin<kPer, WAVES>(c, need, sh_scan, sh_res);
       need -= sh_res[1];
       pop = sh_res[2];
       pref = dbase + sh_res[0];
       s_in = s;
-      if (pop <= static_cast<uint32_t>(kTieList) || s == 0) break;
+      if (pop <= static_cast<uint32_t>(kTie) || s == 0) break;
       const int s_next = max(0, s - 12);
       dbase = pref << (s - s_next);
       s = s_next;
-      for (int i = tid; i < kBins; i += kMergeThreads) sh_h[i] = 0u;
+      for (int i = tid; i < kBins; i += THREADS) sh_h[i] = 0u;
       __syncthreads();
     }
     out_lo = pref << s_in;
@@ -302,7 +304,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
       if ((k >> s_in) > pref || (need == pop && (k >> s_in) == pref)) win(k, p);
     });
     if (need < pop) {
-      if (pop <= static_cast<uint32_t>(kTieList)) {
+      if (pop <= static_cast<uint32_t>(kTie)) {
         // rank the bin's keys by (key descending, position ascending): one 64-bit entry per
         // key, and each thread counts the entries above its own, two per LDS read
         each([&](uint32_t k, int32_t p) {
@@ -323,25 +325,25 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
           if (rank < need) win(static_cast<uint32_t>(mine >> 32), static_cast<int32_t>(~static_cast<uint32_t>(mine)));
         }
       } else {
-        // more than kTieList equal keys (s_in == 0): the `need` lowest positions among them, by
+        // more than kTie equal keys (s_in == 0): the `need` lowest positions among them, by
         // a radix select on the position (below 2^20): its top 12 bits, then its low 8.  Digits
         // are mirrored so that select_bin's target-th largest is the target-th lowest position.
-        constexpr int kPer = kBins / kMergeThreads;
+        constexpr int kPer = kBins / THREADS;
         uint32_t want = need, hi_digit = 0, cut = 0;
         for (int round = 0; round < 2; ++round) {
-          for (int i = tid; i < kBins; i += kMergeThreads) sh_h[i] = 0u;
+          for (int i = tid; i < kBins; i += THREADS) sh_h[i] = 0u;
           __syncthreads();
           each([&](uint32_t k, int32_t p) {
             const uint32_t u = static_cast<uint32_t>(p);
             if (k != pref) return;
-            if (round == 0) atomicAdd(&sh_h[bin_slot<kMergeThreads>(kBins - 1 - (u >> 8))], 1u);
-            else if ((u >> 8) == hi_digit) atomicAdd(&sh_h[bin_slot<kMergeThreads>(kBins - 1 - (u & 255u))], 1u);
+            if (round == 0) atomicAdd(&sh_h[bin_slot<THREADS>(kBins - 1 - (u >> 8))], 1u);
+            else if ((u >> 8) == hi_digit) atomicAdd(&sh_h[bin_slot<THREADS>(kBins - 1 - (u & 255u))], 1u);
           });
           __syncthreads();
           uint32_t c[kPer];
 #pragma unroll
-          for (int i = 0; i < kPer; ++i) c[i] = sh_h[i * kMergeThreads + tid];
-          select_bin<kPer, kMergeWaves>(c, want, sh_scan, sh_res);
+          for (int i = 0; i < kPer; ++i) c[i] = sh_h[i * THREADS + tid];
+          select_bin<kPer, WAVES>(c, want, sh_scan, sh_res);
           want -= sh_res[1];
           const uint32_t d = kBins - 1 - sh_res[0];
           if (round == 0) hi_digit = d;
@@ -362,12 +364,12 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
     }
   } else {
     // compact the middle bitmap into out[I .. I + R)
-    const int wpt = (mid_words + kMergeThreads - 1) / kMergeThreads;
+    const int wpt = (mid_words + THREADS - 1) / THREADS;
     const int w0 = tid * wpt, w1 = min(mid_words, w0 + wpt);
     uint32_t mine = 0;
     for (int w = w0; w < w1; ++w) mine += __popc(sh_bits[w]);
     uint32_t total;
-    uint32_t at = block_prefix<kMergeWaves>(mine, sh_scan, &total);
+    uint32_t at = block_prefix<WAVES>(mine, sh_scan, &total);
     for (int w = w0; w < w1; ++w) {
       uint32_t bits = sh_bits[w];
       while (bits) {
@@ -379,7 +381,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(TopkParams P)
     }
     // fewer winners than slots only when the lists hold fewer than R candidates (not for valid
     // inputs); the slots are then padded rather than left stale
-    for (uint32_t j = total + static_cast<uint32_t>(tid); j < static_cast<uint32_t>(R); j += kMergeThreads)
+    for (uint32_t j = total + static_cast<uint32_t>(tid); j < static_cast<uint32_t>(R); j += THREADS)
       out[I + j] = -1;
   }
 }
@@ -434,7 +436,7 @@ size_t merge_lds_bytes(int S_max) {
 
 // The attribute is a maximum: it is raised only when a launch needs more than the device's
 // current setting, so calls of different sizes do not reset it back and forth.
-template <bool LIST_OUT>
+template <bool LIST_OUT, int THREADS>
 hipError_t set_merge_lds(size_t lds) {
   constexpr int kDevices = 64;
   static std::atomic<size_t> set_to[kDevices];
@@ -442,7 +444,7 @@ hipError_t set_merge_lds(size_t lds) {
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
   if (dev >= 0 && dev < kDevices && set_to[dev].load(std::memory_order_relaxed) >= lds) return hipSuccess;
-  err = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_merge_kernel<LIST_OUT>),
+  err = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_merge_kernel<LIST_OUT, THREADS>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (err == hipSuccess && dev >= 0 && dev < kDevices) {
     size_t cur = set_to[dev].load(std::memory_order_relaxed);
@@ -457,19 +459,19 @@ hipError_t set_merge_lds(size_t lds) {
 // kGroupLists lists and the final merge over the groups' lists.
 hipError_t launch_merges(TopkParams P, int rows, void* level1, hipStream_t stream) {
   const size_t lds = merge_lds_bytes(P.S_max);
-  hipError_t err = set_merge_lds<false>(lds);
+  hipError_t err = set_merge_lds<false, kMergeThreads>(lds);
   if (err != hipSuccess) return err;
   const Level1 l1 = level1_plan(rows, P.chunks, P.R);
   if (l1.groups > 0 && level1 != nullptr) {
     // the first level keeps no bitmap: only the fixed part of the LDS layout
     const size_t lds1 = sizeof(uint32_t) * static_cast<size_t>(kMsBits);
-    if ((err = set_merge_lds<true>(lds1)) != hipSuccess) return err;
+    if ((err = set_merge_lds<true, kMergeThreads>(lds1)) != hipSuccess) return err;
     char* r = static_cast<char*>(level1);
     P.groups = l1.groups;
     P.g_count = reinterpret_cast<uint32_t*>(r);
     P.g_range = reinterpret_cast<uint32_t*>(r + l1.count_bytes);
     P.g_cand = reinterpret_cast<uint2*>(r + l1.count_bytes + l1.range_bytes);
-    hipLaunchKernelGGL(topk_merge_kernel<true>, dim3(static_cast<unsigned>(rows * l1.groups)),
+    hipLaunchKernelGGL((topk_merge_kernel<true, kMergeThreads>), dim3(static_cast<unsigned>(rows * l1.groups)),
                        dim3(kMergeThreads), lds1, stream, P);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     P.chunks = l1.groups;
@@ -478,8 +480,16 @@ hipError_t launch_merges(TopkParams P, int rows, void* level1, hipStream_t strea
     P.range = P.g_range;
     P.cand = P.g_cand;
   }
-  hipLaunchKernelGGL(topk_merge_kernel<false>, dim3(static_cast<unsigned>(rows)), dim3(kMergeThreads), lds,
-                     stream, P);
+  // Many rows whose lists all fit the registers of half a workgroup: 512-thread merges, two rows
+  // per CU at once, whose latency chains overlap.
+  if (rows >= kHalfMergeRows && kRegItems * (kMergeThreads / 2 / P.chunks) >= P.chunk_keys) {
+    if ((err = set_merge_lds<false, kMergeThreads / 2>(lds)) != hipSuccess) return err;
+    hipLaunchKernelGGL((topk_merge_kernel<false, kMergeThreads / 2>), dim3(static_cast<unsigned>(rows)),
+                       dim3(kMergeThreads / 2), lds, stream, P);
+  } else {
+    hipLaunchKernelGGL((topk_merge_kernel<false, kMergeThreads>), dim3(static_cast<unsigned>(rows)),
+                       dim3(kMergeThreads), lds, stream, P);
+  }
   return hipGetLastError();
 }
 

@@ -108,6 +108,21 @@ def test_topk_extreme_finite_scores():
     assert np.array_equal(idx, ref_idx)
 
 
+def test_topk_many_rows_half_size_merges():
+    """1024 query rows select through 512-thread merges (two per CU): heavily tied bf16-valued
+    scores, signed zeros, and rows where more keys than one such merge ranks share the
+    threshold value, against the oracle."""
+    print("case topk 1024 rows", flush=True)
+    S, Lq = 20000, 1024
+    h = gen.hashes(4444, gen.TAGS["scores"], np.arange(Lq * S, dtype=np.uint64))
+    vals = gen.bf16_bits_to_f32(gen.values_from_hashes(h, gen.DYADIC)).reshape(1, Lq, S).copy()
+    vals[0, ::3, 2000:9000] = 0.0          # thousands of keys tied at the threshold
+    vals[0, 1::3, 5000:5600] = -0.0
+    idx, nsel, ref_idx, ref_n = _topk_both(vals, (S,), 2048, 16, 1024)
+    assert np.array_equal(nsel, ref_n)
+    assert np.array_equal(idx, ref_idx)
+
+
 def test_topk_all_equal_scores():
     S = 50000
     vals = np.zeros((2, 1, S), np.float32)
