@@ -17,9 +17,11 @@
 //     exact top R by (key descending, position ascending), which still holds every row winner
 //     from that chunk.  Lists sit at that fixed stride.  No global atomics and nothing that
 //     must be cleared beforehand.
-//  2. merge (one workgroup per row): an exact radix select over the union of the chunk lists
-//     (candidates held in registers) narrows the threshold to a bin of at most 1024 keys, which
-//     are then ranked by (key descending, position ascending) in LDS.  Winners are set in an
+//  2. merge (one workgroup per row, of 1024 threads, or of 512 -- two rows per CU, whose chains
+//     of dependent phases overlap -- for launches of many rows whose lists fit): an exact radix
+//     select over the union of the chunk lists (candidates held in registers) narrows the
+//     threshold to a bin of at most one key per thread, which are then ranked by (key
+//     descending, position ascending) in LDS.  Winners are set in an
 //     LDS bitmap over the middle range, which a popcount prefix compacts into ascending
 //     indices.  A row with more than 16 lists first merges them in groups of 16, each group
 //     into one list of its exact top R (a first-level launch), so the final merge never holds
