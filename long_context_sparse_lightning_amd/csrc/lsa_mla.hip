@@ -314,6 +314,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
       for (int i = 0; i < C::KSW; ++i)
         kb[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
                                                kvt + (i + 1 < C::KSW ? k_lane + 128 * i : k_last)));
+      __builtin_amdgcn_sched_barrier(0);  // every fragment read is issued before the first step
 #pragma unroll
       for (int i = 0; i < C::KSW; ++i) {
         acc0 = mfma16(kb[i], qf[0][i], acc0);
@@ -328,14 +329,19 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
     // ---- logits of head `col` for the tile rows of A-operand slots e: acc_row(e, g)
     float sv[8];
     {
-      const float* p0 = &spart[0][col * kPartStride + 4 * g];
-      f32x4 lo = *reinterpret_cast<const f32x4*>(p0);
-      f32x4 hi = *reinterpret_cast<const f32x4*>(p0 + 8);
+      f32x4 lw[4], hw[4];  // all eight reads are issued before the first add
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float* pw = &spart[w][col * kPartStride + 4 * g];
+        lw[w] = *reinterpret_cast<const f32x4*>(pw);
+        hw[w] = *reinterpret_cast<const f32x4*>(pw + 8);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 lo = lw[0], hi = hw[0];
 #pragma unroll
       for (int w = 1; w < 4; ++w) {
-        const float* pw = &spart[w][col * kPartStride + 4 * g];
-        lo += *reinterpret_cast<const f32x4*>(pw);
-        hi += *reinterpret_cast<const f32x4*>(pw + 8);
+        lo += lw[w];
+        hi += hw[w];
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
