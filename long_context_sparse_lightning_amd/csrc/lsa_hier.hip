@@ -110,7 +110,7 @@ __device__ __forceinline__ float score32(const HierParams& P, int b, const uint1
     const float wh = h < P.Hi ? P.w[static_cast<size_t>(b) * P.Hi + h] : 0.0f;
     s += wh * fmaxf(acc[r], 0.0f);
   }
-  return s + xor32(s);
+  return sum_xor32(s);
 }
 
 // grid (ceil(nblk / 128), B): scores of blocks [0, nb) and the row's nb.

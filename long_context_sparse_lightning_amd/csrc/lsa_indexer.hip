@@ -157,7 +157,7 @@ __global__ __launch_bounds__(THREADS) void index_scores_kernel(IndexParams P) {
     float part = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) part += wr[r] * fmaxf(acc[r], 0.0f);
-    const float score = part + xor32(part);
+    const float score = sum_xor32(part);
     if (g == 0) stage[t0 - start + col] = score;  // t0 - start + col < keys_per_wg
     if constexpr (FUSED) {
       const uint32_t k = sel::order_key(score);
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void index_scores_qb_kernel(QbParams
 #pragma unroll
   for (int q = 0; q < RPW; ++q) held[q] = 0.0f;
   auto store_row = [&](int q, int t, float part, bool odd) {
-    part += xor32(part);
+    part = sum_xor32(part);
     if (!odd) {
       held[q] = part;
       return;

@@ -52,10 +52,17 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 
 __device__ __forceinline__ uint64_t wave_ballot(bool pred) { return __ballot(pred); }
 
-// Value of lane ^ 32 via the gfx950 permlane swap (VALU, no LDS round trip).
-__device__ __forceinline__ float xor32(float x) {
+// x combined with x of lane ^ 32 by the gfx950 permlane swap (VALU, no LDS round trip).  Swapping
+// a value with itself leaves the lower half's value in every lane of r[0] and the upper half's
+// in every lane of r[1], so the sum or maximum of the pair needs no per-lane select and is the
+// same in both halves.
+__device__ __forceinline__ float sum_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(((threadIdx.x >> 5) & 1) ? r[0] : r[1]);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Inclusive scan of op over the 64 lanes of a wavefront on the vector ALU (gfx9 DPP): shifts by

@@ -376,7 +376,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
     float mloc = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 8; ++e) mloc = fmaxf(mloc, sv[e]);
-    mloc = fmaxf(mloc, xor32(mloc));
+    mloc = max_xor32(mloc);
     const bool grow = mloc > m_ref + kRescaleSlack;
     if (__ballot(grow)) {
       const float m_new = grow ? mloc : m_ref;
@@ -403,7 +403,7 @@ __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
       pw[i] = __builtin_bit_cast(uint32_t, pr);
       psum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, psum, false);  // both bf16 values, in fp32
     }
-    psum += xor32(psum);
+    psum = sum_xor32(psum);
     l_run += psum;
     // A operand: k-slot e of lane half g is tile row acc_row(e, g)
     const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
