@@ -147,10 +147,19 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 template <int DQK, int DV, bool SPARSE>
 __global__ __launch_bounds__(kThreads, 2) void sparse_mla_kernel(MlaParams P) {
   using C = Cfg<DQK, DV>;
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[kStages][C::STAGE_UNITS * 8];
-  __shared__ __attribute__((aligned(16))) float spart[4][kHeadGroup * kPartStride];  // partial logits
-  __shared__ int32_t slice[kMaxRowsPerSplit];
-  __shared__ __attribute__((aligned(16))) float inv_head[kHeadGroup];  // 1 / l per head (epilogue)
+  // One LDS block in a fixed order: the row-position slice, read every tile, sits at the bottom,
+  // so that every LDS offset of the loop fits an instruction's 16-bit immediate.
+  struct Smem {
+    int32_t slice[kMaxRowsPerSplit];
+    __attribute__((aligned(16))) float spart[4][kHeadGroup * kPartStride];  // partial logits
+    __attribute__((aligned(16))) float inv_head[kHeadGroup];  // 1 / l per head (epilogue)
+    __attribute__((aligned(1024))) uint16_t ring[kStages][C::STAGE_UNITS * 8];
+  };
+  __shared__ __attribute__((aligned(1024))) Smem sm;
+  auto& slice = sm.slice;
+  auto& spart = sm.spart;
+  auto& inv_head = sm.inv_head;
+  auto& ring = sm.ring;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
