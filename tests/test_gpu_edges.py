@@ -66,6 +66,12 @@ def _topk_both(scores_np, seqlens, topk, init, local):
     (200000, 2048, 16, 1024, (200000, 16385)),
     (40000, 64, 0, 0, (40000, 33000)),
     (16384, 2048, 16, 1024, (16384, 2049)),
+    # degenerate selections: the arg-max (lowest position among ties), the sink alone, the
+    # current position alone, one of each; rows of one and two positions take the dense path
+    (5000, 1, 0, 0, (5000, 2, 1)),
+    (5000, 1, 1, 0, (5000, 2, 1)),
+    (5000, 1, 0, 1, (5000, 2, 1)),
+    (70000, 2, 1, 1, (70000, 3)),
 ])
 def test_topk_on_tied_fp32_scores(S, topk, init, local, seqlens):
     """Scores built from bf16 values (8-bit mantissa -> heavy ties), negatives and signed
@@ -165,6 +171,41 @@ def test_dense_attention_matches_oracle(Lq):
                                          wl.Dv, wl.scale)
         assert_attention_close(bf16_to_f64(out[b]), ref[0], f"dense b={b}")
         assert np.abs(lse[b].cpu().numpy() - ref_lse[0]).max() <= 5e-3
+
+
+def test_attention_largest_selection():
+    """topk at its largest (131072, every split of the launch at its LDS slice limit): one row
+    lists all 131072 positions of its cache in shuffled order, so it equals dense attention; a
+    second row lists 65536 distinct positions of its 100000, and the list entries past n_sel
+    hold out-of-range values that must be ignored.  Both rows against the oracle."""
+    topk = 131072
+    wl = Workload("max_selection", B=2, S_max=topk, Lq=1, seqlens=(topk, 100000), Hi=4, Di=32,
+                  topk=topk, init=0, local=0, H=4, seed=86)
+    print("case attention topk=131072", flush=True)
+    X = device_inputs(wl)
+    rng = np.random.default_rng(86)
+    idx = np.empty((2, topk), np.int32)
+    idx[0] = rng.permutation(topk)
+    idx[1, :65536] = rng.choice(100000, 65536, replace=False)
+    idx[1, 65536::2] = -7
+    idx[1, 65537::2] = 1 << 30
+    nsel = np.array([topk, 65536], np.int32)
+    lse = torch.empty(wl.B, wl.H, dtype=torch.float32, device="cuda")
+    out = lsa.lsa_sparse_mla_decode(X["q0"][:, 0], X["kv0"], torch.from_numpy(idx).cuda(),
+                                    torch.from_numpy(nsel).cuda(), X["seqlens"], wl.Dv, wl.scale,
+                                    lse=lse)
+    dense = lsa.lsa_sparse_mla_decode(X["q0"][:, 0], X["kv0"], None, None, X["seqlens"], wl.Dv,
+                                      wl.scale)
+    torch.cuda.synchronize()
+    for b in range(wl.B):
+        q = host_slice(wl, "q0", b)[None]
+        kv = host_slice(wl, "kv0", b)[None]
+        ref, ref_lse = oracle.sparse_mla(q, kv, idx[b][None, None], nsel[b][None, None],
+                                         np.array([wl.seqlens[b]], np.int32), wl.Dv, wl.scale)
+        assert_attention_close(bf16_to_f64(out[b][None]), ref[0], f"max selection b={b}")
+        assert np.abs(lse[b].cpu().numpy() - ref_lse[0, 0]).max() <= 5e-3
+    assert_attention_close(bf16_to_f64(out[0][None]), bf16_to_f64(dense[0][None]),
+                           "max selection row 0 against dense attention")
 
 
 def test_dense_fallback_equals_dense_attention():

@@ -24,6 +24,12 @@ EDGE = [
              init=32, local=64, H=4, Dqk=80, Dv=64, seed=94),
     Workload("f_multi_chunk", B=3, S_max=70001, Lq=1, seqlens=(70001, 40000, 2049), Hi=8, Di=128,
              topk=2048, init=16, local=1024, H=4, Dqk=80, Dv=64, seed=95),
+    # topk = 1 with no forced column: the arg-max, lowest position among ties
+    Workload("f_topk1", B=3, S_max=5000, Lq=1, seqlens=(1, 2, 5000), Hi=4, Di=32, topk=1, init=0,
+             local=0, H=4, Dqk=80, Dv=64, seed=96),
+    # the longest supported row (S_max = 2^20)
+    Workload("f_max_len", B=1, S_max=1 << 20, Lq=1, seqlens=(1 << 20,), Hi=4, Di=32, topk=2048,
+             init=16, local=1024, H=4, Dqk=80, Dv=64, seed=97),
 ]
 
 
