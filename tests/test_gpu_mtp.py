@@ -95,6 +95,27 @@ def test_draft_steps_match_oracle(c):
         compare(c, q, kv, idx, nsel, iseq, seq, 3, out, lse, f"{c.name} step {j}")
 
 
+def test_largest_selection_and_most_appended():
+    """The largest pass the draft call takes (topk = 65536) with the most appended positions
+    (max_appended = 64): draft steps with 0, 1 and 64 positions appended, and 70 (clamped to
+    64), against the oracle.  The appended positions ride in the last split, which stays within
+    its LDS slice."""
+    c = Case("max_selection", 2, 4, 576, 512, 65700, 65536, 65600, 605)
+    q, kv, idx, nsel = make(c)
+    d_idx, d_nsel = torch.from_numpy(idx).cuda(), torch.from_numpy(nsel).cuda()
+    iseq = np.full(c.B, c.S0, np.int32)
+    d_iseq = torch.from_numpy(iseq).cuda()
+    scale = 1.0 / np.sqrt(192.0)
+    for j in (0, 1, 64, 70):
+        print(f"case draft topk=65536 appended={j}", flush=True)
+        seq = iseq + j
+        lse = torch.empty(c.B, c.H, dtype=torch.float32, device="cuda")
+        out = lsa.lsa_mtp_draft_attention(q, kv, d_idx, d_nsel, d_iseq, torch.from_numpy(seq).cuda(),
+                                          c.Dv, scale, max_appended=64, lse=lse)
+        torch.cuda.synchronize()
+        compare(c, q, kv, idx, nsel, iseq, seq, 64, out, lse, f"max selection, {j} appended")
+
+
 def test_nothing_appended_equals_decode():
     c = CASES[0]
     q, kv, idx, nsel = make(c)
