@@ -20,7 +20,6 @@ import csv
 import hashlib
 import json
 import os
-import statistics
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -86,16 +85,19 @@ def summarize(fetch_csv, write_csv, calib_mib, workload, path, alg_bytes, cmd_fe
         if not c:
             raise SystemExit(f"{csv_path}: no {COPY_MATCH} dispatch")
         factor = max(c) / calib  # the largest copy is the calibration copy
-        raw, ndisp = 0.0, []
+        # The first kernel runs once per call; the others may run more than once (a two-level
+        # merge): per call, every matching dispatch summed over the number of calls.
+        raw, calls = 0.0, None
         per_kernel = {}
-        for kname in kernels:  # one dispatch of each per call: sum of the per-kernel means
+        for kname in kernels:
             k = [v * 1024.0 for n, v in disp.values() if kname in n]
             if not k:
                 raise SystemExit(f"{csv_path}: no {kname} dispatches")
-            raw += statistics.mean(k)
-            ndisp.append(len(k))
-            per_kernel[kname] = statistics.mean(k) / factor
-        res[counter] = {"kernel_raw_bytes_mean": raw, "dispatches": min(ndisp),
+            if calls is None:
+                calls = len(k)
+            raw += sum(k) / calls
+            per_kernel[kname] = sum(k) / calls / factor
+        res[counter] = {"kernel_raw_bytes_mean": raw, "dispatches": calls,
                         "copy_raw_bytes": max(c), "factor": factor,
                         "kernel_bytes_per_launch": raw / factor,
                         "bytes_per_kernel": {k: round(v) for k, v in per_kernel.items()}}

@@ -55,6 +55,28 @@ def test_traffic_is_calibrated_by_the_copy_and_goes_stale_with_the_sources(tmp_p
     assert pmc.load_traffic("unit_wl", "fused") is None
 
 
+def test_traffic_counts_every_dispatch_of_a_multi_launch_call(tmp_path, monkeypatch):
+    """A call whose merge runs in two launches (two merge dispatches per indexer dispatch): both
+    count, per call."""
+    monkeypatch.setattr(pmc, "ROOT", str(tmp_path))
+    fetch = [(K1, "FETCH_SIZE", 1000.0, 0, 1), (MERGE, "FETCH_SIZE", 40.0, 1, 2),
+             (MERGE, "FETCH_SIZE", 20.0, 2, 3), (K1, "FETCH_SIZE", 1200.0, 3, 4),
+             (MERGE, "FETCH_SIZE", 60.0, 4, 5), (MERGE, "FETCH_SIZE", 30.0, 5, 6),
+             (COPY, "FETCH_SIZE", 64 * 1024.0, 6, 7)]
+    write = [(K1, "WRITE_SIZE", 10.0, 0, 1), (MERGE, "WRITE_SIZE", 2.0, 1, 2),
+             (MERGE, "WRITE_SIZE", 1.0, 2, 3), (K1, "WRITE_SIZE", 14.0, 3, 4),
+             (MERGE, "WRITE_SIZE", 4.0, 4, 5), (MERGE, "WRITE_SIZE", 3.0, 5, 6),
+             (COPY, "WRITE_SIZE", 64 * 1024.0, 6, 7)]
+    _write_csv(tmp_path / "f.csv", fetch)
+    _write_csv(tmp_path / "w.csv", write)
+    rec = pmc.summarize(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), 64, "unit_wl", "fused",
+                        1_000_000, "cmd f", "cmd w")
+    fetch_bytes = (1100.0 + (40.0 + 20.0 + 60.0 + 30.0) / 2) * 1024
+    write_bytes = (12.0 + (2.0 + 1.0 + 4.0 + 3.0) / 2) * 1024
+    assert rec["counters"]["FETCH_SIZE"]["dispatches"] == 2
+    assert rec["traffic_bytes_per_launch"] == round(fetch_bytes + write_bytes)
+
+
 def test_traffic_without_a_calibration_copy_is_refused(tmp_path, monkeypatch):
     monkeypatch.setattr(pmc, "ROOT", str(tmp_path))
     _write_csv(tmp_path / "f.csv", [(K1, "FETCH_SIZE", 1.0, 0, 1), (MERGE, "FETCH_SIZE", 1.0, 1, 2)])
