@@ -2,7 +2,12 @@
 the standalone and fused top-k bit-exact against the oracle, attention within tolerance.  The
 shapes span the boundaries of the method: n = topk and topk + 1, n <= init + local, all-equal
 scores (zero index queries: ReLU gives 0 everywhere), negative head weights, prefill rows on
-the query-blocked scan (Di = 128, Lq >= 16) and on the per-row scan."""
+the query-blocked scan (Di = 128, Lq >= 16) and on the per-row scan.  A second, wider strategy
+draws production-like sizes (several top-k chunks, up to 40 heads in two head groups, the
+576/512 latent rows).  LSA_PROPERTY_EXAMPLES scales the number of drawn cases (default 30 small
+and 8 wide) for a deeper sweep."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -47,7 +52,32 @@ def _boundary(n_minus_topk, Di=32, Lq=1, pattern="random"):
                 seqlens=[n], pattern=pattern, H=2, seed=5)
 
 
-@settings(max_examples=30, derandomize=True, deadline=None,
+EXAMPLES = int(os.environ.get("LSA_PROPERTY_EXAMPLES", "30"))
+
+
+@st.composite
+def wide_cases(draw):
+    Di = draw(st.sampled_from([32, 64, 128]))
+    Hi = draw(st.integers(1, 32))
+    topk = draw(st.sampled_from([64, 256, 1024, 2048]))
+    init = draw(st.integers(0, min(16, topk // 4)))
+    local = draw(st.integers(0, topk - init))
+    Lq = draw(st.sampled_from([1, 2, 17]))
+    B = draw(st.integers(1, 3))
+    dims = draw(st.sampled_from([(80, 64), (576, 512)]))
+    # lengths around the selection's chunk boundaries (8192 and 16384 positions) and beyond;
+    # at most ~3e7 latent elements, so a case generates in a few seconds on the host
+    S = draw(st.sampled_from([2049, 8191, 8193, 16384, 16385, 24577, 32768, 40000]))
+    S = max(Lq, min(S, 30_000_000 // (B * dims[0])))
+    seqlens = [S if draw(st.booleans()) else draw(st.integers(Lq, S)) for _ in range(B)]
+    pattern = draw(st.sampled_from(["random", "zero_queries", "negative_weights"]))
+    H = draw(st.sampled_from([1, 4, 32, 40]))
+    seed = draw(st.integers(0, 2**20))
+    return dict(Di=Di, Hi=Hi, topk=topk, init=init, local=local, Lq=Lq, S=S, B=B,
+                seqlens=seqlens, pattern=pattern, H=H, dims=dims, seed=seed)
+
+
+@settings(max_examples=EXAMPLES, derandomize=True, deadline=None,
           suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
 @given(cases())
 @example(_boundary(0))                       # n == topk: dense fallback
@@ -56,9 +86,23 @@ def _boundary(n_minus_topk, Di=32, Lq=1, pattern="random"):
 @example(_boundary(40, pattern="zero_queries"))  # every score 0: ties everywhere
 @example(_boundary(300, Di=128, Lq=17))      # prefill rows on the query-blocked scan
 def test_path_matches_oracle(c):
+    print(f"case {c}", flush=True)
+    _check(c)
+
+
+@settings(max_examples=max(1, EXAMPLES * 8 // 30), derandomize=True, deadline=None,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
+@given(wide_cases())
+def test_wide_shapes_match_oracle(c):
+    print(f"case {c}", flush=True)
+    _check(c)
+
+
+def _check(c):
     B, Lq, S, Hi, Di, H = c["B"], c["Lq"], c["S"], c["Hi"], c["Di"], c["H"]
     topk, init, local, seed = c["topk"], c["init"], c["local"], c["seed"]
-    Dqk, Dv, scale = 80, 64, 1.0 / np.sqrt(80.0)
+    Dqk, Dv = c.get("dims", (80, 64))
+    scale = 1.0 / np.sqrt(float(Dqk))
     qidx = gen.ref_tensor(seed, gen.TAGS["qidx"], (B, Lq, Hi, Di), gen.DYADIC)
     if c["pattern"] == "zero_queries":
         qidx = np.zeros_like(qidx)
